@@ -1,0 +1,37 @@
+"""CPU oracle for the performer's per-unit flow-matching denoise step.
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import or run anything here.  The
+product path (``flow_matching_denoising_amd``) never imports it and shares no
+code with it; the two meet only in the seeded input module ``workload``.
+
+What it computes, in the pages' order (sources are the pages' titles and
+sections):
+
+1. ``ring.kv_append`` -- the performer writes the thinker's K/V slice into its
+   local, preallocated cache at the slice's position
+   [Wan-Streamer v0.2: Higher Resolution, Same Latency (nanless digest),
+   方法概述和架构; Wan-Streamer v0.2 (zhao9797 blog), Infra].
+2. ``attention.attention`` -- the unit's noisy audio and video tokens attend to
+   all clean history plus the unit's own tokens, bidirectionally inside the
+   unit [Wan-Streamer (gongshangzheng blog), 3.3 Block-Causal Transformer and
+   3.4 条件流匹配: cross-modal conditioning, clean context].
+3. ``flow.velocity`` -- one dense output projection gives the velocity of both
+   modalities [same page, 3.4: one f_theta predicts both velocity fields].
+4. ``flow.euler_step`` / ``flow.denoise_unit`` -- the linear (rectified-flow)
+   path has a constant velocity, integrated by an ODE solver over a few steps
+   [same page, 3.4; Fig. 2: the performer receives the slice, then only runs
+   the flow-matching solver].
+
+Everything is float64 unless a function says otherwise.  bf16 inputs arrive as
+uint16 bit patterns and are widened exactly by ``ring.bf16_bits_to_f64``.
+
+Pins: every function here is checked by ``tests/test_oracle_*.py`` against
+something other than itself (brute force on tiny inputs, a library attention
+routine on independently gathered keys, closed forms, invariants).  The
+end-to-end composition on random N(0,1) inputs has no pin beyond its parts:
+parity unpinned for that composition as a whole.
+"""
+from .ring import bf16_bits_to_f64, kv_append, valid_slots  # noqa: F401
+from .attention import attention, attention_naive  # noqa: F401
+from .flow import velocity, euler_step, denoise_step, denoise_unit  # noqa: F401

@@ -1,0 +1,148 @@
+"""Pin checks for the oracle, written as functions of the oracle entry points so
+that the planted-mistake tests can run the same checks against a broken oracle.
+
+Each check derives its expected value without the oracle's own code path:
+from the append history (not from slot arithmetic), from a library attention
+routine, or from a closed form.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import torch
+
+from workload import round_to_bf16_bits
+
+
+def bits(x):
+    return round_to_bf16_bits(np.asarray(x, dtype=np.float32))
+
+
+def widen(b):
+    # Independent of the oracle's own widening: go through torch's bf16 type.
+    t = torch.from_numpy(np.ascontiguousarray(b).astype(np.int16)).view(torch.bfloat16)
+    return t.to(torch.float64).numpy()
+
+
+def random_bits(rng, shape, scale=1.0):
+    return bits(rng.standard_normal(shape).astype(np.float32) * scale)
+
+
+def build_ring_by_history(rng, H, hd, cap, slice_lens, head0=0):
+    """Empty ring (NaN-filled), then append the given slices through ``append_fn``
+    later; returns the slices and the concatenated history [N][H][hd] for K, V."""
+    ks = [random_bits(rng, (T, H, hd)) for T in slice_lens]
+    vs = [random_bits(rng, (T, H, hd)) for T in slice_lens]
+    return ks, vs
+
+
+def apply_history(append_fn, H, hd, cap, ks, vs, head0):
+    nan = np.full((H, cap, hd), 0x7FC0, dtype=np.uint16)
+    rk, rv, length, head = nan.copy(), nan.copy(), 0, head0
+    for k, v in zip(ks, vs):
+        rk, rv, length, head = append_fn(rk, rv, length, head, k, v)
+    return rk, rv, length, head
+
+
+def sdpa_reference(q_bits, hist_k, hist_v, length, k_u, v_u):
+    """torch SDPA in float64 over the last ``length`` tokens of history plus the
+    unit's own tokens (no mask).  Returns [n_q][H][hd]."""
+    tail_k = hist_k[len(hist_k) - length:] if length else hist_k[:0]
+    tail_v = hist_v[len(hist_v) - length:] if length else hist_v[:0]
+    K = np.concatenate([tail_k, k_u])          # [Lk][H][hd]
+    V = np.concatenate([tail_v, v_u])
+    qt = torch.from_numpy(widen(q_bits)).permute(1, 0, 2)[None]   # [1][H][n][hd]
+    kt = torch.from_numpy(widen(K)).permute(1, 0, 2)[None]
+    vt = torch.from_numpy(widen(V)).permute(1, 0, 2)[None]
+    o = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt)
+    return o[0].permute(1, 0, 2).numpy()
+
+
+def check_attention_vs_history(attention_fn, append_fn, seed=0, H=3, hd=16, cap=48,
+                               slice_lens=(20, 13), head0=30, n_q=9):
+    """max |oracle - SDPA(history tail || unit)| for a ring filled by appends
+    (default: a partly filled ring whose valid range wraps; unwritten slots are
+    NaN, so reading one gives an infinite error)."""
+    rng = np.random.default_rng(seed)
+    ks, vs = build_ring_by_history(rng, H, hd, cap, slice_lens)
+    rk, rv, length, head = apply_history(append_fn, H, hd, cap, ks, vs, head0)
+    hist_k, hist_v = np.concatenate(ks), np.concatenate(vs)
+    q = random_bits(rng, (n_q, H, hd))
+    k_u = random_bits(rng, (n_q, H, hd))
+    v_u = random_bits(rng, (n_q, H, hd))
+    got = attention_fn(q, rk, rv, length, head, k_u, v_u)
+    ref = sdpa_reference(q, hist_k, hist_v, min(sum(slice_lens), cap), k_u, v_u)
+    if not np.all(np.isfinite(got)):
+        return float("inf")
+    return float(np.max(np.abs(got - ref)))
+
+
+def expected_ring_from_history(init, hist, head0, cap):
+    """Closed form of the ring after writing history token n at (head0+n) mod cap:
+    each slot holds the latest token that maps to it, else its initial bytes."""
+    N = hist.shape[0]
+    out = init.copy()
+    p = np.arange(cap)
+    r = (p - head0) % cap                      # first history index landing on p
+    touched = r < N
+    last = r + cap * ((N - 1 - r) // cap)      # latest index landing on p
+    out[:, p[touched], :] = np.transpose(hist[last[touched]], (1, 0, 2))
+    return out
+
+
+def check_closed_form_flow(denoise_unit_fn, hs, seed=0, H=2, hd=8, n_q=5, cap=32, length=24):
+    """K == 0 (uniform weights), every V row == w, W = I, start at eps.
+    The velocity is exactly w = eps - z0 with z0 := eps - w, so Euler over any
+    schedule summing to 1 must land on z0.  Returns max |z - z0|."""
+    rng = np.random.default_rng(seed)
+    d = H * hd
+    w = bits(rng.standard_normal(d).astype(np.float32))       # bf16-exact values
+    w_f = widen(w)
+    zero = np.zeros((H, cap, hd), dtype=np.uint16)             # +0.0 bits
+    ring_v = np.broadcast_to(w.reshape(H, 1, hd), (H, cap, hd)).copy()
+    q = random_bits(rng, (n_q, H, hd))
+    k_u = np.zeros((n_q, H, hd), dtype=np.uint16)
+    v_u = np.broadcast_to(w.reshape(1, H, hd), (n_q, H, hd)).copy()
+    eye = bits(np.eye(d, dtype=np.float32))
+    eps = rng.standard_normal((n_q, d))
+    z0 = eps - w_f[None, :]
+    res = denoise_unit_fn(zero, ring_v, length, 3, None, None, [q], [k_u], [v_u],
+                          eps, hs, eye)
+    return float(np.max(np.abs(res["z"] - z0)))
+
+
+def brute_velocity(o, w_bits):
+    """v[i][n] = sum_k O[i][k] * W[n][k], scalar loops (tiny sizes only)."""
+    W = widen(w_bits)
+    n_rows, d = o.shape
+    v = np.zeros((n_rows, W.shape[0]))
+    for i in range(n_rows):
+        for n in range(W.shape[0]):
+            acc = 0.0
+            for k in range(d):
+                acc += o[i, k] * W[n, k]
+            v[i, n] = acc
+    return v
+
+
+def rel_l2(a, b):
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    return float(np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-300))
+
+
+def softmax_scale(hd):
+    return 1.0 / math.sqrt(hd)
+
+
+def check_values_one(attention_fn, seed=2, H=2, hd=16, cap=40, n_q=7):
+    """V == 1 everywhere => O == 1 (softmax weights sum to one).  Returns max |O - 1|."""
+    rng = np.random.default_rng(seed)
+    one = bits(np.ones(1))[0]
+    rk = random_bits(rng, (H, cap, hd))
+    rv = np.full((H, cap, hd), one, dtype=np.uint16)
+    q, ku = random_bits(rng, (n_q, H, hd)), random_bits(rng, (n_q, H, hd))
+    vu = np.full((n_q, H, hd), one, dtype=np.uint16)
+    o = attention_fn(q, rk, rv, 33, 5, ku, vu)
+    return float(np.max(np.abs(o - 1.0)))
