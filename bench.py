@@ -1,0 +1,222 @@
+"""Benchmark: denoised units per second on one MI355X.
+
+One step = one denoised unit of the 640x368-class workload (40 heads x 128,
+920 video + 8 audio queries, a 64-unit ring of 944-token slices = 60,416 keys):
+the slice append, then 4 Euler solver steps, each attention over
+[60,416 cached keys || 928 unit keys] -> projection (5120 x 5120) -> Euler
+update.  Inputs are seeded synthetic tensors (no weights or data were
+released for the method), resident in HBM before the timed region.
+
+Prints ONE JSON line (rank 0, N=1).  Besides throughput it reports:
+* roofline: the attention kernel (the dominant kernel), algorithmic flops per
+  launch / its mean launch duration measured with HIP events recorded on the
+  launch stream during the timed region, against the bf16 dense MFMA peak;
+* cpu_baseline: the CPU oracle timed on a bounded sample of the same workload
+  (one full solver step: attention of every head, the projection and the Euler
+  update), scaled to the unit's solver steps.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+MFMA_BF16_PEAK_TFLOPS = 2500.0     # MI355X dense bf16 (published)
+HBM_PEAK_GBS = 8000.0              # MI355X HBM3E (published)
+UNIT_BUDGET_S = 0.160              # one streaming unit
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_v02_unit_traffic.json")
+ATTN_SRC = os.path.join(ROOT, "flow_matching_denoising_amd", "csrc", "attention.hip")
+
+
+def _args():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="v02_unit")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--quiet", action="store_true")
+    return ap.parse_args()
+
+
+def _log(args, *a):
+    if not args.quiet:
+        print(*a, file=sys.stderr, flush=True)
+
+
+def _attn_traffic():
+    """HBM bytes per attention launch from committed rocprofv3 counter runs,
+    valid only while attention.hip is unchanged since they were taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+        with open(ATTN_SRC, "rb") as f:
+            h = hashlib.sha256(f.read()).hexdigest()
+        if t.get("attention_hip_sha256") != h:
+            return None
+        return float(t["hbm_bytes_per_launch"])
+    except (OSError, ValueError, KeyError):
+        return None
+
+
+def cpu_baseline(wl, ui, args):
+    """The oracle, as it stands, on a bounded sample of one unit."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max((p.get("num_threads", 1) for p in threadpool_info()), default=1)
+    except Exception:  # pragma: no cover
+        cores = len(os.sched_getaffinity(0))
+    si = ui.sessions[0]
+    s = si.shape
+    rk, rv, ln, hd_ = oracle.kv_append(si.ring_k, si.ring_v, s.len_before, s.head_before,
+                                       si.slice_k, si.slice_v)[:4]
+    heads = list(range(s.n_heads))
+    t0 = time.perf_counter()
+    O = oracle.attention(si.q[0], rk, rv, ln, hd_, si.k_u[0], si.v_u[0], heads=heads)
+    t_attn = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    v = oracle.velocity(O.reshape(O.shape[0], -1), ui.w_o)
+    oracle.euler_step(si.eps, s.h[0], v)
+    t_proj = time.perf_counter() - t0
+    t_unit = s.n_steps * (t_attn * s.n_heads / len(heads) + t_proj)
+    _log(args, f"cpu oracle: attention {len(heads)} heads {t_attn:.2f}s, projection {t_proj:.2f}s"
+               f" -> {t_unit:.1f}s per unit")
+    return {"value": 1.0 / t_unit, "unit": "units/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"float64 oracle on one of the unit's {s.n_steps} solver steps: attention "
+                      f"of all {s.n_heads} heads ({s.n_q} queries x {s.keys_per_query} keys), the "
+                      f"{s.n_q}x{s.d}x{s.d} projection and the Euler update "
+                      f"({t_attn + t_proj:.1f} s), scaled by {s.n_steps} steps per unit"}
+
+
+def main():
+    args = _args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on exactly one GPU: the denoise step here is a single-GPU "
+              "kernel path (multi-GPU sharding is design-only); use --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import flow_matching_denoising_amd as fmd
+    import workload
+
+    wl = workload.get(args.workload)
+    dev = torch.device("cuda:0")
+    t0 = time.perf_counter()
+    ui = workload.make_inputs(wl)
+    _log(args, f"inputs drawn in {time.perf_counter() - t0:.1f}s")
+
+    def bf(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    caches, ios, states = [], [], []
+    for si in ui.sessions:
+        s = si.shape
+        c = fmd.KVCache(s.n_heads, s.head_dim, s.cap_tokens, device=dev, k=bf(si.ring_k),
+                        v=fmd.KVCache.logical_to_device_v(bf(si.ring_v)),
+                        len_tokens=s.len_before, head_tokens=s.head_before)
+        z = torch.from_numpy(si.eps.copy()).to(dev)
+        q = bf(np.stack(si.q))
+        ku = bf(np.stack(si.k_u))
+        vu = bf(np.stack(si.v_u))
+        io = fmd.UnitIO(c, bf(si.slice_k), bf(si.slice_v), q, ku, vu, z, list(s.h),
+                        n_audio=s.n_audio)
+        caches.append(c)
+        ios.append(io)
+        states.append((s.len_before, s.head_before))
+    w_o = bf(ui.w_o)
+    ws = fmd.alloc_workspace(fmd.unit_workspace_bytes(ios), dev)
+    torch.cuda.synchronize()
+
+    def one_unit():
+        # Every timed unit appends at the same offset into the same ring state.
+        for c, (ln, hd_) in zip(caches, states):
+            c.set_state(ln, hd_)
+        fmd.denoise_unit(ios, w_o, ws)
+
+    for _ in range(args.warmup):
+        one_unit()
+    torch.cuda.synchronize()
+
+    fmd.profile_enable(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        one_unit()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kt = {k: fmd.profile_read(k) for k in fmd.KERNEL_CLASSES}
+    fmd.profile_enable(False)
+
+    n_sess = len(ui.sessions)
+    ms_per_step = wall / args.steps * 1e3
+    units_per_s = n_sess * args.steps / wall
+    attn_ms, attn_n = kt["attn"]
+    attn_avg_s = attn_ms / attn_n / 1e3
+    attn_flops_launch = wl.attention_flops_per_step()    # one launch covers all sessions of a step
+    attn_tflops = attn_flops_launch / attn_avg_s / 1e12
+    traffic = _attn_traffic()
+    per_kernel_us = {k: (v[0] / v[1] * 1e3 if v[1] else None) for k, v in kt.items()}
+    app_ms, app_n = kt["append"]
+    append_gbs = wl.append_bytes() / (app_ms / app_n / 1e3) / 1e9 if app_n else None
+    proj_ms, proj_n = kt["proj"]
+    proj_tflops = wl.projection_flops_per_step() / (proj_ms / proj_n / 1e3) / 1e12 if proj_n else None
+
+    s0 = wl.sessions[0]
+    out = {
+        "metric": "denoised units/sec (1 GPU) at 640×368-class shape; attn TFLOP/s vs MFMA peak",
+        "value": round(units_per_s, 3),
+        "unit": "units/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": wl.name,
+            "sessions": n_sess,
+            "heads": s0.n_heads, "head_dim": s0.head_dim,
+            "queries_per_unit": s0.n_q, "cached_keys": s0.len_after,
+            "keys_per_query": s0.keys_per_query, "slice_tokens": s0.slice_tokens,
+            "solver_steps": s0.n_steps,
+        },
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(attn_tflops, 2),
+            "peak": MFMA_BF16_PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(attn_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+            "traffic": traffic,
+            "kernel": "attn_kernel<128>",
+            "flops_per_launch": attn_flops_launch,
+            "avg_launch_us": round(attn_avg_s * 1e6, 2),
+        },
+        "per_kernel_us": {k: (round(v, 2) if v is not None else None)
+                          for k, v in per_kernel_us.items()},
+        "append_GBps": round(append_gbs, 1) if append_gbs else None,
+        "append_frac_hbm": round(append_gbs / HBM_PEAK_GBS, 4) if append_gbs else None,
+        "proj_TFLOPs": round(proj_tflops, 1) if proj_tflops else None,
+        "unit_layers_per_160ms": round(UNIT_BUDGET_S / (ms_per_step / 1e3 / n_sess), 2),
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(wl, ui, args)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

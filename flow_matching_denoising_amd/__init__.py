@@ -1,0 +1,316 @@
+"""Python binding of libfmd, the MI355X (gfx950) performer denoise step.
+
+Argument marshalling only: every step of the path runs in the HIP kernels of
+``libfmd.so`` behind the C ABI declared in ``include/fmd.h``.  PyTorch is used
+for device memory and streams.  There is no fallback: if the library is not
+built, importing this package raises ``ImportError``.
+
+Names follow the C ABI: ``kv_append``, ``kv_append_batched``, ``attention``,
+``denoise_step``, ``denoise_unit``, ``workspace_bytes``,
+``unit_workspace_bytes``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libfmd.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"{LIB_PATH} is missing: build it with `python -c 'import __graft_entry__ as g; g.build()'` "
+        "(hipcc for gfx950). There is no CPU fallback.")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+FMD_MAX_SESSIONS = 64
+FMD_CACHE_BLOCK = 16
+STATUS = {0: "FMD_OK", -1: "FMD_E_INVAL", -2: "FMD_E_SHAPE", -3: "FMD_E_CAPACITY",
+          -4: "FMD_E_ALIGN", -5: "FMD_E_WORKSPACE", -6: "FMD_E_HIP"}
+KERNEL_CLASSES = {"append": 0, "vt": 1, "attn": 2, "combine": 3, "proj": 4}
+
+
+class FmdError(RuntimeError):
+    def __init__(self, code: int, detail: str):
+        self.code = code
+        self.name = STATUS.get(code, str(code))
+        super().__init__(f"{self.name} ({code}): {detail}")
+
+
+class _Cache(ctypes.Structure):
+    _fields_ = [("k", ctypes.c_void_p), ("v", ctypes.c_void_p), ("n_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("cap_tokens", ctypes.c_int64),
+                ("len_tokens", ctypes.c_int64), ("head_tokens", ctypes.c_int64)]
+
+
+class _UnitStep(ctypes.Structure):
+    _fields_ = [("cache", ctypes.POINTER(_Cache)), ("q", ctypes.c_void_p),
+                ("k_u", ctypes.c_void_p), ("v_u", ctypes.c_void_p),
+                ("z", ctypes.c_void_p), ("n_video", ctypes.c_int32),
+                ("n_audio", ctypes.c_int32), ("h", ctypes.c_float)]
+
+
+class _UnitIO(ctypes.Structure):
+    _fields_ = [("cache", ctypes.POINTER(_Cache)), ("k_slice", ctypes.c_void_p),
+                ("v_slice", ctypes.c_void_p), ("slice_tokens", ctypes.c_int64),
+                ("q", ctypes.c_void_p), ("k_u", ctypes.c_void_p), ("v_u", ctypes.c_void_p),
+                ("step_stride_elems", ctypes.c_int64), ("z", ctypes.c_void_p),
+                ("n_video", ctypes.c_int32), ("n_audio", ctypes.c_int32),
+                ("h", ctypes.POINTER(ctypes.c_float))]
+
+
+def _sig(name, restype, *argtypes):
+    f = getattr(_lib, name)
+    f.restype = restype
+    f.argtypes = list(argtypes)
+    return f
+
+
+_vp, _i32, _i64, _sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+_kv_append = _sig("fmd_kv_append", ctypes.c_int, ctypes.POINTER(_Cache), _vp, _vp, _i64, _vp)
+_kv_append_batched = _sig("fmd_kv_append_batched", ctypes.c_int,
+                          ctypes.POINTER(ctypes.POINTER(_Cache)), ctypes.POINTER(_vp),
+                          ctypes.POINTER(_vp), ctypes.POINTER(_i64), _i32, _vp)
+_workspace_bytes = _sig("fmd_workspace_bytes", ctypes.c_int, ctypes.POINTER(_UnitStep), _i32,
+                        ctypes.POINTER(_sz))
+_denoise_step = _sig("fmd_denoise_step", ctypes.c_int, ctypes.POINTER(_UnitStep), _i32, _vp, _vp,
+                     _sz, _vp)
+_attention = _sig("fmd_attention", ctypes.c_int, ctypes.POINTER(_UnitStep), _i32, _vp, _vp, _sz,
+                  _vp)
+_unit_workspace_bytes = _sig("fmd_unit_workspace_bytes", ctypes.c_int, ctypes.POINTER(_UnitIO),
+                             _i32, ctypes.POINTER(_sz))
+_denoise_unit = _sig("fmd_denoise_unit", ctypes.c_int, ctypes.POINTER(_UnitIO), _i32, _i32, _vp,
+                     _vp, _sz, _vp)
+_strerror = _sig("fmd_strerror", ctypes.c_char_p, ctypes.c_int)
+_last_error = _sig("fmd_last_error", ctypes.c_char_p)
+_profile_enable = _sig("fmd_profile_enable", ctypes.c_int, ctypes.c_int)
+_profile_read = _sig("fmd_profile_read", ctypes.c_int, ctypes.c_int,
+                     ctypes.POINTER(ctypes.c_double), ctypes.POINTER(_i64))
+_version = _sig("fmd_version", ctypes.c_char_p)
+
+EXPORTED = ["fmd_kv_append", "fmd_kv_append_batched", "fmd_workspace_bytes", "fmd_denoise_step",
+            "fmd_attention", "fmd_unit_workspace_bytes", "fmd_denoise_unit", "fmd_strerror",
+            "fmd_last_error", "fmd_profile_enable", "fmd_profile_read", "fmd_version"]
+
+
+def _check(rc: int):
+    if rc != 0:
+        raise FmdError(rc, _last_error().decode(errors="replace") or _strerror(rc).decode())
+
+
+def strerror(code: int) -> str:
+    return _strerror(code).decode()
+
+
+def version() -> str:
+    return _version().decode()
+
+
+def _stream_ptr(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _ptr(t, dtype, name, allow_none=False):
+    if t is None:
+        if allow_none:
+            return None
+        raise ValueError(f"{name} is required")
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on a GPU")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+class KVCache:
+    """One session's ring: device tensors k [H][cap][hd] and v
+    [H][cap/16][hd][16] (bf16), plus the host-side (len, head) state that the
+    library advances on every append."""
+
+    def __init__(self, n_heads: int, head_dim: int, cap_tokens: int, device="cuda",
+                 k: torch.Tensor | None = None, v: torch.Tensor | None = None,
+                 len_tokens: int = 0, head_tokens: int = 0):
+        if k is None:
+            k = torch.empty((n_heads, cap_tokens, head_dim), dtype=torch.bfloat16, device=device)
+        if v is None:
+            v = torch.empty((n_heads, cap_tokens // FMD_CACHE_BLOCK, head_dim, FMD_CACHE_BLOCK),
+                            dtype=torch.bfloat16, device=device)
+        self.k, self.v = k, v
+        self._c = _Cache(_ptr(k, torch.bfloat16, "k"), _ptr(v, torch.bfloat16, "v"), n_heads,
+                         head_dim, cap_tokens, len_tokens, head_tokens)
+
+    n_heads = property(lambda self: self._c.n_heads)
+    head_dim = property(lambda self: self._c.head_dim)
+    cap_tokens = property(lambda self: self._c.cap_tokens)
+
+    @property
+    def len_tokens(self):
+        return self._c.len_tokens
+
+    @property
+    def head_tokens(self):
+        return self._c.head_tokens
+
+    def set_state(self, len_tokens: int, head_tokens: int):
+        self._c.len_tokens = len_tokens
+        self._c.head_tokens = head_tokens
+
+    @staticmethod
+    def logical_to_device_v(v_logical: torch.Tensor) -> torch.Tensor:
+        """[H][cap][hd] -> [H][cap/16][hd][16] (the device layout of the V ring)."""
+        H, cap, hd = v_logical.shape
+        return v_logical.reshape(H, cap // 16, 16, hd).transpose(2, 3).contiguous()
+
+    @staticmethod
+    def device_to_logical_v(v_dev: torch.Tensor) -> torch.Tensor:
+        H, nb, hd, b = v_dev.shape
+        return v_dev.transpose(2, 3).reshape(H, nb * b, hd).contiguous()
+
+
+def kv_append(cache: KVCache, k_slice, v_slice, stream=None):
+    """Append one slice [T][H][hd] (bf16) to the ring; advances len/head."""
+    _check(_kv_append(ctypes.byref(cache._c), _ptr(k_slice, torch.bfloat16, "k_slice"),
+                      _ptr(v_slice, torch.bfloat16, "v_slice"), k_slice.shape[0],
+                      _stream_ptr(stream)))
+
+
+def kv_append_batched(caches, k_slices, v_slices, stream=None):
+    n = len(caches)
+    arr_c = (ctypes.POINTER(_Cache) * n)(*[ctypes.pointer(c._c) for c in caches])
+    arr_k = (_vp * n)(*[_ptr(t, torch.bfloat16, "k_slice") for t in k_slices])
+    arr_v = (_vp * n)(*[_ptr(t, torch.bfloat16, "v_slice") for t in v_slices])
+    arr_t = (_i64 * n)(*[t.shape[0] for t in k_slices])
+    _check(_kv_append_batched(arr_c, arr_k, arr_v, arr_t, n, _stream_ptr(stream)))
+
+
+class UnitStep:
+    """One session's inputs for one solver step (see ``fmd_unit_step``)."""
+
+    def __init__(self, cache: KVCache, q, k_u, v_u, z=None, n_video=None, n_audio=0, h=1.0):
+        self.cache, self.q, self.k_u, self.v_u, self.z = cache, q, k_u, v_u, z
+        n_q = q.shape[0]
+        self.n_video = n_q - n_audio if n_video is None else n_video
+        self.n_audio = n_audio
+        self.h = h
+
+    def _struct(self):
+        return _UnitStep(ctypes.pointer(self.cache._c), _ptr(self.q, torch.bfloat16, "q"),
+                         _ptr(self.k_u, torch.bfloat16, "k_u"),
+                         _ptr(self.v_u, torch.bfloat16, "v_u"),
+                         _ptr(self.z, torch.float32, "z", allow_none=True),
+                         self.n_video, self.n_audio, self.h)
+
+
+def _steps_array(units):
+    n = len(units)
+    return (_UnitStep * n)(*[u._struct() for u in units]), n
+
+
+def workspace_bytes(units) -> int:
+    arr, n = _steps_array(units)
+    out = _sz(0)
+    _check(_workspace_bytes(arr, n, ctypes.byref(out)))
+    return out.value
+
+
+def alloc_workspace(nbytes: int, device="cuda") -> torch.Tensor:
+    # torch's caching allocator returns blocks aligned to 512 bytes.
+    return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
+
+
+def attention(units, o_out=None, workspace=None, stream=None):
+    """O = attention of every session (bf16 [sum n_q][H][hd]).  Test entry."""
+    arr, n = _steps_array(units)
+    H, hd = units[0].cache.n_heads, units[0].cache.head_dim
+    rows = sum(u.q.shape[0] for u in units)
+    if o_out is None:
+        o_out = torch.empty((rows, H, hd), dtype=torch.bfloat16, device=units[0].q.device)
+    need = _sz(0)
+    _check(_workspace_bytes(arr, n, ctypes.byref(need)))
+    if workspace is None:
+        workspace = alloc_workspace(need.value, units[0].q.device)
+    _check(_attention(arr, n, _ptr(o_out, torch.bfloat16, "o_out"),
+                      workspace.data_ptr(), workspace.numel(), _stream_ptr(stream)))
+    return o_out
+
+
+def denoise_step(units, w_o, workspace=None, stream=None):
+    """One solver step for every session: z <- z - h * (attention(...) W_o^T)."""
+    arr, n = _steps_array(units)
+    if workspace is None:
+        workspace = alloc_workspace(workspace_bytes(units), units[0].q.device)
+    _check(_denoise_step(arr, n, _ptr(w_o, torch.bfloat16, "w_o"), workspace.data_ptr(),
+                         workspace.numel(), _stream_ptr(stream)))
+
+
+class UnitIO:
+    """One session's inputs for a whole unit (see ``fmd_unit_io``).
+
+    q, k_u, v_u: bf16 [S][n_q][H][hd] (one set per step) or [n_q][H][hd]
+    (reused for every step); z: float32 [n_q][d], eps in, final latent out;
+    h: step sizes."""
+
+    def __init__(self, cache: KVCache, k_slice, v_slice, q, k_u, v_u, z, h, n_audio=0):
+        self.cache, self.k_slice, self.v_slice = cache, k_slice, v_slice
+        self.q, self.k_u, self.v_u, self.z = q, k_u, v_u, z
+        self.h = (ctypes.c_float * len(h))(*[float(x) for x in h])
+        self.n_steps = len(h)
+        per_step = q.dim() == 4
+        self.n_q = q.shape[1] if per_step else q.shape[0]
+        self.stride = q[0].numel() if per_step else 0
+        self.n_audio = n_audio
+
+    def _struct(self):
+        T = 0 if self.k_slice is None else self.k_slice.shape[0]
+        return _UnitIO(ctypes.pointer(self.cache._c),
+                       _ptr(self.k_slice, torch.bfloat16, "k_slice", allow_none=True),
+                       _ptr(self.v_slice, torch.bfloat16, "v_slice", allow_none=True), T,
+                       _ptr(self.q, torch.bfloat16, "q"), _ptr(self.k_u, torch.bfloat16, "k_u"),
+                       _ptr(self.v_u, torch.bfloat16, "v_u"), self.stride,
+                       _ptr(self.z, torch.float32, "z"), self.n_q - self.n_audio, self.n_audio,
+                       ctypes.cast(self.h, ctypes.POINTER(ctypes.c_float)))
+
+
+def _io_array(sessions):
+    n = len(sessions)
+    return (_UnitIO * n)(*[s._struct() for s in sessions]), n
+
+
+def unit_workspace_bytes(sessions) -> int:
+    arr, n = _io_array(sessions)
+    out = _sz(0)
+    _check(_unit_workspace_bytes(arr, n, ctypes.byref(out)))
+    return out.value
+
+
+def denoise_unit(sessions, w_o, workspace=None, stream=None):
+    """Append every session's slice, then run the S solver steps."""
+    n_steps = sessions[0].n_steps
+    if any(s.n_steps != n_steps for s in sessions):
+        raise ValueError("all sessions must have the same number of steps")
+    if workspace is None:
+        workspace = alloc_workspace(unit_workspace_bytes(sessions), sessions[0].z.device)
+    arr, n = _io_array(sessions)
+    _check(_denoise_unit(arr, n, n_steps, _ptr(w_o, torch.bfloat16, "w_o"), workspace.data_ptr(),
+                         workspace.numel(), _stream_ptr(stream)))
+    # The library advanced each cache's (len, head) in the struct array it was
+    # given; the array holds pointers to the caches' own structs, so nothing to copy.
+
+
+def profile_enable(on: bool = True):
+    _check(_profile_enable(1 if on else 0))
+
+
+def profile_read(kernel: str):
+    ms, n = ctypes.c_double(0), _i64(0)
+    _check(_profile_read(KERNEL_CLASSES[kernel], ctypes.byref(ms), ctypes.byref(n)))
+    return ms.value, n.value

@@ -1,0 +1,615 @@
+// C ABI of libfmd: argument validation, work planning, workspace layout and
+// kernel launches.  Nothing is enqueued unless every argument of the call is
+// valid; a failed call leaves every cache's (len, head) unchanged.
+//
+// One denoised unit [Wan-Streamer (gongshangzheng blog), Fig. 2 and 5.2]: the
+// performer writes the thinker's K/V slice into its local cache, then runs the
+// flow-matching solver: per step, attention over [valid cache || unit],
+// projection to a velocity, Euler update [same page, 3.4].
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "fmd_internal.h"
+
+using namespace fmd;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// ---------------------------------------------------------------------------
+// Event timing of launches (off unless enabled).
+// ---------------------------------------------------------------------------
+struct ProfRec {
+  hipEvent_t a, b;
+  int cls;
+};
+std::mutex g_prof_mu;
+bool g_prof_on = false;
+std::vector<ProfRec> g_prof;
+std::vector<hipEvent_t> g_event_pool;
+
+hipEvent_t take_event() {
+  if (!g_event_pool.empty()) {
+    hipEvent_t e = g_event_pool.back();
+    g_event_pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+template <class F>
+int timed_launch(int cls, hipStream_t st, F&& launch) {
+  hipEvent_t a = nullptr, b = nullptr;
+  bool rec = false;
+  {
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    if (g_prof_on) {
+      a = take_event();
+      b = take_event();
+      rec = a && b;
+    }
+  }
+  if (rec) (void)hipEventRecord(a, st);
+  hipError_t err = launch();
+  if (rec) {
+    (void)hipEventRecord(b, st);
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    g_prof.push_back({a, b, cls});
+  }
+  if (err != hipSuccess)
+    return fail(FMD_E_HIP, "kernel launch failed: %s", hipGetErrorString(err));
+  return FMD_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Validation.
+// ---------------------------------------------------------------------------
+int check_cache(const fmd_kv_cache* c, int idx) {
+  if (!c) return fail(FMD_E_INVAL, "session %d: cache is NULL", idx);
+  if (!c->k || !c->v) return fail(FMD_E_INVAL, "session %d: cache k/v pointer is NULL", idx);
+  if (!aligned16(c->k) || !aligned16(c->v))
+    return fail(FMD_E_ALIGN, "session %d: cache k/v not 16-byte aligned", idx);
+  if (c->head_dim != 64 && c->head_dim != 128)
+    return fail(FMD_E_SHAPE, "session %d: head_dim %d (must be 64 or 128)", idx, c->head_dim);
+  if (c->n_heads < 1 || c->n_heads > 1024)
+    return fail(FMD_E_SHAPE, "session %d: n_heads %d out of range", idx, c->n_heads);
+  if (c->cap_tokens < 16 || c->cap_tokens % 16 != 0 || c->cap_tokens > (int64_t)1 << 30)
+    return fail(FMD_E_SHAPE, "session %d: cap_tokens %lld (positive multiple of 16, <= 2^30)",
+                idx, (long long)c->cap_tokens);
+  if (c->len_tokens < 0 || c->len_tokens > c->cap_tokens || c->head_tokens < 0 ||
+      c->head_tokens >= c->cap_tokens)
+    return fail(FMD_E_INVAL, "session %d: ring state len=%lld head=%lld out of range", idx,
+                (long long)c->len_tokens, (long long)c->head_tokens);
+  return FMD_OK;
+}
+
+int check_tensor(const void* p, int idx, const char* name) {
+  if (!p) return fail(FMD_E_INVAL, "session %d: %s is NULL", idx, name);
+  if (!aligned16(p)) return fail(FMD_E_ALIGN, "session %d: %s not 16-byte aligned", idx, name);
+  return FMD_OK;
+}
+
+int check_step(const fmd_unit_step* u, int idx, bool need_z) {
+  int rc;
+  if ((rc = check_cache(u->cache, idx))) return rc;
+  if ((rc = check_tensor(u->q, idx, "q"))) return rc;
+  if ((rc = check_tensor(u->k_u, idx, "k_u"))) return rc;
+  if ((rc = check_tensor(u->v_u, idx, "v_u"))) return rc;
+  if (need_z && (rc = check_tensor(u->z, idx, "z"))) return rc;
+  if (u->n_video < 0 || u->n_audio < 0 || (int64_t)u->n_video + u->n_audio < 1 ||
+      (int64_t)u->n_video + u->n_audio > (1 << 24))
+    return fail(FMD_E_INVAL, "session %d: n_video=%d n_audio=%d (need 1 <= n_q <= 2^24)", idx,
+                u->n_video, u->n_audio);
+  if (need_z && !(u->h > 0.f && isfinite(u->h)))
+    return fail(FMD_E_INVAL, "session %d: step size h=%g must be finite and > 0", idx, u->h);
+  return FMD_OK;
+}
+
+int check_same_shape(const fmd_kv_cache* c0, const fmd_kv_cache* c, int idx) {
+  if (c->n_heads != c0->n_heads || c->head_dim != c0->head_dim)
+    return fail(FMD_E_SHAPE, "session %d: heads %dx%d differ from session 0's %dx%d", idx,
+                c->n_heads, c->head_dim, c0->n_heads, c0->head_dim);
+  return FMD_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Planning.
+// ---------------------------------------------------------------------------
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+struct SessPlan {
+  int n_q, npad;
+  int seg_lo[2], seg_hi[2];
+  int nwin[3], nwin_total;
+  int n_qblk, nsplit;
+  size_t off_vt, off_o, off_opart, off_lse;   // workspace offsets
+};
+
+int nwin_of(int lo, int hi) {
+  if (hi <= lo) return 0;
+  const int start = lo & ~15;
+  return (hi - start + kAttnWindow - 1) / kAttnWindow;
+}
+
+void plan_session(const fmd_kv_cache* c, int n_q, SessPlan& p) {
+  const int64_t cap = c->cap_tokens, len = c->len_tokens, head = c->head_tokens;
+  p.n_q = n_q;
+  p.npad = (n_q + 15) & ~15;
+  p.seg_lo[0] = p.seg_hi[0] = p.seg_lo[1] = p.seg_hi[1] = 0;
+  if (len > 0) {
+    const int64_t start = ((head - len) % cap + cap) % cap;
+    if (start + len <= cap) {
+      p.seg_lo[0] = (int)start;
+      p.seg_hi[0] = (int)(start + len);
+    } else {
+      p.seg_lo[0] = (int)start;
+      p.seg_hi[0] = (int)cap;
+      p.seg_lo[1] = 0;
+      p.seg_hi[1] = (int)(start + len - cap);
+    }
+  }
+  p.nwin[0] = nwin_of(p.seg_lo[0], p.seg_hi[0]);
+  p.nwin[1] = nwin_of(p.seg_lo[1], p.seg_hi[1]);
+  p.nwin[2] = (n_q + kAttnWindow - 1) / kAttnWindow;
+  p.nwin_total = p.nwin[0] + p.nwin[1] + p.nwin[2];
+  p.n_qblk = (n_q + kAttnBlockM - 1) / kAttnBlockM;
+  p.nsplit = 1;
+}
+
+int env_int(const char* name, int dflt) {
+  const char* v = getenv(name);
+  if (!v || !*v) return dflt;
+  return atoi(v);
+}
+
+// Key splits: enough work items to keep every CU busy for several rounds,
+// with at least kMinWindows windows per item.  Depends only on the shapes.
+void choose_splits(std::vector<SessPlan>& plans, int H) {
+  constexpr int kMinWindows = 16;
+  const int target_items = env_int("FMD_ATTN_TARGET_ITEMS", 4 * kTargetCUs);
+  const int forced = env_int("FMD_ATTN_SPLIT", 0);
+  double work = 0;
+  for (auto& p : plans) work += (double)H * p.n_qblk * p.nwin_total;
+  const double per_item = work / target_items;
+  for (auto& p : plans) {
+    int ns;
+    if (forced > 0) {
+      ns = forced;
+    } else {
+      ns = (int)ceil(p.nwin_total / (per_item > 1 ? per_item : 1.0));
+      ns = std::min(ns, std::max(1, p.nwin_total / kMinWindows));
+    }
+    p.nsplit = std::max(1, std::min(ns, p.nwin_total));
+  }
+}
+
+// Workspace layout, sessions in order.  With o_external, O goes to the
+// caller's buffer and takes no workspace.
+size_t layout_workspace(std::vector<SessPlan>& plans, int H, int hd, bool o_external) {
+  size_t off = 0;
+  for (auto& p : plans) {
+    p.off_vt = off;
+    off = align256(off + (size_t)H * p.npad * hd * 2);
+    p.off_o = off;
+    if (!o_external) off = align256(off + (size_t)p.n_q * H * hd * 2);
+    p.off_opart = p.off_lse = off;
+    if (p.nsplit > 1) {
+      off = align256(off + (size_t)p.nsplit * p.n_q * H * hd * 4);
+      p.off_lse = off;
+      off = align256(off + (size_t)p.nsplit * p.n_q * H * 4);
+    }
+  }
+  return off;
+}
+
+int plan_steps(const fmd_unit_step* units, int n, bool o_external, std::vector<SessPlan>& plans,
+               size_t* bytes) {
+  const int H = units[0].cache->n_heads, hd = units[0].cache->head_dim;
+  plans.resize(n);
+  for (int i = 0; i < n; ++i)
+    plan_session(units[i].cache, units[i].n_video + units[i].n_audio, plans[i]);
+  choose_splits(plans, H);
+  *bytes = layout_workspace(plans, H, hd, o_external);
+  return FMD_OK;
+}
+
+int validate_steps(const fmd_unit_step* units, int n, bool need_z) {
+  if (!units) return fail(FMD_E_INVAL, "units is NULL");
+  if (n < 1 || n > FMD_MAX_SESSIONS)
+    return fail(FMD_E_INVAL, "n_units=%d (must be 1..%d)", n, FMD_MAX_SESSIONS);
+  int rc;
+  for (int i = 0; i < n; ++i) {
+    if ((rc = check_step(&units[i], i, need_z))) return rc;
+    if (i && (rc = check_same_shape(units[0].cache, units[i].cache, i))) return rc;
+  }
+  return FMD_OK;
+}
+
+int check_workspace(void* ws, size_t have, size_t need) {
+  if (need == 0) return FMD_OK;
+  if (!ws) return fail(FMD_E_WORKSPACE, "workspace is NULL but %zu bytes are needed", need);
+  if ((reinterpret_cast<uintptr_t>(ws) & 255u) != 0)
+    return fail(FMD_E_ALIGN, "workspace not 256-byte aligned");
+  if (have < need)
+    return fail(FMD_E_WORKSPACE, "workspace has %zu bytes, %zu needed", have, need);
+  return FMD_OK;
+}
+
+// Enqueue the step kernels (validation already done).  o_out != nullptr:
+// attention only, O to the caller's buffer.
+int enqueue_steps(const fmd_unit_step* units, int n, const std::vector<SessPlan>& plans,
+                  const void* w_o, char* ws, bf16* o_out, hipStream_t st) {
+  const int H = units[0].cache->n_heads, hd = units[0].cache->head_dim;
+  const int d = H * hd;
+  const float scale_log2 = (float)(1.4426950408889634 / sqrt((double)hd));
+  int64_t o_row = 0;
+  for (int c0 = 0; c0 < n; c0 += kMaxSessPerLaunch) {
+    const int cn = std::min(kMaxSessPerLaunch, n - c0);
+    VtArgs va = {};
+    AttnArgs aa = {};
+    CombineArgs ca = {};
+    ProjArgs pa = {};
+    va.n_sess = aa.n_sess = ca.n_sess = pa.n_sess = cn;
+    va.H = aa.H = ca.H = H;
+    aa.scale_log2 = scale_log2;
+    pa.d = d;
+    pa.w = static_cast<const bf16*>(w_o);
+    bool any_split = false;
+    for (int k = 0; k < cn; ++k) {
+      const fmd_unit_step& u = units[c0 + k];
+      const SessPlan& p = plans[c0 + k];
+      const fmd_kv_cache* c = u.cache;
+      bf16* vt = reinterpret_cast<bf16*>(ws + p.off_vt);
+      bf16* o = o_out ? o_out + o_row * d : reinterpret_cast<bf16*>(ws + p.off_o);
+      o_row += p.n_q;
+
+      va.s[k] = VtSess{static_cast<const bf16*>(u.v_u), vt, p.n_q, p.npad / 16, va.items, 0};
+      va.items += H * (p.npad / 16);
+
+      AttnSess& as = aa.s[k];
+      as.q = static_cast<const bf16*>(u.q);
+      as.k_u = static_cast<const bf16*>(u.k_u);
+      as.vt_u = vt;
+      as.ring_k = static_cast<const bf16*>(c->k);
+      as.ring_v = static_cast<const bf16*>(c->v);
+      as.o = o;
+      as.opart = reinterpret_cast<float*>(ws + p.off_opart);
+      as.lse = reinterpret_cast<float*>(ws + p.off_lse);
+      as.cap = c->cap_tokens;
+      as.n_q = p.n_q;
+      as.npad = p.npad;
+      for (int t = 0; t < 2; ++t) {
+        as.seg_lo[t] = p.seg_lo[t];
+        as.seg_hi[t] = p.seg_hi[t];
+      }
+      for (int t = 0; t < 3; ++t) as.nwin[t] = p.nwin[t];
+      as.nwin_total = p.nwin_total;
+      as.n_qblk = p.n_qblk;
+      as.nsplit = p.nsplit;
+      as.item0 = aa.items;
+      aa.items += H * p.nsplit * p.n_qblk;
+
+      ca.s[k] = CombineSess{as.opart, as.lse, o, p.n_q, p.nsplit, ca.items, 0};
+      if (p.nsplit > 1) {
+        ca.items += p.n_q * H;
+        any_split = true;
+      }
+
+      const int mtiles = (p.n_q + kProjTile - 1) / kProjTile;
+      const int ntiles = (d + kProjTile - 1) / kProjTile;
+      pa.s[k] = ProjSess{o, u.z, p.n_q, mtiles, pa.items, u.h};
+      pa.items += mtiles * ntiles;
+    }
+    // Sessions without splits take no combine items; the combine kernel finds
+    // its session by item0, so give them an empty range at the current end.
+    int rc;
+    if ((rc = timed_launch(FMD_KERNEL_VT, st, [&] { return launch_vt(va, hd, st); }))) return rc;
+    if ((rc = timed_launch(FMD_KERNEL_ATTN, st, [&] { return launch_attn(aa, hd, st); })))
+      return rc;
+    if (any_split &&
+        (rc = timed_launch(FMD_KERNEL_COMBINE, st, [&] { return launch_combine(ca, hd, st); })))
+      return rc;
+    if (!o_out &&
+        (rc = timed_launch(FMD_KERNEL_PROJ, st, [&] { return launch_proj(pa, st); })))
+      return rc;
+  }
+  return FMD_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Append.
+// ---------------------------------------------------------------------------
+int check_append(const fmd_kv_cache* c, const void* ks, const void* vs, int64_t T, int idx) {
+  int rc;
+  if ((rc = check_cache(c, idx))) return rc;
+  if ((rc = check_tensor(ks, idx, "k_slice"))) return rc;
+  if ((rc = check_tensor(vs, idx, "v_slice"))) return rc;
+  if (T < 1) return fail(FMD_E_INVAL, "session %d: slice of %lld tokens", idx, (long long)T);
+  if (T > c->cap_tokens)
+    return fail(FMD_E_CAPACITY, "session %d: slice of %lld tokens exceeds capacity %lld", idx,
+                (long long)T, (long long)c->cap_tokens);
+  return FMD_OK;
+}
+
+// Enqueue appends (validated) and advance each cache's host state.
+int enqueue_appends(fmd_kv_cache* const* caches, const void* const* ks, const void* const* vs,
+                    const int64_t* T, int n, hipStream_t st) {
+  const int H = caches[0]->n_heads, hd = caches[0]->head_dim;
+  for (int c0 = 0; c0 < n; c0 += kMaxSessPerLaunch) {
+    const int cn = std::min(kMaxSessPerLaunch, n - c0);
+    AppendArgs a = {};
+    a.n_sess = cn;
+    a.H = H;
+    for (int k = 0; k < cn; ++k) {
+      const fmd_kv_cache* c = caches[c0 + k];
+      const int64_t cap = c->cap_tokens, head = c->head_tokens, t = T[c0 + k];
+      const int64_t nb_ring = cap / 16;
+      const int64_t blk0 = head / 16;
+      const int64_t blk_last = (head + t - 1) / 16;            // linear (unwrapped)
+      const int64_t nblk = std::min(blk_last - blk0 + 1, nb_ring);
+      a.s[k] = AppendSess{static_cast<const bf16*>(ks[c0 + k]), static_cast<const bf16*>(vs[c0 + k]),
+                          static_cast<bf16*>(c->k), static_cast<bf16*>(c->v), cap, (int32_t)t,
+                          (int32_t)head, (int32_t)blk0, (int32_t)nblk, a.items, 0};
+      a.items += H * (int)nblk;
+    }
+    int rc = timed_launch(FMD_KERNEL_APPEND, st, [&] { return launch_append(a, hd, st); });
+    if (rc) return rc;
+    for (int k = 0; k < cn; ++k) {
+      fmd_kv_cache* c = caches[c0 + k];
+      const int64_t t = T[c0 + k];
+      c->head_tokens = (c->head_tokens + t) % c->cap_tokens;
+      c->len_tokens = std::min(c->len_tokens + t, c->cap_tokens);
+    }
+  }
+  return FMD_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* fmd_version(void) { return "0.1.0"; }
+
+const char* fmd_strerror(int status) {
+  switch (status) {
+    case FMD_OK: return "ok";
+    case FMD_E_INVAL: return "invalid argument";
+    case FMD_E_SHAPE: return "unsupported or mismatched shape";
+    case FMD_E_CAPACITY: return "slice longer than the ring capacity";
+    case FMD_E_ALIGN: return "pointer not aligned";
+    case FMD_E_WORKSPACE: return "workspace missing or too small";
+    case FMD_E_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+const char* fmd_last_error(void) { return g_last_error.c_str(); }
+
+int fmd_kv_append(fmd_kv_cache* cache, const void* k_slice, const void* v_slice,
+                  int64_t n_tokens, void* stream) {
+  g_last_error.clear();
+  int rc = check_append(cache, k_slice, v_slice, n_tokens, 0);
+  if (rc) return rc;
+  fmd_kv_cache* cs[1] = {cache};
+  const void* ks[1] = {k_slice};
+  const void* vs[1] = {v_slice};
+  int64_t ts[1] = {n_tokens};
+  return enqueue_appends(cs, ks, vs, ts, 1, static_cast<hipStream_t>(stream));
+}
+
+int fmd_kv_append_batched(fmd_kv_cache* const* caches, const void* const* k_slices,
+                          const void* const* v_slices, const int64_t* n_tokens,
+                          int32_t n_sessions, void* stream) {
+  g_last_error.clear();
+  if (!caches || !k_slices || !v_slices || !n_tokens)
+    return fail(FMD_E_INVAL, "NULL array argument");
+  if (n_sessions < 1 || n_sessions > FMD_MAX_SESSIONS)
+    return fail(FMD_E_INVAL, "n_sessions=%d (must be 1..%d)", n_sessions, FMD_MAX_SESSIONS);
+  int rc;
+  for (int i = 0; i < n_sessions; ++i) {
+    if ((rc = check_append(caches[i], k_slices[i], v_slices[i], n_tokens[i], i))) return rc;
+    if (i && (rc = check_same_shape(caches[0], caches[i], i))) return rc;
+    for (int j = 0; j < i; ++j)
+      if (caches[j] == caches[i])
+        return fail(FMD_E_INVAL, "session %d: same cache as session %d", i, j);
+  }
+  return enqueue_appends(caches, k_slices, v_slices, n_tokens, n_sessions,
+                         static_cast<hipStream_t>(stream));
+}
+
+int fmd_workspace_bytes(const fmd_unit_step* units, int32_t n_units, size_t* out_bytes) {
+  g_last_error.clear();
+  if (!out_bytes) return fail(FMD_E_INVAL, "out_bytes is NULL");
+  int rc = validate_steps(units, n_units, false);
+  if (rc) return rc;
+  std::vector<SessPlan> plans;
+  return plan_steps(units, n_units, false, plans, out_bytes);
+}
+
+int fmd_denoise_step(const fmd_unit_step* units, int32_t n_units, const void* w_o,
+                     void* workspace, size_t workspace_bytes, void* stream) {
+  g_last_error.clear();
+  int rc = validate_steps(units, n_units, true);
+  if (rc) return rc;
+  if ((rc = check_tensor(w_o, 0, "w_o"))) return rc;
+  std::vector<SessPlan> plans;
+  size_t need = 0;
+  plan_steps(units, n_units, false, plans, &need);
+  if ((rc = check_workspace(workspace, workspace_bytes, need))) return rc;
+  return enqueue_steps(units, n_units, plans, w_o, static_cast<char*>(workspace), nullptr,
+                       static_cast<hipStream_t>(stream));
+}
+
+int fmd_attention(const fmd_unit_step* units, int32_t n_units, void* o_out, void* workspace,
+                  size_t workspace_bytes, void* stream) {
+  g_last_error.clear();
+  int rc = validate_steps(units, n_units, false);
+  if (rc) return rc;
+  if ((rc = check_tensor(o_out, 0, "o_out"))) return rc;
+  std::vector<SessPlan> plans;
+  size_t need = 0;
+  plan_steps(units, n_units, true, plans, &need);
+  if ((rc = check_workspace(workspace, workspace_bytes, need))) return rc;
+  return enqueue_steps(units, n_units, plans, nullptr, static_cast<char*>(workspace),
+                       static_cast<bf16*>(o_out), static_cast<hipStream_t>(stream));
+}
+
+static int validate_unit_io(const fmd_unit_io* ss, int n, int n_steps) {
+  if (!ss) return fail(FMD_E_INVAL, "sessions is NULL");
+  if (n < 1 || n > FMD_MAX_SESSIONS)
+    return fail(FMD_E_INVAL, "n_sessions=%d (must be 1..%d)", n, FMD_MAX_SESSIONS);
+  if (n_steps < 1) return fail(FMD_E_INVAL, "n_steps=%d (must be >= 1)", n_steps);
+  int rc;
+  for (int i = 0; i < n; ++i) {
+    const fmd_unit_io& s = ss[i];
+    if ((rc = check_cache(s.cache, i))) return rc;
+    if (i && (rc = check_same_shape(ss[0].cache, s.cache, i))) return rc;
+    for (int j = 0; j < i; ++j)
+      if (ss[j].cache == s.cache) return fail(FMD_E_INVAL, "session %d: same cache as %d", i, j);
+    if (s.slice_tokens < 0)
+      return fail(FMD_E_INVAL, "session %d: slice_tokens %lld", i, (long long)s.slice_tokens);
+    if (s.slice_tokens > 0 &&
+        (rc = check_append(s.cache, s.k_slice, s.v_slice, s.slice_tokens, i)))
+      return rc;
+    if (s.step_stride_elems < 0 || (s.step_stride_elems * 2) % 16 != 0)
+      return fail(FMD_E_ALIGN, "session %d: step stride %lld elements (>= 0, multiple of 8)", i,
+                  (long long)s.step_stride_elems);
+    if (!s.h) return fail(FMD_E_INVAL, "session %d: h is NULL", i);
+    for (int k = 0; k < n_steps; ++k)
+      if (!(s.h[k] > 0.f && isfinite(s.h[k])))
+        return fail(FMD_E_INVAL, "session %d: h[%d]=%g must be finite and > 0", i, k, s.h[k]);
+    fmd_unit_step u = {s.cache, s.q, s.k_u, s.v_u, s.z, s.n_video, s.n_audio, s.h[0]};
+    if ((rc = check_step(&u, i, true))) return rc;
+  }
+  return FMD_OK;
+}
+
+// The post-append ring states of a unit's sessions (for planning).
+static void post_append_steps(const fmd_unit_io* ss, int n, std::vector<fmd_kv_cache>& after,
+                              std::vector<fmd_unit_step>& steps) {
+  after.resize(n);
+  steps.resize(n);
+  for (int i = 0; i < n; ++i) {
+    after[i] = *ss[i].cache;
+    if (ss[i].slice_tokens > 0) {
+      after[i].head_tokens = (after[i].head_tokens + ss[i].slice_tokens) % after[i].cap_tokens;
+      after[i].len_tokens = std::min(after[i].len_tokens + ss[i].slice_tokens, after[i].cap_tokens);
+    }
+    steps[i] = fmd_unit_step{&after[i], ss[i].q, ss[i].k_u, ss[i].v_u, ss[i].z,
+                             ss[i].n_video, ss[i].n_audio, ss[i].h[0]};
+  }
+}
+
+int fmd_unit_workspace_bytes(const fmd_unit_io* sessions, int32_t n_sessions, size_t* out_bytes) {
+  g_last_error.clear();
+  if (!out_bytes) return fail(FMD_E_INVAL, "out_bytes is NULL");
+  int rc = validate_unit_io(sessions, n_sessions, 1);
+  if (rc) return rc;
+  std::vector<fmd_kv_cache> after;
+  std::vector<fmd_unit_step> steps;
+  post_append_steps(sessions, n_sessions, after, steps);
+  std::vector<SessPlan> plans;
+  return plan_steps(steps.data(), n_sessions, false, plans, out_bytes);
+}
+
+int fmd_denoise_unit(fmd_unit_io* sessions, int32_t n_sessions, int32_t n_steps, const void* w_o,
+                     void* workspace, size_t workspace_bytes, void* stream) {
+  g_last_error.clear();
+  int rc = validate_unit_io(sessions, n_sessions, n_steps);
+  if (rc) return rc;
+  if ((rc = check_tensor(w_o, 0, "w_o"))) return rc;
+  std::vector<fmd_kv_cache> after;
+  std::vector<fmd_unit_step> steps;
+  post_append_steps(sessions, n_sessions, after, steps);
+  std::vector<SessPlan> plans;
+  size_t need = 0;
+  plan_steps(steps.data(), n_sessions, false, plans, &need);
+  if ((rc = check_workspace(workspace, workspace_bytes, need))) return rc;
+
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  std::vector<fmd_kv_cache*> caches;
+  std::vector<const void*> ks, vs;
+  std::vector<int64_t> ts;
+  for (int i = 0; i < n_sessions; ++i) {
+    if (sessions[i].slice_tokens > 0) {
+      caches.push_back(sessions[i].cache);
+      ks.push_back(sessions[i].k_slice);
+      vs.push_back(sessions[i].v_slice);
+      ts.push_back(sessions[i].slice_tokens);
+    }
+  }
+  if (!caches.empty() &&
+      (rc = enqueue_appends(caches.data(), ks.data(), vs.data(), ts.data(), (int)caches.size(), st)))
+    return rc;
+  for (int s = 0; s < n_steps; ++s) {
+    for (int i = 0; i < n_sessions; ++i) {
+      const int64_t off = (int64_t)s * sessions[i].step_stride_elems;
+      steps[i].cache = sessions[i].cache;   // now in its post-append state
+      steps[i].q = static_cast<const bf16*>(sessions[i].q) + off;
+      steps[i].k_u = static_cast<const bf16*>(sessions[i].k_u) + off;
+      steps[i].v_u = static_cast<const bf16*>(sessions[i].v_u) + off;
+      steps[i].h = sessions[i].h[s];
+    }
+    if ((rc = enqueue_steps(steps.data(), n_sessions, plans, w_o, static_cast<char*>(workspace),
+                            nullptr, st)))
+      return rc;
+  }
+  return FMD_OK;
+}
+
+int fmd_profile_enable(int enable) {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  for (auto& r : g_prof) {
+    g_event_pool.push_back(r.a);
+    g_event_pool.push_back(r.b);
+  }
+  g_prof.clear();
+  g_prof_on = enable != 0;
+  return FMD_OK;
+}
+
+int fmd_profile_read(int kernel_class, double* total_ms, int64_t* launches) {
+  if (!total_ms || !launches) return fail(FMD_E_INVAL, "NULL output");
+  if (kernel_class < 0 || kernel_class >= FMD_KERNEL_COUNT)
+    return fail(FMD_E_INVAL, "kernel class %d", kernel_class);
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  double tot = 0;
+  int64_t n = 0;
+  for (auto& r : g_prof) {
+    if (r.cls != kernel_class) continue;
+    hipError_t e = hipEventSynchronize(r.b);
+    if (e != hipSuccess) return fail(FMD_E_HIP, "event wait: %s", hipGetErrorString(e));
+    float ms = 0;
+    e = hipEventElapsedTime(&ms, r.a, r.b);
+    if (e != hipSuccess) return fail(FMD_E_HIP, "event time: %s", hipGetErrorString(e));
+    tot += ms;
+    ++n;
+  }
+  *total_ms = tot;
+  *launches = n;
+  return FMD_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,164 @@
+// Internal declarations shared by the HIP sources of libfmd (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/fmd.h"
+
+namespace fmd {
+
+// Sessions whose descriptors travel by value in one launch's kernel arguments
+// (kept well under the 4 KiB kernel-argument limit).  Calls with more sessions
+// are issued as several launches.
+constexpr int kMaxSessPerLaunch = 16;
+constexpr int kNumXcd = 8;          // MI355X: 8 XCDs x 32 CUs, round-robin dispatch
+constexpr int kTargetCUs = 256;     // split heuristics assume a full MI355X
+
+typedef __bf16 bf16;
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
+typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4;
+
+// Map a hardware block id to a logical work id so that each XCD runs a
+// contiguous range of logical ids (blocks are dispatched to XCDs round-robin).
+// Work that shares data is then placed at adjacent logical ids and lands in
+// the same XCD's L2 at about the same time.  A bijection on [0, n).
+__device__ __forceinline__ int xcd_remap(int bid, int n) {
+  const int per = (n + kNumXcd - 1) / kNumXcd;
+  const int tall = n % kNumXcd == 0 ? kNumXcd : n % kNumXcd;
+  const int xcd = bid % kNumXcd;
+  const int local = bid / kNumXcd;
+  return xcd < tall ? xcd * per + local
+                    : tall * per + (xcd - tall) * (per - 1) + local;
+}
+
+__device__ __forceinline__ f32x16 mfma32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ u32x4 ld16(const void* p) {
+  return *reinterpret_cast<const u32x4*>(p);
+}
+__device__ __forceinline__ void st16(void* p, u32x4 v) {
+  *reinterpret_cast<u32x4*>(p) = v;
+}
+
+// ---------------------------------------------------------------------------
+// Launch descriptors (passed by value).
+// ---------------------------------------------------------------------------
+
+struct AppendSess {
+  const bf16* ks;   // [T][H][hd]
+  const bf16* vs;
+  bf16* ck;         // [H][cap][hd]
+  bf16* cv;         // [H][cap/16][hd][16]
+  int64_t cap;
+  int32_t T;
+  int32_t head0;    // slot of the slice's first token
+  int32_t blk0;     // first 16-slot block touched
+  int32_t nblk;     // blocks touched (<= cap/16)
+  int32_t item0;    // first work item of this session
+  int32_t pad_;
+};
+struct AppendArgs {
+  AppendSess s[kMaxSessPerLaunch];
+  int32_t n_sess;
+  int32_t H;
+  int32_t items;
+};
+
+struct VtSess {
+  const bf16* v;    // [n][H][hd]
+  bf16* vt;         // [H][npad/16][hd][16]
+  int32_t n;
+  int32_t nblk;     // npad/16
+  int32_t item0;
+  int32_t pad_;
+};
+struct VtArgs {
+  VtSess s[kMaxSessPerLaunch];
+  int32_t n_sess;
+  int32_t H;
+  int32_t items;
+};
+
+struct AttnSess {
+  const bf16* q;      // [n_q][H][hd]
+  const bf16* k_u;    // [n_q][H][hd]
+  const bf16* vt_u;   // [H][npad/16][hd][16]   (workspace)
+  const bf16* ring_k; // [H][cap][hd]
+  const bf16* ring_v; // [H][cap/16][hd][16]
+  bf16* o;            // [n_q][H][hd]            (when nsplit == 1)
+  float* opart;       // [nsplit][n_q][H][hd]    (when nsplit > 1)
+  float* lse;         // [nsplit][n_q][H]
+  int64_t cap;
+  int32_t n_q;
+  int32_t npad;       // n_q rounded up to 16
+  int32_t seg_lo[2];  // valid ring slots: [seg_lo[i], seg_hi[i])
+  int32_t seg_hi[2];
+  int32_t nwin[3];    // 64-key windows over ring seg 0, ring seg 1, unit keys
+  int32_t nwin_total;
+  int32_t n_qblk;
+  int32_t nsplit;
+  int32_t item0;
+};
+struct AttnArgs {
+  AttnSess s[kMaxSessPerLaunch];
+  int32_t n_sess;
+  int32_t H;
+  int32_t items;
+  float scale_log2;   // log2(e) / sqrt(head_dim)
+};
+
+struct CombineSess {
+  const float* opart;
+  const float* lse;
+  bf16* o;
+  int32_t n_q;
+  int32_t nsplit;
+  int32_t item0;      // first (row, head) group handled by this session
+  int32_t pad_;
+};
+struct CombineArgs {
+  CombineSess s[kMaxSessPerLaunch];
+  int32_t n_sess;
+  int32_t H;
+  int32_t items;
+};
+
+struct ProjSess {
+  const bf16* o;      // [n_q][d]
+  float* z;           // [n_q][d]
+  int32_t n_q;
+  int32_t n_mtiles;
+  int32_t item0;
+  float h;
+};
+struct ProjArgs {
+  ProjSess s[kMaxSessPerLaunch];
+  const bf16* w;      // [d][d], [d_out][d_in]
+  int32_t n_sess;
+  int32_t d;
+  int32_t items;
+};
+
+// Host-side launchers (defined next to their kernels).
+hipError_t launch_append(const AppendArgs& a, int head_dim, hipStream_t st);
+hipError_t launch_vt(const VtArgs& a, int head_dim, hipStream_t st);
+hipError_t launch_attn(const AttnArgs& a, int head_dim, hipStream_t st);
+hipError_t launch_combine(const CombineArgs& a, int head_dim, hipStream_t st);
+hipError_t launch_proj(const ProjArgs& a, hipStream_t st);
+
+// Attention tiling shared by host planning and the kernel.
+constexpr int kAttnWaves = 8;
+constexpr int kAttnThreads = kAttnWaves * 64;
+constexpr int kAttnRowsPerWave = 32;
+constexpr int kAttnBlockM = kAttnWaves * kAttnRowsPerWave;   // 256 query rows per block
+constexpr int kAttnWindow = 64;                              // keys per window
+
+// Projection tiling.
+constexpr int kProjTile = 128;
+
+}  // namespace fmd

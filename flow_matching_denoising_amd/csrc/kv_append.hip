@@ -1,0 +1,131 @@
+// Ring append of the thinker's K/V slice, and the 16-token transpose of the
+// unit's own values.
+//
+// The performer writes each incoming K/V slice into its preallocated local
+// cache at the slice's position, before the solver runs [Wan-Streamer v0.2:
+// Higher Resolution, Same Latency (nanless digest), 方法概述和架构;
+// Wan-Streamer v0.2 (zhao9797 blog), Infra].  Token t of a slice goes to ring
+// slot (head + t) mod cap of every head.
+//
+// Layouts: K ring [H][cap][hd]; V ring in 16-slot blocks stored feature-major,
+// [H][cap/16][hd][16], so that the attention kernel reads V with keys
+// contiguous (the contraction axis of P*V) without transposing per step.  One
+// work-group handles one (session, head, 16-slot block): it copies the K rows
+// of the block's written slots directly (16-byte lanes), stages the V rows in
+// LDS and writes the block back transposed with 16-byte stores.  A block that
+// is only partly covered by the slice keeps its other slots (read-merge-write
+// of the same 16 bytes by the same thread; blocks are never shared between
+// work-groups, also when T == cap and the slice wraps onto its own first block).
+#include "fmd_internal.h"
+
+namespace fmd {
+
+template <int HD>
+__global__ __launch_bounds__(2 * HD) void append_kernel(AppendArgs a) {
+  constexpr int PARTS = HD / 8;  // 16-byte parts of one token row
+  __shared__ __attribute__((aligned(16))) bf16 tile[16][HD + 8];
+
+  const int item = blockIdx.x;
+  int si = 0;
+#pragma unroll
+  for (int i = 1; i < kMaxSessPerLaunch; ++i)
+    if (i < a.n_sess && item >= a.s[i].item0) si = i;
+  const AppendSess& s = a.s[si];
+
+  const int local = item - s.item0;
+  const int h = local / s.nblk;
+  const int bi = local % s.nblk;
+  const int64_t nb_ring = s.cap / 16;
+  const int64_t pb = (s.blk0 + bi) % nb_ring;       // physical block
+  const int H = a.H;
+
+  // Load phase: thread -> (slot r of the block, 16-byte part).
+  {
+    const int r = threadIdx.x / PARTS;
+    const int part = threadIdx.x % PARTS;
+    const int64_t p = pb * 16 + r;
+    const int64_t tt = ((p - s.head0) % s.cap + s.cap) % s.cap;   // token index
+    if (tt < s.T) {
+      const int64_t src = (tt * H + h) * HD + part * 8;
+      st16(s.ck + ((int64_t)h * s.cap + p) * HD + part * 8, ld16(s.ks + src));
+      st16(&tile[r][part * 8], ld16(s.vs + src));
+    }
+  }
+  __syncthreads();
+
+  // Store phase: thread -> (feature e, half hh of the block's 16 slots).
+  {
+    const int e = threadIdx.x >> 1;
+    const int hh = threadIdx.x & 1;
+    bf16* dst = s.cv + (((int64_t)h * nb_ring + pb) * HD + e) * 16 + hh * 8;
+    unsigned written = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int64_t p = pb * 16 + hh * 8 + i;
+      const int64_t tt = ((p - s.head0) % s.cap + s.cap) % s.cap;
+      written |= (tt < s.T ? 1u : 0u) << i;
+    }
+    if (written == 0) return;
+    union { u32x4 v; bf16 b[8]; } u;
+    if (written != 0xFFu) u.v = ld16(dst);
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      if (written & (1u << i)) u.b[i] = tile[hh * 8 + i][e];
+    st16(dst, u.v);
+  }
+}
+
+// Unit values [n][H][hd] -> [H][npad/16][hd][16], zero beyond n.
+template <int HD>
+__global__ __launch_bounds__(2 * HD) void vt_kernel(VtArgs a) {
+  constexpr int PARTS = HD / 8;
+  __shared__ __attribute__((aligned(16))) bf16 tile[16][HD + 8];
+
+  const int item = blockIdx.x;
+  int si = 0;
+#pragma unroll
+  for (int i = 1; i < kMaxSessPerLaunch; ++i)
+    if (i < a.n_sess && item >= a.s[i].item0) si = i;
+  const VtSess& s = a.s[si];
+  const int local = item - s.item0;
+  const int h = local / s.nblk;
+  const int b = local % s.nblk;
+  const int H = a.H;
+  {
+    const int r = threadIdx.x / PARTS;
+    const int part = threadIdx.x % PARTS;
+    const int tok = b * 16 + r;
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (tok < s.n) v = ld16(s.v + ((int64_t)tok * H + h) * HD + part * 8);
+    st16(&tile[r][part * 8], v);
+  }
+  __syncthreads();
+  {
+    const int e = threadIdx.x >> 1;
+    const int hh = threadIdx.x & 1;
+    union { u32x4 v; bf16 b[8]; } u;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) u.b[i] = tile[hh * 8 + i][e];
+    st16(s.vt + (((int64_t)h * s.nblk + b) * HD + e) * 16 + hh * 8, u.v);
+  }
+}
+
+hipError_t launch_append(const AppendArgs& a, int head_dim, hipStream_t st) {
+  if (a.items <= 0) return hipSuccess;
+  if (head_dim == 128)
+    hipLaunchKernelGGL(append_kernel<128>, dim3(a.items), dim3(256), 0, st, a);
+  else
+    hipLaunchKernelGGL(append_kernel<64>, dim3(a.items), dim3(128), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_vt(const VtArgs& a, int head_dim, hipStream_t st) {
+  if (a.items <= 0) return hipSuccess;
+  if (head_dim == 128)
+    hipLaunchKernelGGL(vt_kernel<128>, dim3(a.items), dim3(256), 0, st, a);
+  else
+    hipLaunchKernelGGL(vt_kernel<64>, dim3(a.items), dim3(128), 0, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace fmd

@@ -1,0 +1,214 @@
+/*
+ * fmd.h -- C ABI of the performer's per-unit flow-matching denoise step
+ * (Wan-Streamer v0.2), built for one MI355X (gfx950).
+ *
+ * What the calls implement, by source page and section:
+ *  - fmd_kv_append / fmd_kv_append_batched: the performer writes the thinker's
+ *    compact K/V slice into its own preallocated cache at the slice's position
+ *    [Wan-Streamer v0.2: Higher Resolution, Same Latency (nanless digest),
+ *    方法概述和架构; Wan-Streamer v0.2 (zhao9797 blog), Infra].
+ *  - fmd_attention / fmd_denoise_step: the unit's noisy video and audio latent
+ *    tokens attend to all clean history and to each other (bidirectional inside
+ *    the unit) [Wan-Streamer (gongshangzheng blog), 3.3 Block-Causal
+ *    Transformer; 3.4 条件流匹配, cross-modal conditioning and clean context];
+ *    one dense projection gives the velocity of both modalities and an Euler
+ *    step moves z along the rectified-flow path [same page, 3.4].
+ *  - fmd_denoise_unit: one unit = the append, then the flow-matching solver
+ *    [same page, Fig. 2: the performer receives the slice and only runs the
+ *    solver].
+ *
+ * Conventions shared by every call
+ *  - Tensor pointers are DEVICE pointers owned by the caller.  The library
+ *    never allocates, frees or retains device memory; scratch space is the
+ *    caller's `workspace`.
+ *  - `stream` is a hipStream_t (NULL = the default stream).  Calls enqueue
+ *    work and return; results are valid once the stream reaches that point.
+ *  - Every argument is validated before anything is enqueued.  A non-zero
+ *    return means no kernel was launched and no host state (a cache's
+ *    len_tokens/head_tokens) changed.  fmd_last_error() then describes the
+ *    first failed check.  Errors of an already-enqueued launch are reported
+ *    as FMD_E_HIP.
+ *  - All tensor pointers must be 16-byte aligned (FMD_E_ALIGN otherwise).
+ *  - bf16 = IEEE binary32's upper 16 bits; fp32 = IEEE binary32.
+ *  - Calls on different caches are independent; one cache must not be used
+ *    by two host threads at once.
+ */
+#ifndef FMD_H
+#define FMD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FMD_MAX_SESSIONS 64   /* sessions per call */
+#define FMD_CACHE_BLOCK 16    /* tokens per block of the V cache layout */
+
+typedef enum {
+  FMD_OK = 0,
+  FMD_E_INVAL = -1,      /* null pointer, non-positive count, bad ring state */
+  FMD_E_SHAPE = -2,      /* head_dim not 64/128, heads or d mismatched, cap not a multiple of 16 */
+  FMD_E_CAPACITY = -3,   /* slice longer than the ring */
+  FMD_E_ALIGN = -4,      /* a pointer is not 16-byte aligned */
+  FMD_E_WORKSPACE = -5,  /* workspace missing or smaller than required */
+  FMD_E_HIP = -6         /* the HIP runtime reported an error */
+} fmd_status;
+
+/*
+ * One session's K/V ring.  The struct lives in host memory and is owned by
+ * the caller; k and v point to device memory the caller allocated.
+ *   k : bf16 [n_heads][cap_tokens][head_dim]              (token rows per head)
+ *   v : bf16 [n_heads][cap_tokens/16][head_dim][16]       (16-token blocks, each
+ *       stored feature-major: element (h, slot p, e) is at
+ *       ((h*(cap/16) + p/16)*head_dim + e)*16 + p%16)
+ *   head_dim   : 64 or 128
+ *   cap_tokens : ring capacity in tokens, a positive multiple of 16
+ *   len_tokens : valid tokens, 0..cap_tokens
+ *   head_tokens: slot the next token goes to, 0..cap_tokens-1
+ * The valid tokens are the len_tokens slots just before head_tokens (mod cap).
+ * The library updates len_tokens/head_tokens when it enqueues an append.
+ */
+typedef struct fmd_kv_cache {
+  void* k;
+  void* v;
+  int32_t n_heads;
+  int32_t head_dim;
+  int64_t cap_tokens;
+  int64_t len_tokens;
+  int64_t head_tokens;
+} fmd_kv_cache;
+
+/*
+ * Append one slice of n_tokens tokens to a ring: token t goes to slot
+ * (head + t) mod cap of every head; then head += n_tokens (mod cap) and
+ * len = min(len + n_tokens, cap).  Oldest tokens are overwritten.
+ *   k_slice, v_slice: bf16 [n_tokens][n_heads][head_dim], contiguous,
+ *                     token-major as the thinker's projection emits them.
+ * Errors: FMD_E_INVAL (null, n_tokens < 1, bad ring state), FMD_E_CAPACITY
+ * (n_tokens > cap), FMD_E_SHAPE, FMD_E_ALIGN, FMD_E_HIP.
+ */
+int fmd_kv_append(fmd_kv_cache* cache, const void* k_slice, const void* v_slice,
+                  int64_t n_tokens, void* stream);
+
+/* The same for n_sessions rings in one launch (sessions may differ in
+ * capacity, state and slice length; n_heads and head_dim must match).
+ * caches[i] is updated as by fmd_kv_append.  Same errors. */
+int fmd_kv_append_batched(fmd_kv_cache* const* caches, const void* const* k_slices,
+                          const void* const* v_slices, const int64_t* n_tokens,
+                          int32_t n_sessions, void* stream);
+
+/*
+ * One session's inputs for ONE solver step.
+ *   cache     : the session's ring in its post-append state (read only)
+ *   q, k_u, v_u: bf16 [n_q][n_heads][head_dim], the unit's queries and its own
+ *               keys/values, n_q = n_video + n_audio, rows video then audio
+ *   z         : fp32 [n_q][n_heads*head_dim], updated in place
+ *   h         : positive step size; the step is z <- z - h * v
+ */
+typedef struct fmd_unit_step {
+  const fmd_kv_cache* cache;
+  const void* q;
+  const void* k_u;
+  const void* v_u;
+  float* z;
+  int32_t n_video;
+  int32_t n_audio;
+  float h;
+} fmd_unit_step;
+
+/* Workspace bytes fmd_attention / fmd_denoise_step need for these units.
+ * Pure host arithmetic. Errors: FMD_E_INVAL, FMD_E_SHAPE. */
+int fmd_workspace_bytes(const fmd_unit_step* units, int32_t n_units, size_t* out_bytes);
+
+/*
+ * One solver step for n_units sessions:
+ *   O = attention(q, [valid ring || k_u], [valid ring || v_u]) per head, scale
+ *       1/sqrt(head_dim), no mask; fp32 softmax and accumulation, O rounded to
+ *       bf16;
+ *   v = O_flat * W_o^T with O_flat [n_q][d] (heads concatenated);
+ *   z <- z - h * v  (fp32).
+ *   w_o: bf16 [d][d] stored [d_out][d_in], d = n_heads*head_dim, shared.
+ *   workspace: device scratch of at least fmd_workspace_bytes() bytes.
+ * Errors: FMD_E_INVAL, FMD_E_SHAPE, FMD_E_ALIGN, FMD_E_WORKSPACE, FMD_E_HIP.
+ */
+int fmd_denoise_step(const fmd_unit_step* units, int32_t n_units, const void* w_o,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
+/* The attention part of fmd_denoise_step alone (z and h unused), writing
+ * O as bf16 [sum n_q][n_heads][head_dim], sessions in order.  Same errors. */
+int fmd_attention(const fmd_unit_step* units, int32_t n_units, void* o_out,
+                  void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * One session's inputs for a whole unit.
+ *   cache          : the session's ring (state before the append; updated)
+ *   k_slice/v_slice: bf16 [slice_tokens][n_heads][head_dim]; slice_tokens = 0
+ *                    means the unit appends nothing
+ *   q, k_u, v_u    : bf16 base pointers of step 0's [n_q][n_heads][head_dim]
+ *                    tensors; step s uses base + s*step_stride_elems
+ *                    (0 = the same tensors for every step)
+ *   z              : fp32 [n_q][d], holds eps on entry, the final latent on exit
+ *   h              : HOST array [n_steps] of positive step sizes, read during
+ *                    the call
+ */
+typedef struct fmd_unit_io {
+  fmd_kv_cache* cache;
+  const void* k_slice;
+  const void* v_slice;
+  int64_t slice_tokens;
+  const void* q;
+  const void* k_u;
+  const void* v_u;
+  int64_t step_stride_elems;
+  float* z;
+  int32_t n_video;
+  int32_t n_audio;
+  const float* h;
+} fmd_unit_io;
+
+/* Workspace bytes fmd_denoise_unit needs (pure host arithmetic). */
+int fmd_unit_workspace_bytes(const fmd_unit_io* sessions, int32_t n_sessions,
+                             size_t* out_bytes);
+
+/*
+ * One denoised unit for n_sessions sessions: one batched append, then
+ * n_steps solver steps, each as fmd_denoise_step with h[s].
+ * Errors: as fmd_kv_append and fmd_denoise_step; n_steps < 1 -> FMD_E_INVAL.
+ */
+int fmd_denoise_unit(fmd_unit_io* sessions, int32_t n_sessions, int32_t n_steps,
+                     const void* w_o, void* workspace, size_t workspace_bytes,
+                     void* stream);
+
+/* Static description of a status code (never NULL). */
+const char* fmd_strerror(int status);
+
+/* Detail of the last error on this host thread (empty string if none). */
+const char* fmd_last_error(void);
+
+/* Kernel classes that fmd_profile_* report on. */
+enum {
+  FMD_KERNEL_APPEND = 0,    /* ring append */
+  FMD_KERNEL_VT = 1,        /* 16-token transpose of the unit's values */
+  FMD_KERNEL_ATTN = 2,      /* attention main kernel */
+  FMD_KERNEL_COMBINE = 3,   /* merge of key-split partial results */
+  FMD_KERNEL_PROJ = 4,      /* projection GEMM with the Euler update */
+  FMD_KERNEL_COUNT = 5
+};
+
+/* Per-launch timing with HIP events recorded on the launch stream around
+ * every kernel of the classes above.  enable != 0 turns recording on (and
+ * clears earlier records); fmd_profile_read waits for the recorded events and
+ * returns the summed duration in ms and the launch count of one class. */
+int fmd_profile_enable(int enable);
+int fmd_profile_read(int kernel_class, double* total_ms, int64_t* launches);
+
+/* Library version, "major.minor.patch". */
+const char* fmd_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FMD_H */

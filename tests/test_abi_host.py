@@ -1,0 +1,180 @@
+"""Host-side checks of the C ABI (no GPU needed, no kernel is launched):
+the library loads and exports every function fmd.h declares, argument
+validation returns the documented codes without touching cache state, and the
+workspace sizing is consistent.  Pointers here are fake, aligned integers:
+every call is rejected before anything would touch device memory."""
+import ctypes
+import os
+import re
+import subprocess
+import tempfile
+
+import pytest
+
+import flow_matching_denoising_amd as fmd
+from flow_matching_denoising_amd import _Cache, _UnitIO, _UnitStep, _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fmd.h")
+
+FAKE = 0x10000000        # 256-byte aligned, never dereferenced
+
+
+def _declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(fmd_[a-z_0-9]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_function():
+    names = _declared_functions()
+    assert len(names) >= 12
+    for n in names:
+        assert hasattr(_lib, n), f"libfmd.so does not export {n}"
+    assert set(names) == set(fmd.EXPORTED)
+
+
+def test_strerror_and_version():
+    for code, name in fmd.STATUS.items():
+        assert fmd.strerror(code) and isinstance(fmd.strerror(code), str)
+    assert fmd.strerror(12345) == "unknown status"
+    assert re.match(r"^\d+\.\d+\.\d+$", fmd.version())
+
+
+def _cache(H=2, hd=64, cap=128, ln=96, head=96, k=FAKE, v=FAKE + 0x100000):
+    return _Cache(k, v, H, hd, cap, ln, head)
+
+
+def _append(c, T, ks=FAKE + 0x200000, vs=FAKE + 0x300000):
+    return fmd._kv_append(ctypes.byref(c), ks, vs, T, None)
+
+
+@pytest.mark.parametrize("mut,code", [
+    (dict(hd=96), -2), (dict(hd=0), -2), (dict(cap=100), -2), (dict(cap=0), -2),
+    (dict(H=0), -2), (dict(ln=129), -1), (dict(head=128), -1), (dict(head=-1), -1),
+    (dict(k=FAKE + 8), -4), (dict(v=0), -1),
+])
+def test_append_rejects_bad_cache(mut, code):
+    c = _cache(**mut)
+    before = (c.len_tokens, c.head_tokens)
+    assert _append(c, 32) == code
+    assert (c.len_tokens, c.head_tokens) == before
+    assert fmd._last_error().decode()
+
+
+@pytest.mark.parametrize("T,code", [(0, -1), (-5, -1), (129, -3)])
+def test_append_rejects_bad_slice(T, code):
+    c = _cache()
+    assert _append(c, T) == code
+    assert (c.len_tokens, c.head_tokens) == (96, 96)
+
+
+def test_append_rejects_misaligned_or_null_slice():
+    c = _cache()
+    assert _append(c, 32, ks=FAKE + 2) == -4
+    assert _append(c, 32, vs=0) == -1
+    assert (c.len_tokens, c.head_tokens) == (96, 96)
+
+
+def test_batched_append_rejects_mismatch_and_duplicates():
+    a, b = _cache(), _cache(H=3)
+    arr = (ctypes.POINTER(_Cache) * 2)(ctypes.pointer(a), ctypes.pointer(b))
+    ks = (ctypes.c_void_p * 2)(FAKE, FAKE)
+    ts = (ctypes.c_int64 * 2)(16, 16)
+    assert fmd._kv_append_batched(arr, ks, ks, ts, 2, None) == -2
+    arr2 = (ctypes.POINTER(_Cache) * 2)(ctypes.pointer(a), ctypes.pointer(a))
+    assert fmd._kv_append_batched(arr2, ks, ks, ts, 2, None) == -1
+    assert fmd._kv_append_batched(arr2, ks, ks, ts, 0, None) == -1
+    assert fmd._kv_append_batched(arr2, ks, ks, ts, 65, None) == -1
+    assert (a.len_tokens, a.head_tokens) == (96, 96)
+
+
+def _step(c, n_video=12, n_audio=4, h=1.0, q=FAKE, z=FAKE):
+    return _UnitStep(ctypes.pointer(c), q, FAKE, FAKE, z, n_video, n_audio, h)
+
+
+def _ws(units):
+    arr = (_UnitStep * len(units))(*units)
+    out = ctypes.c_size_t(0)
+    rc = fmd._workspace_bytes(arr, len(units), ctypes.byref(out))
+    return rc, out.value
+
+
+def test_workspace_bytes_is_host_arithmetic():
+    c = _cache(H=40, hd=128, cap=60416, ln=60416, head=0)
+    rc, n1 = _ws([_step(c, 920, 8)])
+    assert rc == 0 and n1 > 0
+    # V transpose (40 x 928 x 128 bf16) + O (928 x 5120 bf16) are always there.
+    assert n1 >= 40 * 928 * 128 * 2 + 928 * 5120 * 2
+    rc, n2 = _ws([_step(c, 920, 8), _step(_cache(H=40, hd=128, cap=944, ln=944, head=0), 920, 8)])
+    assert rc == 0 and n2 > n1
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(n_video=0, n_audio=0), -1), (dict(n_video=-1), -1), (dict(q=FAKE + 4), -4),
+    (dict(q=0), -1),
+])
+def test_step_validation(kw, code):
+    c = _cache()
+    rc, _ = _ws([_step(c, **kw)])
+    assert rc == code
+
+
+def test_denoise_step_checks_h_z_and_workspace():
+    c = _cache()
+    for kw, code in [(dict(h=0.0), -1), (dict(h=float("nan")), -1), (dict(z=0), -1)]:
+        arr = (_UnitStep * 1)(_step(c, **kw))
+        assert fmd._denoise_step(arr, 1, FAKE, FAKE, 1 << 30, None) == code
+    arr = (_UnitStep * 1)(_step(c))
+    assert fmd._denoise_step(arr, 1, FAKE, None, 0, None) == -5          # no workspace
+    assert fmd._denoise_step(arr, 1, FAKE, FAKE, 16, None) == -5         # too small
+    assert fmd._denoise_step(arr, 1, FAKE, FAKE + 16, 1 << 30, None) == -4   # misaligned
+    assert fmd._denoise_step(arr, 1, 0, FAKE, 1 << 30, None) == -1       # no W_o
+    # Mismatched heads across sessions.
+    arr2 = (_UnitStep * 2)(_step(c), _step(_cache(H=3)))
+    assert fmd._denoise_step(arr2, 2, FAKE, FAKE, 1 << 30, None) == -2
+
+
+def test_denoise_unit_validation_leaves_state():
+    c = _cache()
+    h = (ctypes.c_float * 2)(0.5, -0.5)
+    io = _UnitIO(ctypes.pointer(c), FAKE, FAKE, 32, FAKE, FAKE, FAKE, 0, FAKE, 12, 4,
+                 ctypes.cast(h, ctypes.POINTER(ctypes.c_float)))
+    arr = (_UnitIO * 1)(io)
+    assert fmd._denoise_unit(arr, 1, 2, FAKE, FAKE, 1 << 30, None) == -1   # h[1] < 0
+    assert fmd._denoise_unit(arr, 1, 0, FAKE, FAKE, 1 << 30, None) == -1   # no steps
+    assert (c.len_tokens, c.head_tokens) == (96, 96)
+    io.slice_tokens = 200
+    arr = (_UnitIO * 1)(io)
+    h[1] = 0.5
+    assert fmd._denoise_unit(arr, 1, 2, FAKE, FAKE, 1 << 30, None) == -3   # slice > cap
+    io.slice_tokens = 32
+    io.step_stride_elems = 3
+    arr = (_UnitIO * 1)(io)
+    assert fmd._denoise_unit(arr, 1, 2, FAKE, FAKE, 1 << 30, None) == -4   # unaligned stride
+    assert (c.len_tokens, c.head_tokens) == (96, 96)
+    io.step_stride_elems = 0
+    arr = (_UnitIO * 1)(io)
+    out = ctypes.c_size_t(0)
+    assert fmd._unit_workspace_bytes(arr, 1, ctypes.byref(out)) == 0 and out.value > 0
+
+
+def test_profile_read_rejects_bad_class():
+    ms, n = ctypes.c_double(0), ctypes.c_int64(0)
+    assert fmd._profile_read(99, ctypes.byref(ms), ctypes.byref(n)) == -1
+
+
+def test_device_code_has_no_packed_fp32_arithmetic():
+    # The kernels are built with packed-FP32 generation switched off; check
+    # the gfx950 assembly of our own sources for v_pk_{add,mul,fma}_f32.
+    from flow_matching_denoising_amd import _build
+    hipcc = _build._hipcc()
+    with tempfile.TemporaryDirectory() as td:
+        for name in ("attention.hip", "proj_euler.hip", "kv_append.hip"):
+            out = os.path.join(td, name + ".s")
+            cmd = [hipcc, *_build.COMMON, "--cuda-device-only", "-S",
+                   os.path.join(_build.CSRC, name), "-o", out]
+            subprocess.run(cmd, check=True, capture_output=True)
+            asm = open(out).read()
+            assert not re.search(r"v_pk_(add|mul|fma)_f32", asm), name
+            assert "scratch_" not in asm, f"{name}: register spills to scratch"

@@ -1,0 +1,175 @@
+"""GPU parity of the whole step and unit (append + S Euler steps) against the
+oracle, and the rectified-flow closed form on the GPU."""
+import numpy as np
+import pytest
+
+import oracle
+import workload
+from tests.pins import bits, random_bits
+
+import flow_matching_denoising_amd as fmd  # noqa: E402  (no fallback: fails if not built)
+import torch  # noqa: E402
+from tests.gpu_util import (DEV, assert_close, cache_logical, dev_bf16, host_f64,  # noqa: E402
+                            make_cache, rel_l2, stack_steps)
+
+pytestmark = pytest.mark.gpu
+
+
+def _unit_io(ui, si, cache, z):
+    s = si.shape
+    q = stack_steps(si.q)
+    ku = stack_steps(si.k_u)
+    vu = stack_steps(si.v_u)
+    sk = dev_bf16(si.slice_k) if si.slice_k is not None else None
+    sv = dev_bf16(si.slice_v) if si.slice_v is not None else None
+    return fmd.UnitIO(cache, sk, sv, q, ku, vu, z, list(s.h), n_audio=s.n_audio)
+
+
+def _run_unit(wl, poison=True, reuse=False):
+    ui = workload.make_inputs(wl, poison_invalid=poison, reuse_step_inputs=reuse)
+    caches, ios, zs = [], [], []
+    for si in ui.sessions:
+        c = make_cache(fmd, si.shape, si.ring_k, si.ring_v)
+        z = torch.from_numpy(si.eps.copy()).to(DEV)
+        caches.append(c)
+        zs.append(z)
+        ios.append(_unit_io(ui, si, c, z))
+    fmd.denoise_unit(ios, dev_bf16(ui.w_o))
+    torch.cuda.synchronize()
+    return ui, caches, zs
+
+
+def _oracle_unit(ui, si):
+    s = si.shape
+    return oracle.denoise_unit(si.ring_k, si.ring_v, s.len_before, s.head_before, si.slice_k,
+                               si.slice_v, si.q, si.k_u, si.v_u, si.eps, list(s.h), ui.w_o)
+
+
+@pytest.mark.parametrize("name", ["tiny", "v01_unit"])
+def test_unit_matches_oracle(name):
+    wl = workload.get(name)
+    ui, caches, zs = _run_unit(wl)
+    for si, c, z in zip(ui.sessions, caches, zs):
+        ref = _oracle_unit(ui, si)
+        zg = host_f64(z)
+        assert_close(zg, ref["z"], f"{name} z")
+        assert_close(zg - si.eps, ref["z"] - si.eps, f"{name} dz", max_abs=2e-2, rel=1e-2)
+        gk, gv = cache_logical(fmd, c)
+        assert np.array_equal(gk, ref["ring_k"]) and np.array_equal(gv, ref["ring_v"])
+        assert (c.len_tokens, c.head_tokens) == (ref["length"], ref["head"])
+
+
+def test_small_batch_sessions_independent():
+    # Three ragged sessions in one call give bit-identical results to each alone.
+    sess = [workload.custom_session(4, 128, 60, 4, 48, 480, 480, 96, (0.4, 0.3, 0.2, 0.1)),
+            workload.custom_session(4, 128, 30, 2, 48, 192, 150, 150, (0.4, 0.3, 0.2, 0.1)),
+            workload.custom_session(4, 128, 120, 8, 48, 960, 912, 912, (0.4, 0.3, 0.2, 0.1))]
+    wl = workload.custom_workload("batch3", 21, sess)
+    ui, caches, zs = _run_unit(wl)
+    for i, si in enumerate(ui.sessions):
+        ref = _oracle_unit(ui, si)
+        assert_close(host_f64(zs[i]) - si.eps, ref["z"] - si.eps, f"batch session {i} dz")
+        ui1 = workload.make_inputs(wl, poison_invalid=True, sessions=[i])
+        c1 = make_cache(fmd, ui1.sessions[0].shape, ui1.sessions[0].ring_k,
+                        ui1.sessions[0].ring_v)
+        z1 = torch.from_numpy(ui1.sessions[0].eps.copy()).to(DEV)
+        fmd.denoise_unit([_unit_io(ui1, ui1.sessions[0], c1, z1)], dev_bf16(ui1.w_o))
+        torch.cuda.synchronize()
+        assert torch.equal(z1, zs[i]), f"session {i} differs when run alone"
+
+
+@pytest.mark.parametrize("hs", [[1.0], [0.5, 0.5], [0.25] * 4, [0.4, 0.3, 0.2, 0.1],
+                                [1.0 / 7] * 7])
+def test_closed_form_rectified_flow(hs):
+    # K == 0, every V row == w (bf16), W_o = I, z starts at eps: the velocity
+    # is exactly w = eps - z0, and Euler must land on z0 for any schedule.
+    rng = np.random.default_rng(0)
+    H, hd, n_q, cap, length = 2, 64, 40, 256, 200
+    d = H * hd
+    w = bits(rng.standard_normal(d).astype(np.float32))
+    wf = oracle.bf16_bits_to_f64(w)
+    zero = np.zeros((H, cap, hd), dtype=np.uint16)
+    ring_v = np.broadcast_to(w.reshape(H, 1, hd), (H, cap, hd)).copy()
+    q = random_bits(rng, (n_q, H, hd))
+    ku = np.zeros((n_q, H, hd), dtype=np.uint16)
+    vu = np.broadcast_to(w.reshape(1, H, hd), (n_q, H, hd)).copy()
+    eps = rng.standard_normal((n_q, d)).astype(np.float32)
+    z0 = eps.astype(np.float64) - wf[None, :]
+    shape = workload.custom_session(H, hd, n_q, 0, 0, cap, length, 17, tuple(hs))
+    cache = make_cache(fmd, shape, zero, ring_v)
+    z = torch.from_numpy(eps.copy()).to(DEV)
+    io = fmd.UnitIO(cache, None, None, dev_bf16(q), dev_bf16(ku), dev_bf16(vu), z, hs)
+    fmd.denoise_unit([io], dev_bf16(bits(np.eye(d, dtype=np.float32))))
+    torch.cuda.synchronize()
+    err = np.max(np.abs(host_f64(z) - z0))
+    print(f"closed form S={len(hs)}: max |z - z0| = {err:.3e}", flush=True)
+    assert err <= 1e-5
+
+
+def test_reused_inputs_equal_one_big_step():
+    # step stride 0: four steps of [0.4, 0.3, 0.2, 0.1] == one step of 1.0
+    s4 = workload.custom_session(4, 128, 90, 6, 0, 512, 400, 300, (0.4, 0.3, 0.2, 0.1))
+    s1 = workload.custom_session(4, 128, 90, 6, 0, 512, 400, 300, (1.0,))
+    ui4, _, z4 = _run_unit(workload.custom_workload("lin", 5, [s4]), reuse=True)
+    ui1, _, z1 = _run_unit(workload.custom_workload("lin", 5, [s1]), reuse=True)
+    a, b = host_f64(z4[0]), host_f64(z1[0])
+    assert np.max(np.abs(a - b)) <= 1e-5
+
+
+def test_projection_isolated_from_attention_rounding():
+    # Take the GPU's own O, run one step with z = 0 and h = 1: z must equal
+    # -(O W^T) computed in float64 from that same O.
+    rng = np.random.default_rng(6)
+    H, hd, n_q, cap = 8, 128, 200, 512
+    d = H * hd
+    rk, rv = random_bits(rng, (H, cap, hd)), random_bits(rng, (H, cap, hd))
+    q, ku, vu = (random_bits(rng, (n_q, H, hd)) for _ in range(3))
+    w = random_bits(rng, (d, d), scale=d ** -0.5)
+    shape = workload.custom_session(H, hd, n_q, 0, 0, cap, 333, 100, (1.0,))
+    cache = make_cache(fmd, shape, rk, rv)
+    unit = fmd.UnitStep(cache, dev_bf16(q), dev_bf16(ku), dev_bf16(vu),
+                        z=torch.zeros((n_q, d), dtype=torch.float32, device=DEV), h=1.0)
+    o = fmd.attention([unit])
+    fmd.denoise_step([unit], dev_bf16(w))
+    torch.cuda.synchronize()
+    v_ref = host_f64(o).reshape(n_q, d) @ oracle.bf16_bits_to_f64(w).T
+    got = -host_f64(unit.z)
+    assert rel_l2(got, v_ref) <= 1e-5, rel_l2(got, v_ref)
+
+
+def test_unit_deterministic():
+    wl = workload.get("v01_unit")
+    _, _, za = _run_unit(wl)
+    _, _, zb = _run_unit(wl)
+    assert torch.equal(za[0], zb[0])
+
+
+def test_v02_unit_full_size_sampled_rows():
+    # The 640x368-class unit at full size (append + 4 steps), in the launch
+    # configuration the benchmark times; the oracle computes sampled rows of
+    # every head (video rows across all query blocks, the ragged tail, audio).
+    wl = workload.get("v02_unit")
+    ui = workload.make_inputs(wl, poison_invalid=True)
+    si = ui.sessions[0]
+    s = si.shape
+    cache = make_cache(fmd, s, si.ring_k, si.ring_v)
+    z = torch.from_numpy(si.eps.copy()).to(DEV)
+    io = _unit_io(ui, si, cache, z)
+    fmd.denoise_unit([io], dev_bf16(ui.w_o))
+    torch.cuda.synchronize()
+    rows = [0, 31, 255, 256, 511, 700, 767, 768, 900, 919, 920, 927]
+    rk, rv, ln, hd_ = oracle.kv_append(si.ring_k, si.ring_v, s.len_before, s.head_before,
+                                       si.slice_k, si.slice_v)[:4]
+    dz_ref = np.zeros((len(rows), s.d))
+    W = oracle.bf16_bits_to_f64(ui.w_o)
+    for st in range(s.n_steps):
+        O = oracle.attention(si.q[st], rk, rv, ln, hd_, si.k_u[st], si.v_u[st], rows=rows)
+        dz_ref -= s.h[st] * (O.reshape(len(rows), -1) @ W.T)
+        print(f"oracle step {st} done", flush=True)
+    dz = host_f64(z)[rows] - si.eps[rows]
+    assert_close(dz, dz_ref, "v02_unit sampled dz")
+    # O of the last step for the same rows, through the attention entry.
+    unit = fmd.UnitStep(cache, dev_bf16(si.q[-1]), dev_bf16(si.k_u[-1]), dev_bf16(si.v_u[-1]),
+                        n_audio=s.n_audio)
+    o = host_f64(fmd.attention([unit]))[rows]
+    assert_close(o, O, "v02_unit sampled O (last step)")
