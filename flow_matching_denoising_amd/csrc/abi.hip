@@ -144,7 +144,7 @@ struct SessPlan {
   int seg_lo[2], seg_hi[2];
   int nwin[3], nwin_total;
   int n_qblk, nsplit;
-  size_t off_vt, off_o, off_opart, off_lse;   // workspace offsets
+  size_t off_kt, off_vt, off_o, off_opart, off_lse;   // workspace offsets
 };
 
 int nwin_of(int lo, int hi) {
@@ -210,6 +210,8 @@ void choose_splits(std::vector<SessPlan>& plans, int H) {
 size_t layout_workspace(std::vector<SessPlan>& plans, int H, int hd, bool o_external) {
   size_t off = 0;
   for (auto& p : plans) {
+    p.off_kt = off;
+    off = align256(off + (size_t)H * p.npad * hd * 2);
     p.off_vt = off;
     off = align256(off + (size_t)H * p.npad * hd * 2);
     p.off_o = off;
@@ -281,16 +283,18 @@ int enqueue_steps(const fmd_unit_step* units, int n, const std::vector<SessPlan>
       const fmd_unit_step& u = units[c0 + k];
       const SessPlan& p = plans[c0 + k];
       const fmd_kv_cache* c = u.cache;
+      bf16* kt = reinterpret_cast<bf16*>(ws + p.off_kt);
       bf16* vt = reinterpret_cast<bf16*>(ws + p.off_vt);
       bf16* o = o_out ? o_out + o_row * d : reinterpret_cast<bf16*>(ws + p.off_o);
       o_row += p.n_q;
 
-      va.s[k] = VtSess{static_cast<const bf16*>(u.v_u), vt, p.n_q, p.npad / 16, va.items, 0};
+      va.s[k] = VtSess{static_cast<const bf16*>(u.k_u), static_cast<const bf16*>(u.v_u), kt, vt,
+                       p.n_q, p.npad / 16, va.items, 0};
       va.items += H * (p.npad / 16);
 
       AttnSess& as = aa.s[k];
       as.q = static_cast<const bf16*>(u.q);
-      as.k_u = static_cast<const bf16*>(u.k_u);
+      as.kt_u = kt;
       as.vt_u = vt;
       as.ring_k = static_cast<const bf16*>(c->k);
       as.ring_v = static_cast<const bf16*>(c->v);

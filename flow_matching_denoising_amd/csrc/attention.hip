@@ -40,11 +40,9 @@ constexpr float kNegInf = -__builtin_inff();
 __device__ __forceinline__ int perm_k(int r) {
   return (r & 0x13) | ((r & 4) << 1) | ((r & 8) >> 1);
 }
-// Row permutation of the V^T operand: row rho = [b0 b1 | g | a0 a1] loads
-// feature [b0 b1 | a0 a1 | g]; sigma_inv maps a feature back to its row.
-__device__ __forceinline__ int sigma_inv(int x) {
-  return (x & 3) | (((x >> 4) & 1) << 2) | (((x >> 2) & 3) << 3);
-}
+// Row permutation of the V^T operand: A-operand row rho = [b0 b1 | g | a0 a1]
+// (bits) loads feature sigma(rho) = [b0 b1 | a0 a1 | g], so that output
+// register r of lane group g holds feature 16g + r of the 32-row block.
 
 __device__ __forceinline__ float max_xor32(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
@@ -61,200 +59,191 @@ template <int HD>
 struct Tiles {
   static constexpr int KC = HD / 16;           // 16-wide k chunks of the QK product
   static constexpr int HB = HD / 32;           // 32-row feature blocks of the PV product
-  static constexpr int PARTS = HD / 8;         // 16-byte parts of one key row
   static constexpr int K_BYTES = kAttnWindow * HD * 2;
   static constexpr int V_BYTES = kAttnWindow * HD * 2;
-  static constexpr int BUF_BYTES = K_BYTES + V_BYTES;
-  static constexpr int K_CHUNKS = K_BYTES / 16 / kAttnThreads;   // per thread
-  static constexpr int V_CHUNKS = V_BYTES / 16 / kAttnThreads;
+  static constexpr int K_BLOCKS = K_BYTES / 1024;        // 1 KiB operand blocks
+  static constexpr int V_BLOCKS = V_BYTES / 1024;
+  static constexpr int K_PER_WAVE = K_BLOCKS / kAttnWaves;
+  static constexpr int V_PER_WAVE = V_BLOCKS / kAttnWaves;
+  static constexpr int STAGES = 3;                       // K and V triple-buffered
+  static constexpr int LDS_BYTES = STAGES * (K_BYTES + V_BYTES);
 };
 
 struct Window {
-  const bf16* kbase;   // address of key 0 of the window's key space, this head
-  int64_t kstride;     // elements between consecutive keys
-  const bf16* vbase;   // address of 16-key block 0 of the window's key space
-  int start;           // first key index of the window (multiple of 16)
-  int lo, hi;          // valid keys [lo, hi)
-  bool full;           // every key of the window is valid
+  const bf16* k;      // K of the window's first key
+  const bf16* v;      // V block of the window's first key
+  int start;          // first key of the window (multiple of 16)
+  int lo, hi;         // valid keys [lo, hi) of its segment
+  bool full;          // every key of the window is valid
 };
 
-__device__ __forceinline__ Window make_window(const AttnSess& s, int H, int h, int HD, int w) {
-  Window win;
-  int seg;
-  if (w < s.nwin[0]) {
-    seg = 0;
-  } else if (w < s.nwin[0] + s.nwin[1]) {
-    seg = 1;
-    w -= s.nwin[0];
+// Window w of a session's key sequence: the valid ring range before the wrap
+// point, the one after it, then the unit's own keys.  In both key layouts key
+// k of a segment sits at element k*HD of the segment's base (K: [keys][HD];
+// V: [keys/16][HD][16]).  Every value involved is wave-uniform (scalar).
+__device__ __forceinline__ Window window_at(const AttnSess& s, const bf16* ring_k,
+                                            const bf16* ring_v, const bf16* unit_k,
+                                            const bf16* unit_v, int w, int HD) {
+  Window r;
+  if (w < s.nwin[0] + s.nwin[1]) {
+    const bool second = w >= s.nwin[0];
+    r.lo = second ? s.seg_lo[1] : s.seg_lo[0];
+    r.hi = second ? s.seg_hi[1] : s.seg_hi[0];
+    r.start = (r.lo & ~15) + (second ? w - s.nwin[0] : w) * kAttnWindow;
+    r.k = ring_k + (int64_t)r.start * HD;
+    r.v = ring_v + (int64_t)r.start * HD;
   } else {
-    seg = 2;
-    w -= s.nwin[0] + s.nwin[1];
+    r.lo = 0;
+    r.hi = s.n_q;
+    r.start = (w - s.nwin[0] - s.nwin[1]) * kAttnWindow;
+    r.k = unit_k + (int64_t)r.start * HD;
+    r.v = unit_v + (int64_t)r.start * HD;
   }
-  if (seg < 2) {
-    const int lo = s.seg_lo[seg];
-    win.kbase = s.ring_k + (int64_t)h * s.cap * HD;
-    win.kstride = HD;
-    win.vbase = s.ring_v + (int64_t)h * (s.cap / 16) * HD * 16;
-    win.start = (lo & ~15) + w * kAttnWindow;
-    win.lo = lo;
-    win.hi = s.seg_hi[seg];
+  r.full = r.start >= r.lo && r.start + kAttnWindow <= r.hi;
+  return r;
+}
+
+// Direct-to-LDS loads of one window.  LDS holds each MFMA operand block
+// contiguously in lane order, which is where the hardware puts lane i's 16
+// bytes (base + 16*i).  K: wave w fills blocks b = w, w+8, ...; block
+// b = kb*KC + kc, lane (g, rho) -> key 32kb + perm_k(rho), features 16kc+8g.
+// V^T: block b = c*HB + hb, lane (g, e) -> feature 32hb + sigma(e), keys
+// 16c + 8g .. +7.  koff/voff are those lane offsets (elements, loop-invariant).
+// In a partial window every lane still loads (so each wave issues the same
+// number of loads), from an address clamped into the valid range; scores of
+// invalid keys are masked and their values zeroed in LDS before use.
+template <int HD>
+__device__ __forceinline__ void load_window(const Window& w, char* kdst, char* vdst, bool do_k,
+                                            bool do_v, const int (&koff)[Tiles<HD>::K_PER_WAVE],
+                                            const int (&voff)[Tiles<HD>::V_PER_WAVE]) {
+  using T = Tiles<HD>;
+  const int wave = threadIdx.x >> 6;
+  if (w.full) {
+    if (do_k)
+#pragma unroll
+      for (int i = 0; i < T::K_PER_WAVE; ++i)
+        __builtin_amdgcn_global_load_lds(w.k + koff[i], kdst + (wave + kAttnWaves * i) * 1024,
+                                         16, 0, 0);
+    if (do_v)
+#pragma unroll
+      for (int i = 0; i < T::V_PER_WAVE; ++i)
+        __builtin_amdgcn_global_load_lds(w.v + voff[i], vdst + (wave + kAttnWaves * i) * 1024,
+                                         16, 0, 0);
   } else {
-    win.kbase = s.k_u + (int64_t)h * HD;
-    win.kstride = (int64_t)H * HD;
-    win.vbase = s.vt_u + (int64_t)h * (s.npad / 16) * HD * 16;
-    win.start = w * kAttnWindow;
-    win.lo = 0;
-    win.hi = s.n_q;
-  }
-  win.full = win.start >= win.lo && win.start + kAttnWindow <= win.hi;
-  return win;
-}
-
-// Global -> registers for one window.
-template <int HD>
-__device__ __forceinline__ void stage_load(const Window& win, u32x4 (&kr)[Tiles<HD>::K_CHUNKS],
-                                           u32x4 (&vr)[Tiles<HD>::V_CHUNKS]) {
-  using T = Tiles<HD>;
-  const int tid = threadIdx.x;
+    if (do_k)
 #pragma unroll
-  for (int i = 0; i < T::K_CHUNKS; ++i) {
-    const int c = tid + kAttnThreads * i;
-    const int rho = (c & 7) | (((c >> 6) & 3) << 3);
-    const int part = ((c >> 3) & 7) | (HD == 128 ? ((c >> 8) & 1) << 3 : 0);
-    const int kb = HD == 128 ? (c >> 9) : (c >> 8);
-    const int key = win.start + kb * 32 + perm_k(rho);
-    if (win.full || (key >= win.lo && key < win.hi))
-      kr[i] = ld16(win.kbase + (int64_t)key * win.kstride + part * 8);
-    else
-      kr[i] = u32x4{0u, 0u, 0u, 0u};
-  }
+      for (int i = 0; i < T::K_PER_WAVE; ++i) {
+        const int rel = koff[i] / HD;              // key within the window
+        const int col = koff[i] - rel * HD;
+        const int key = min(max(w.start + rel, w.lo), w.hi - 1);
+        __builtin_amdgcn_global_load_lds(w.k + (key - w.start) * HD + col,
+                                         kdst + (wave + kAttnWaves * i) * 1024, 16, 0, 0);
+      }
+    if (do_v)
 #pragma unroll
-  for (int i = 0; i < T::V_CHUNKS; ++i) {
-    const int c = tid + kAttnThreads * i;
-    const int hd_lo = c & 31;
-    const int g = (c >> 5) & 1;
-    const int hd_hi = HD == 128 ? ((c >> 6) & 3) : ((c >> 6) & 1);
-    const int blk = HD == 128 ? (c >> 8) : (c >> 7);
-    const int hd = hd_hi * 32 + hd_lo;
-    const int key0 = win.start + blk * 16 + g * 8;
-    const bf16* src = win.vbase + ((int64_t)(win.start / 16 + blk) * HD + hd) * 16 + g * 8;
-    if (win.full || (key0 >= win.lo && key0 + 8 <= win.hi)) {
-      vr[i] = ld16(src);
-    } else if (key0 + 8 <= win.lo || key0 >= win.hi) {
-      vr[i] = u32x4{0u, 0u, 0u, 0u};
-    } else {
-      union { u32x4 v; unsigned short u[8]; } x;
-      x.v = ld16(src);
-#pragma unroll
-      for (int j = 0; j < 8; ++j)
-        if (key0 + j < win.lo || key0 + j >= win.hi) x.u[j] = 0;
-      vr[i] = x.v;
-    }
-  }
-}
-
-// Registers -> LDS, in the MFMA operand order (each 1 KiB block is read by one
-// ds_read_b128 of a whole wave, lane (g, row) at (g*32 + row)*16).
-template <int HD>
-__device__ __forceinline__ void stage_store(char* lds, const u32x4 (&kr)[Tiles<HD>::K_CHUNKS],
-                                            const u32x4 (&vr)[Tiles<HD>::V_CHUNKS]) {
-  using T = Tiles<HD>;
-  const int tid = threadIdx.x;
-#pragma unroll
-  for (int i = 0; i < T::K_CHUNKS; ++i) {
-    const int c = tid + kAttnThreads * i;
-    const int rho = (c & 7) | (((c >> 6) & 3) << 3);
-    const int part = ((c >> 3) & 7) | (HD == 128 ? ((c >> 8) & 1) << 3 : 0);
-    const int kb = HD == 128 ? (c >> 9) : (c >> 8);
-    const int kc = part >> 1, g = part & 1;
-    st16(lds + (((kb * T::KC + kc) * 64 + g * 32 + rho) << 4), kr[i]);
-  }
-  char* vl = lds + T::K_BYTES;
-#pragma unroll
-  for (int i = 0; i < T::V_CHUNKS; ++i) {
-    const int c = tid + kAttnThreads * i;
-    const int hd_lo = c & 31;
-    const int g = (c >> 5) & 1;
-    const int hb = HD == 128 ? ((c >> 6) & 3) : ((c >> 6) & 1);
-    const int blk = HD == 128 ? (c >> 8) : (c >> 7);
-    st16(vl + (((blk * T::HB + hb) * 64 + g * 32 + sigma_inv(hd_lo)) << 4), vr[i]);
-  }
-}
-
-// One 64-key window for one wave (32 query rows).
-template <int HD>
-__device__ __forceinline__ void window_compute(const char* lds, const Window& win,
-                                               const bf16x8 (&qr)[Tiles<HD>::KC],
-                                               f32x16 (&o)[Tiles<HD>::HB], float& m_run,
-                                               float& l_run, float scale_log2) {
-  using T = Tiles<HD>;
-  const int lane = threadIdx.x & 63;
-  const int g = lane >> 5;
-  const bf16x8* kl = reinterpret_cast<const bf16x8*>(lds);
-  const bf16x8* vl = reinterpret_cast<const bf16x8*>(lds + T::K_BYTES);
-
-  f32x16 s[2] = {f32x16{}, f32x16{}};
-#pragma unroll
-  for (int kc = 0; kc < T::KC; ++kc) {
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-      s[kb] = mfma32x32x16(kl[(kb * T::KC + kc) * 64 + lane], qr[kc], s[kb]);
-  }
-
-  if (!win.full) {
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = win.start + kb * 32 + (r >> 3) * 16 + g * 8 + (r & 7);
-        if (key < win.lo || key >= win.hi) s[kb][r] = kNegInf;
+      for (int i = 0; i < T::V_PER_WAVE; ++i) {
+        // voff = c*16*HD + feat*16 + 8g: chunk of 8 keys starting at 16c + 8g.
+        const int c = voff[i] / (16 * HD);
+        const int rem = voff[i] - c * 16 * HD;
+        const int feat = rem >> 4, g8 = rem & 15;
+        int key0 = w.start + c * 16 + g8;
+        key0 = min(max(key0, w.lo & ~7), (w.hi - 1) & ~7);    // an in-range 8-key chunk
+        const int rel = key0 - w.start;
+        __builtin_amdgcn_global_load_lds(w.v + (rel & ~15) * HD + feat * 16 + (rel & 15),
+                                         vdst + (wave + kAttnWaves * i) * 1024, 16, 0, 0);
       }
   }
+}
 
-  // Row maximum of this window (scaled after the max: the scale is positive).
+// Zero, in a window's V tile in LDS, the values of keys outside [lo, hi)
+// (they came from clamped loads or other ring slots, which may hold anything).
+// P is 0 for those keys, but 0 * NaN would poison O.  Partial windows only.
+template <int HD>
+__device__ __forceinline__ void zero_invalid_v(char* vbuf, const Window& win) {
+  using T = Tiles<HD>;
+  for (int slot = threadIdx.x; slot < T::V_BLOCKS * 64; slot += kAttnThreads) {
+    const int b = slot >> 6, l = slot & 63;
+    const int c = b / T::HB, g = l >> 5;
+    const int key0 = win.start + c * 16 + g * 8;
+    unsigned keep = 0;
+#pragma unroll
+    for (int t = 0; t < 8; ++t)
+      keep |= (key0 + t >= win.lo && key0 + t < win.hi ? 1u : 0u) << t;
+    if (keep == 0xFFu) continue;
+    union { u32x4 u; unsigned short hw[8]; } x;
+    x.u = *reinterpret_cast<const u32x4*>(vbuf + slot * 16);
+#pragma unroll
+    for (int t = 0; t < 8; ++t)
+      if (!(keep & (1u << t))) x.hw[t] = 0;
+    *reinterpret_cast<u32x4*>(vbuf + slot * 16) = x.u;
+  }
+}
+
+// Wait until at most N of this wave's loads are outstanding, then barrier.
+template <int N>
+__device__ __forceinline__ void wait_loads_and_sync() {
+  __builtin_amdgcn_s_waitcnt(0x0F70 | N);   // vmcnt(N); expcnt/lgkmcnt unconstrained
+  __asm__ volatile("" ::: "memory");
+  __syncthreads();
+  __asm__ volatile("" ::: "memory");
+}
+
+__device__ __forceinline__ float max3f(float a, float b, float c) {
+  return fmaxf(fmaxf(a, b), c);
+}
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+  const bf16x2_t v = __builtin_convertvector(f32x2_t{a, b}, bf16x2_t);
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// Scores of keys outside the window's valid range -> -inf (partial windows).
+__device__ __forceinline__ void mask_scores(f32x16 (&s)[2], const Window& win) {
+  const int g = (threadIdx.x & 63) >> 5;
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int key = win.start + kb * 32 + (r >> 3) * 16 + g * 8 + (r & 7);
+      if (key < win.lo || key >= win.hi) s[kb][r] = kNegInf;
+    }
+}
+
+// Row maximum of a window's scores for this lane's query, in exp2 units.
+__device__ __forceinline__ float row_max(const f32x16 (&s)[2], float scale_log2) {
   float m = fmaxf(s[0][0], s[1][0]);
 #pragma unroll
-  for (int r = 1; r < 16; ++r) m = fmaxf(m, fmaxf(s[0][r], s[1][r]));
-  const float mx = max_xor32(m) * scale_log2;
+  for (int r = 1; r < 16; ++r) m = max3f(m, s[0][r], s[1][r]);
+  return max_xor32(m) * scale_log2;
+}
+
+// Lazy rescale: only when some row's maximum grew by more than the threshold.
+template <int HB>
+__device__ __forceinline__ void maybe_rescale(float mx, f32x16 (&o)[HB], float& m_run,
+                                              float& l_run) {
   if (__ballot(mx > m_run + kRescaleThreshold)) {
     const float m_new = fmaxf(m_run, mx);
     const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
     m_run = m_new;
     l_run *= alpha;
 #pragma unroll
-    for (int hb = 0; hb < T::HB; ++hb)
+    for (int hb = 0; hb < HB; ++hb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) o[hb][r] *= alpha;
   }
-
-  // p = exp2(s * scale_log2 - m).  S^T registers 8c'..8c'+7 of kb hold keys
-  // 32kb + 16c' + 8g .. +7, i.e. the B operand of PV chunk c = 2kb + c'.
-  bf16x8 p[4];
-  float lsum = 0.f;
-#pragma unroll
-  for (int c = 0; c < 4; ++c) {
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const float e = __builtin_amdgcn_exp2f(
-          __builtin_fmaf(s[c >> 1][(c & 1) * 8 + j], scale_log2, -m_run));
-      lsum += e;
-      p[c][j] = (bf16)e;
-    }
-  }
-  l_run += lsum;
-
-#pragma unroll
-  for (int c = 0; c < 4; ++c)
-#pragma unroll
-    for (int hb = 0; hb < T::HB; ++hb)
-      o[hb] = mfma32x32x16(vl[(c * T::HB + hb) * 64 + lane], p[c], o[hb]);
 }
 
 template <int HD>
 __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_kernel(AttnArgs a) {
   using T = Tiles<HD>;
-  __shared__ __attribute__((aligned(16))) char lds[2 * T::BUF_BYTES];
+  extern __shared__ __attribute__((aligned(1024))) char lds[];
+  // LDS: K buffers 0..2, then V buffers 0..2.
+  auto kbuf = [&](int i) { return lds + i * T::K_BYTES; };
+  auto vbuf = [&](int i) { return lds + T::STAGES * T::K_BYTES + i * T::V_BYTES; };
 
   const int item = xcd_remap(blockIdx.x, a.items);
   int si = 0;
@@ -263,6 +252,7 @@ void attn_kernel(AttnArgs a) {
     if (i < a.n_sess && item >= a.s[i].item0) si = i;
   const AttnSess& s = a.s[si];
   const int H = a.H;
+  const float scale_log2 = a.scale_log2;
 
   // Item order inside a session: (head, split, query block), query block fastest,
   // so the query blocks sharing one key range are adjacent (same XCD).
@@ -273,13 +263,44 @@ void attn_kernel(AttnArgs a) {
   const int h = local / s.nsplit;
   const int w_begin = (int)((int64_t)split * s.nwin_total / s.nsplit);
   const int w_end = (int)((int64_t)(split + 1) * s.nwin_total / s.nsplit);
+  const int nw = w_end - w_begin;
 
   const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
   const int j = lane & 31, g = lane >> 5;
   const int row0 = qblk * kAttnBlockM + wave * kAttnRowsPerWave;
-  const bool active = row0 < s.n_q;
+  const bool active = __builtin_amdgcn_readfirstlane(row0) < s.n_q;   // wave-uniform
   const int qrow = row0 + j;
+
+  const bf16* ring_k = s.ring_k + (int64_t)h * s.cap * HD;
+  const bf16* ring_v = s.ring_v + (int64_t)h * s.cap * HD;
+  const bf16* unit_k = s.kt_u + (int64_t)h * s.npad * HD;
+  const bf16* unit_v = s.vt_u + (int64_t)h * s.npad * HD;
+  auto window = [&](int w) { return window_at(s, ring_k, ring_v, unit_k, unit_v, w, HD); };
+
+  // Loop-invariant lane offsets of the window loads.
+  int koff[T::K_PER_WAVE], voff[T::V_PER_WAVE];
+#pragma unroll
+  for (int i = 0; i < T::K_PER_WAVE; ++i) {
+    const int b = wave + kAttnWaves * i;
+    koff[i] = (b / T::KC * 32 + perm_k(j)) * HD + (b % T::KC) * 16 + g * 8;
+  }
+  const int sigma = (j & 3) | (((j >> 3) & 3) << 2) | (((j >> 2) & 1) << 4);
+#pragma unroll
+  for (int i = 0; i < T::V_PER_WAVE; ++i) {
+    const int b = wave + kAttnWaves * i;
+    voff[i] = (b / T::HB) * 16 * HD + ((b % T::HB) * 32 + sigma) * 16 + g * 8;
+  }
+
+  // Windows i..i+3 of the pipeline (window i+3 is loaded in iteration i).
+  Window W[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) W[t] = window(w_begin + min(t, nw - 1));
+
+  // Prologue: K(0), V(0), K(1), V(1), K(2).
+  load_window<HD>(W[0], kbuf(0), vbuf(0), true, true, koff, voff);
+  if (nw > 1) load_window<HD>(W[1], kbuf(1), vbuf(1), true, true, koff, voff);
+  if (nw > 2) load_window<HD>(W[2], kbuf(2), vbuf(2), true, false, koff, voff);
 
   // Q^T operand: lane (j, g) holds query row0+j, features 16kc+8g..+7.
   bf16x8 qr[T::KC];
@@ -293,16 +314,129 @@ void attn_kernel(AttnArgs a) {
 #pragma unroll
   for (int hb = 0; hb < T::HB; ++hb) o[hb] = f32x16{};
   float m_run = kNegInf, l_run = 0.f;
+  f32x16 s_cur[2];
 
-  u32x4 kr[T::K_CHUNKS], vr[T::V_CHUNKS];
-  if (w_begin < w_end) stage_load<HD>(make_window(s, H, h, HD, w_begin), kr, vr);
-  for (int w = w_begin; w < w_end; ++w) {
-    char* buf = lds + ((w - w_begin) & 1) * T::BUF_BYTES;
-    stage_store<HD>(buf, kr, vr);
-    __syncthreads();
-    const Window win = make_window(s, H, h, HD, w);
-    if (w + 1 < w_end) stage_load<HD>(make_window(s, H, h, HD, w + 1), kr, vr);
-    if (active) window_compute<HD>(buf, win, qr, o, m_run, l_run, a.scale_log2);
+  wait_loads_and_sync<0>();
+  if (active) {
+    const bf16x8* kl = reinterpret_cast<const bf16x8*>(kbuf(0));
+    s_cur[0] = s_cur[1] = f32x16{};
+#pragma unroll
+    for (int kc = 0; kc < T::KC; ++kc)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+        s_cur[kb] = mfma32x32x16(kl[(kb * T::KC + kc) * 64 + lane], qr[kc], s_cur[kb]);
+    if (!W[0].full) mask_scores(s_cur, W[0]);
+    maybe_rescale<T::HB>(row_max(s_cur, scale_log2), o, m_run, l_run);
+  }
+
+  // Iteration i: softmax and P*V of window i, scores of window i+1; loads of
+  // K(i+3) and V(i+2) in flight.  s_cur holds window i's (masked) scores with
+  // m_run already updated for them.  Blocks (A) and (B) are branch-free so
+  // their MFMAs interleave with VALU work; everything specific to partial
+  // windows happens in rare, uniform branches.
+  int stage = 0;                                  // i % 3
+  for (int i = 0; i < nw; ++i) {
+    // Loads of window i+1's K and window i's V were issued in iteration i-2
+    // (or the prologue); those of iteration i-1 may still be in flight.
+    if (i == 0) {
+      // the prologue waited for everything
+    } else if (i + 2 < nw) {
+      wait_loads_and_sync<T::K_PER_WAVE + T::V_PER_WAVE>();
+    } else if (i + 1 < nw) {
+      wait_loads_and_sync<T::V_PER_WAVE>();
+    } else {
+      wait_loads_and_sync<0>();
+    }
+    const int st1 = stage == 2 ? 0 : stage + 1;   // (i+1) % 3
+    const int st2 = st1 == 2 ? 0 : st1 + 1;       // (i+2) % 3
+    if (!W[0].full) {
+      zero_invalid_v<HD>(vbuf(stage), W[0]);
+      __syncthreads();
+    }
+    // K(i+3) -> the buffer of K(i) (consumed by QK(i) in iteration i-1);
+    // V(i+2) -> the buffer of V(i-1) (consumed by P*V(i-1)).
+    load_window<HD>(W[3], kbuf(stage), vbuf(st2), i + 3 < nw, false, koff, voff);
+    load_window<HD>(W[2], kbuf(stage), vbuf(st2), false, i + 2 < nw, koff, voff);
+    if (active) {
+      // (A) For each half kb of the window (32 keys): the shifted scores
+      //     (FMA) are read out of s[kb], then the scores of window i+1 are
+      //     accumulated into the same registers while the exponentials, the
+      //     bf16 packing and the row sums of window i proceed.  On the last
+      //     window the new scores read a stale in-bounds K buffer and are
+      //     discarded.
+      const bf16x8* kl = reinterpret_cast<const bf16x8*>(kbuf(st1));
+      uint32_t pw[4][4];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        // All K operands of this half are read up front so their LDS latency
+        // overlaps (one wait instead of one per MFMA).
+        bf16x8 ka[T::KC];
+#pragma unroll
+        for (int kc = 0; kc < T::KC; ++kc) ka[kc] = kl[(kb * T::KC + kc) * 64 + lane];
+        float x[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) x[r] = __builtin_fmaf(s_cur[kb][r], scale_log2, -m_run);
+        __builtin_amdgcn_sched_barrier(0);   // keep the reads issued ahead of the MFMAs
+        s_cur[kb] = f32x16{};
+#pragma unroll
+        for (int kc = 0; kc < T::KC; ++kc) s_cur[kb] = mfma32x32x16(ka[kc], qr[kc], s_cur[kb]);
+#pragma unroll
+        for (int c2 = 0; c2 < 2; ++c2) {
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            const float e0 = __builtin_amdgcn_exp2f(x[c2 * 8 + 2 * t]);
+            const float e1 = __builtin_amdgcn_exp2f(x[c2 * 8 + 2 * t + 1]);
+            const uint32_t w2 = pack_bf16(e0, e1);
+            pw[kb * 2 + c2][t] = w2;
+            l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w2),
+                                                    __builtin_bit_cast(bf16x2_t, 0x3F803F80u),
+                                                    l_run, false);
+          }
+        }
+        // Each MFMA followed by VALU work (exp/pack/row sum).
+#pragma unroll
+        for (int t = 0; t < T::KC; ++t) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+        }
+      }
+      // (B) P*V of window i, and the row maximum of window i+1.  The V
+      //     operands of chunk c+1 are read while chunk c's MFMAs run.
+      const bf16x8* vl = reinterpret_cast<const bf16x8*>(vbuf(stage));
+      bf16x8 va[2][T::HB];
+#pragma unroll
+      for (int hb = 0; hb < T::HB; ++hb) va[0][hb] = vl[hb * 64 + lane];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        if (c + 1 < 4)
+#pragma unroll
+          for (int hb = 0; hb < T::HB; ++hb)
+            va[(c + 1) & 1][hb] = vl[((c + 1) * T::HB + hb) * 64 + lane];
+        __builtin_amdgcn_sched_barrier(0);   // chunk c+1's reads go out before chunk c's MFMAs
+        const u32x4 pv4 = {pw[c][0], pw[c][1], pw[c][2], pw[c][3]};
+        const bf16x8 pc = __builtin_bit_cast(bf16x8, pv4);
+#pragma unroll
+        for (int hb = 0; hb < T::HB; ++hb) o[hb] = mfma32x32x16(va[c & 1][hb], pc, o[hb]);
+      }
+      float mx = row_max(s_cur, scale_log2);
+      // Keep the row-sum updates inside this block (they would otherwise be
+      // sunk past it).
+      __asm__ volatile("" ::"v"(l_run));
+      // (C) window i+1: mask a partial window, then the lazy rescale (which
+      //     applies to O accumulated through window i).
+      if (i + 1 < nw) {
+        if (!W[1].full) {
+          mask_scores(s_cur, W[1]);
+          mx = row_max(s_cur, scale_log2);
+        }
+        maybe_rescale<T::HB>(mx, o, m_run, l_run);
+      }
+    }
+    W[0] = W[1];
+    W[1] = W[2];
+    W[2] = W[3];
+    if (i + 4 < nw) W[3] = window(w_begin + i + 4);
+    stage = st1;
   }
 
   if (!active) return;
@@ -377,10 +511,24 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
 
 hipError_t launch_attn(const AttnArgs& a, int head_dim, hipStream_t st) {
   if (a.items <= 0) return hipSuccess;
+  // The pipeline uses more than the default 64 KiB of LDS (gfx950 has 160 KiB
+  // per CU); raise the kernels' dynamic-LDS limit once.
+  static const hipError_t attr_err = [] {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_kernel<128>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       Tiles<128>::LDS_BYTES);
+    if (e == hipSuccess)
+      e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_kernel<64>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, Tiles<64>::LDS_BYTES);
+    return e;
+  }();
+  if (attr_err != hipSuccess) return attr_err;
   if (head_dim == 128)
-    hipLaunchKernelGGL(attn_kernel<128>, dim3(a.items), dim3(kAttnThreads), 0, st, a);
+    hipLaunchKernelGGL(attn_kernel<128>, dim3(a.items), dim3(kAttnThreads), Tiles<128>::LDS_BYTES,
+                       st, a);
   else
-    hipLaunchKernelGGL(attn_kernel<64>, dim3(a.items), dim3(kAttnThreads), 0, st, a);
+    hipLaunchKernelGGL(attn_kernel<64>, dim3(a.items), dim3(kAttnThreads), Tiles<64>::LDS_BYTES,
+                       st, a);
   return hipGetLastError();
 }
 

@@ -70,8 +70,10 @@ struct AppendArgs {
 };
 
 struct VtSess {
-  const bf16* v;    // [n][H][hd]
-  bf16* vt;         // [H][npad/16][hd][16]
+  const bf16* k;    // [n][H][hd]   the unit's keys
+  const bf16* v;    // [n][H][hd]   the unit's values
+  bf16* kt;         // [H][npad][hd]           keys, head-major, zero past n
+  bf16* vt;         // [H][npad/16][hd][16]   values, 16-key blocks, zero past n
   int32_t n;
   int32_t nblk;     // npad/16
   int32_t item0;
@@ -86,8 +88,8 @@ struct VtArgs {
 
 struct AttnSess {
   const bf16* q;      // [n_q][H][hd]
-  const bf16* k_u;    // [n_q][H][hd]
-  const bf16* vt_u;   // [H][npad/16][hd][16]   (workspace)
+  const bf16* kt_u;   // [H][npad][hd]           (workspace copy of the unit's keys)
+  const bf16* vt_u;   // [H][npad/16][hd][16]   (workspace copy of the unit's values)
   const bf16* ring_k; // [H][cap][hd]
   const bf16* ring_v; // [H][cap/16][hd][16]
   bf16* o;            // [n_q][H][hd]            (when nsplit == 1)

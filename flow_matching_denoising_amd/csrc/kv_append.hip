@@ -1,5 +1,5 @@
-// Ring append of the thinker's K/V slice, and the 16-token transpose of the
-// unit's own values.
+// Ring append of the thinker's K/V slice, and the staging of the unit's own
+// keys and values in the ring's layouts.
 //
 // The performer writes each incoming K/V slice into its preallocated local
 // cache at the slice's position, before the solver runs [Wan-Streamer v0.2:
@@ -36,7 +36,8 @@ __global__ __launch_bounds__(2 * HD) void append_kernel(AppendArgs a) {
   const int h = local / s.nblk;
   const int bi = local % s.nblk;
   const int64_t nb_ring = s.cap / 16;
-  const int64_t pb = (s.blk0 + bi) % nb_ring;       // physical block
+  int64_t pb = s.blk0 + bi;                          // physical block
+  if (pb >= nb_ring) pb -= nb_ring;
   const int H = a.H;
 
   // Load phase: thread -> (slot r of the block, 16-byte part).
@@ -44,7 +45,8 @@ __global__ __launch_bounds__(2 * HD) void append_kernel(AppendArgs a) {
     const int r = threadIdx.x / PARTS;
     const int part = threadIdx.x % PARTS;
     const int64_t p = pb * 16 + r;
-    const int64_t tt = ((p - s.head0) % s.cap + s.cap) % s.cap;   // token index
+    int64_t tt = p - s.head0;                    // token index: (p - head0) mod cap
+    if (tt < 0) tt += s.cap;
     if (tt < s.T) {
       const int64_t src = (tt * H + h) * HD + part * 8;
       st16(s.ck + ((int64_t)h * s.cap + p) * HD + part * 8, ld16(s.ks + src));
@@ -62,7 +64,8 @@ __global__ __launch_bounds__(2 * HD) void append_kernel(AppendArgs a) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int64_t p = pb * 16 + hh * 8 + i;
-      const int64_t tt = ((p - s.head0) % s.cap + s.cap) % s.cap;
+      int64_t tt = p - s.head0;
+      if (tt < 0) tt += s.cap;
       written |= (tt < s.T ? 1u : 0u) << i;
     }
     if (written == 0) return;
@@ -75,7 +78,11 @@ __global__ __launch_bounds__(2 * HD) void append_kernel(AppendArgs a) {
   }
 }
 
-// Unit values [n][H][hd] -> [H][npad/16][hd][16], zero beyond n.
+// The unit's own keys and values, staged in the ring's layouts so that the
+// attention kernel streams every key segment the same way:
+//   keys   [n][H][hd] -> [H][npad][hd]
+//   values [n][H][hd] -> [H][npad/16][hd][16]
+// (npad = n rounded up to 16; rows past n are zero).
 template <int HD>
 __global__ __launch_bounds__(2 * HD) void vt_kernel(VtArgs a) {
   constexpr int PARTS = HD / 8;
@@ -95,8 +102,12 @@ __global__ __launch_bounds__(2 * HD) void vt_kernel(VtArgs a) {
     const int r = threadIdx.x / PARTS;
     const int part = threadIdx.x % PARTS;
     const int tok = b * 16 + r;
-    u32x4 v = {0u, 0u, 0u, 0u};
-    if (tok < s.n) v = ld16(s.v + ((int64_t)tok * H + h) * HD + part * 8);
+    u32x4 v = {0u, 0u, 0u, 0u}, k = {0u, 0u, 0u, 0u};
+    if (tok < s.n) {
+      v = ld16(s.v + ((int64_t)tok * H + h) * HD + part * 8);
+      k = ld16(s.k + ((int64_t)tok * H + h) * HD + part * 8);
+    }
+    st16(s.kt + ((int64_t)h * s.nblk * 16 + tok) * HD + part * 8, k);
     st16(&tile[r][part * 8], v);
   }
   __syncthreads();

@@ -104,8 +104,8 @@ def test_workspace_bytes_is_host_arithmetic():
     c = _cache(H=40, hd=128, cap=60416, ln=60416, head=0)
     rc, n1 = _ws([_step(c, 920, 8)])
     assert rc == 0 and n1 > 0
-    # V transpose (40 x 928 x 128 bf16) + O (928 x 5120 bf16) are always there.
-    assert n1 >= 40 * 928 * 128 * 2 + 928 * 5120 * 2
+    # Staged unit K and V (2 x 40 x 928 x 128 bf16) + O (928 x 5120 bf16).
+    assert n1 >= 2 * 40 * 928 * 128 * 2 + 928 * 5120 * 2
     rc, n2 = _ws([_step(c, 920, 8), _step(_cache(H=40, hd=128, cap=944, ln=944, head=0), 920, 8)])
     assert rc == 0 and n2 > n1
 
