@@ -322,7 +322,7 @@ int enqueue_steps(const fmd_unit_step* units, int n, const std::vector<SessPlan>
       }
 
       const int mtiles = (p.n_q + kProjTile - 1) / kProjTile;
-      const int ntiles = (d + kProjTile - 1) / kProjTile;
+      const int ntiles = (d + kProjTileN - 1) / kProjTileN;
       pa.s[k] = ProjSess{o, u.z, p.n_q, mtiles, pa.items, u.h};
       pa.items += mtiles * ntiles;
     }

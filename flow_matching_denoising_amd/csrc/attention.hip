@@ -40,6 +40,12 @@ constexpr float kNegInf = -__builtin_inff();
 __device__ __forceinline__ int perm_k(int r) {
   return (r & 0x13) | ((r & 4) << 1) | ((r & 8) >> 1);
 }
+// XOR swizzle of the 16-byte chunks of key k's row in the K tile (the row has
+// HD/8 chunks; only the low 4 bits of k matter).
+template <int HD>
+__device__ __forceinline__ int kswz(int k) {
+  return HD == 128 ? (k & 15) : ((k >> 1) & 7);
+}
 // Row permutation of the V^T operand: A-operand row rho = [b0 b1 | g | a0 a1]
 // (bits) loads feature sigma(rho) = [b0 b1 | a0 a1 | g], so that output
 // register r of lane group g holds feature 16g + r of the 32-row block.
@@ -103,12 +109,15 @@ __device__ __forceinline__ Window window_at(const AttnSess& s, const bf16* ring_
   return r;
 }
 
-// Direct-to-LDS loads of one window.  LDS holds each MFMA operand block
-// contiguously in lane order, which is where the hardware puts lane i's 16
-// bytes (base + 16*i).  K: wave w fills blocks b = w, w+8, ...; block
-// b = kb*KC + kc, lane (g, rho) -> key 32kb + perm_k(rho), features 16kc+8g.
-// V^T: block b = c*HB + hb, lane (g, e) -> feature 32hb + sigma(e), keys
-// 16c + 8g .. +7.  koff/voff are those lane offsets (elements, loop-invariant).
+// Direct-to-LDS loads of one window; the hardware puts lane i's 16 bytes at
+// base + 16*i of the wave's 1 KiB destination.  K: the window's keys are kept
+// row by row (key k at byte 2*HD*k), each wave instruction reading 1 KiB of
+// whole rows (512/HD keys); the 16-byte chunk c of key k sits at chunk position
+// c ^ kswz(k) of its row, so that the QK operand reads (16 lanes = 16 keys of
+// one chunk per LDS cycle) hit 16 different bank groups.  V^T: block
+// b = c*HB + hb, lane (g, e) -> feature 32hb + sigma(e), keys 16c + 8g .. +7,
+// which is one contiguous 1 KiB of the [keys/16][HD][16] layout per
+// instruction.  koff/voff are the lane offsets (elements, loop-invariant).
 // In a partial window every lane still loads (so each wave issues the same
 // number of loads), from an address clamped into the valid range; scores of
 // invalid keys are masked and their values zeroed in LDS before use.
@@ -282,9 +291,19 @@ void attn_kernel(AttnArgs a) {
   int koff[T::K_PER_WAVE], voff[T::V_PER_WAVE];
 #pragma unroll
   for (int i = 0; i < T::K_PER_WAVE; ++i) {
-    const int b = wave + kAttnWaves * i;
-    koff[i] = (b / T::KC * 32 + perm_k(j)) * HD + (b % T::KC) * 16 + g * 8;
+    constexpr int CPR = HD / 8;                   // 16-byte chunks per key row
+    const int key = (wave + kAttnWaves * i) * (1024 / (2 * HD)) + lane / CPR;
+    koff[i] = key * HD + ((lane % CPR) ^ kswz<HD>(key)) * 8;
   }
+  // QK operand reads: lane (g, rho) wants key 32kb + perm_k(rho), chunk 2kc+g;
+  // byte offsets within the K tile for kb = 0 (kb adds 64*HD).
+  int kroff[T::KC];
+#pragma unroll
+  for (int kc = 0; kc < T::KC; ++kc)
+    kroff[kc] = perm_k(j) * 2 * HD + ((2 * kc + g) ^ kswz<HD>(perm_k(j))) * 16;
+  auto kread = [&](const char* kt, int kb, int kc) {
+    return *reinterpret_cast<const bf16x8*>(kt + kb * 64 * HD + kroff[kc]);
+  };
   const int sigma = (j & 3) | (((j >> 3) & 3) << 2) | (((j >> 2) & 1) << 4);
 #pragma unroll
   for (int i = 0; i < T::V_PER_WAVE; ++i) {
@@ -318,13 +337,12 @@ void attn_kernel(AttnArgs a) {
 
   wait_loads_and_sync<0>();
   if (active) {
-    const bf16x8* kl = reinterpret_cast<const bf16x8*>(kbuf(0));
     s_cur[0] = s_cur[1] = f32x16{};
 #pragma unroll
     for (int kc = 0; kc < T::KC; ++kc)
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
-        s_cur[kb] = mfma32x32x16(kl[(kb * T::KC + kc) * 64 + lane], qr[kc], s_cur[kb]);
+        s_cur[kb] = mfma32x32x16(kread(kbuf(0), kb, kc), qr[kc], s_cur[kb]);
     if (!W[0].full) mask_scores(s_cur, W[0]);
     maybe_rescale<T::HB>(row_max(s_cur, scale_log2), o, m_run, l_run);
   }
@@ -364,7 +382,7 @@ void attn_kernel(AttnArgs a) {
       //     bf16 packing and the row sums of window i proceed.  On the last
       //     window the new scores read a stale in-bounds K buffer and are
       //     discarded.
-      const bf16x8* kl = reinterpret_cast<const bf16x8*>(kbuf(st1));
+      const char* kl = kbuf(st1);
       uint32_t pw[4][4];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
@@ -372,7 +390,7 @@ void attn_kernel(AttnArgs a) {
         // overlaps (one wait instead of one per MFMA).
         bf16x8 ka[T::KC];
 #pragma unroll
-        for (int kc = 0; kc < T::KC; ++kc) ka[kc] = kl[(kb * T::KC + kc) * 64 + lane];
+        for (int kc = 0; kc < T::KC; ++kc) ka[kc] = kread(kl, kb, kc);
         float x[16];
 #pragma unroll
         for (int r = 0; r < 16; ++r) x[r] = __builtin_fmaf(s_cur[kb][r], scale_log2, -m_run);
