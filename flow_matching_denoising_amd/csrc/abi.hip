@@ -11,6 +11,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <algorithm>
 #include <mutex>
 #include <string>
 #include <vector>
@@ -143,6 +144,7 @@ struct SessPlan {
   int n_q, npad;
   int seg_lo[2], seg_hi[2];
   int nwin[3], nwin_total;
+  int split0[4];      // first key split of each segment (a split never crosses one)
   int n_qblk, nsplit;
   size_t off_kt, off_vt, off_o, off_opart, off_lse;   // workspace offsets
 };
@@ -151,6 +153,23 @@ int nwin_of(int lo, int hi) {
   if (hi <= lo) return 0;
   const int start = lo & ~15;
   return (hi - start + kAttnWindow - 1) / kAttnWindow;
+}
+
+// Distribute about `ns` key splits over the non-empty key segments in
+// proportion to their windows; every non-empty segment gets at least one
+// split and at most one per window, so a split covers >= 1 window of exactly
+// one segment.
+void set_splits(SessPlan& p, int ns) {
+  int acc = 0;
+  for (int t = 0; t < 3; ++t) {
+    p.split0[t] = acc;
+    if (p.nwin[t] > 0) {
+      const int share = (int)llround((double)ns * p.nwin[t] / p.nwin_total);
+      acc += std::max(1, std::min(share, p.nwin[t]));
+    }
+  }
+  p.split0[3] = acc;
+  p.nsplit = acc;
 }
 
 void plan_session(const fmd_kv_cache* c, int n_q, SessPlan& p) {
@@ -175,7 +194,7 @@ void plan_session(const fmd_kv_cache* c, int n_q, SessPlan& p) {
   p.nwin[2] = (n_q + kAttnWindow - 1) / kAttnWindow;
   p.nwin_total = p.nwin[0] + p.nwin[1] + p.nwin[2];
   p.n_qblk = (n_q + kAttnBlockM - 1) / kAttnBlockM;
-  p.nsplit = 1;
+  set_splits(p, 1);
 }
 
 int env_int(const char* name, int dflt) {
@@ -201,7 +220,7 @@ void choose_splits(std::vector<SessPlan>& plans, int H) {
       ns = (int)ceil(p.nwin_total / (per_item > 1 ? per_item : 1.0));
       ns = std::min(ns, std::max(1, p.nwin_total / kMinWindows));
     }
-    p.nsplit = std::max(1, std::min(ns, p.nwin_total));
+    set_splits(p, std::max(1, std::min(ns, p.nwin_total)));
   }
 }
 
@@ -309,7 +328,7 @@ int enqueue_steps(const fmd_unit_step* units, int n, const std::vector<SessPlan>
         as.seg_hi[t] = p.seg_hi[t];
       }
       for (int t = 0; t < 3; ++t) as.nwin[t] = p.nwin[t];
-      as.nwin_total = p.nwin_total;
+      for (int t = 0; t < 4; ++t) as.split0[t] = p.split0[t];
       as.n_qblk = p.n_qblk;
       as.nsplit = p.nsplit;
       as.item0 = aa.items;

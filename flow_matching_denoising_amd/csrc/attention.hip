@@ -83,29 +83,28 @@ struct Window {
   bool full;          // every key of the window is valid
 };
 
-// Window w of a session's key sequence: the valid ring range before the wrap
-// point, the one after it, then the unit's own keys.  In both key layouts key
-// k of a segment sits at element k*HD of the segment's base (K: [keys][HD];
-// V: [keys/16][HD][16]).  Every value involved is wave-uniform (scalar).
-__device__ __forceinline__ Window window_at(const AttnSess& s, const bf16* ring_k,
-                                            const bf16* ring_v, const bf16* unit_k,
-                                            const bf16* unit_v, int w, int HD) {
+// The keys one work item covers: windows [0, nw) of one key segment (the
+// valid ring range before the wrap point, the one after it, or the unit's own
+// keys), window j starting at key start0 + 64j of the segment.  In both key
+// layouts key k of a segment sits at element k*HD of the segment's base
+// (K: [keys][HD]; V: [keys/16][HD][16]).  Keys outside [lo, hi) are not part
+// of the segment; only the first and the last window of a segment can hold
+// such keys.  Every value involved is wave-uniform (scalar).
+struct Span {
+  const bf16* k;
+  const bf16* v;
+  int start0, lo, hi, nw;
+};
+
+template <int HD>
+__device__ __forceinline__ Window window_of(const Span& sp, int j) {
   Window r;
-  if (w < s.nwin[0] + s.nwin[1]) {
-    const bool second = w >= s.nwin[0];
-    r.lo = second ? s.seg_lo[1] : s.seg_lo[0];
-    r.hi = second ? s.seg_hi[1] : s.seg_hi[0];
-    r.start = (r.lo & ~15) + (second ? w - s.nwin[0] : w) * kAttnWindow;
-    r.k = ring_k + (int64_t)r.start * HD;
-    r.v = ring_v + (int64_t)r.start * HD;
-  } else {
-    r.lo = 0;
-    r.hi = s.n_q;
-    r.start = (w - s.nwin[0] - s.nwin[1]) * kAttnWindow;
-    r.k = unit_k + (int64_t)r.start * HD;
-    r.v = unit_v + (int64_t)r.start * HD;
-  }
-  r.full = r.start >= r.lo && r.start + kAttnWindow <= r.hi;
+  r.start = sp.start0 + j * kAttnWindow;
+  r.k = sp.k + (int64_t)r.start * HD;
+  r.v = sp.v + (int64_t)r.start * HD;
+  r.lo = sp.lo;
+  r.hi = sp.hi;
+  r.full = r.start >= sp.lo && r.start + kAttnWindow <= sp.hi;
   return r;
 }
 
@@ -124,9 +123,9 @@ __device__ __forceinline__ Window window_at(const AttnSess& s, const bf16* ring_
 template <int HD>
 __device__ __forceinline__ void load_window(const Window& w, char* kdst, char* vdst, bool do_k,
                                             bool do_v, const int (&koff)[Tiles<HD>::K_PER_WAVE],
-                                            const int (&voff)[Tiles<HD>::V_PER_WAVE]) {
+                                            const int (&voff)[Tiles<HD>::V_PER_WAVE],
+                                            int wave) {
   using T = Tiles<HD>;
-  const int wave = threadIdx.x >> 6;
   if (w.full) {
     if (do_k)
 #pragma unroll
@@ -186,6 +185,11 @@ __device__ __forceinline__ void zero_invalid_v(char* vbuf, const Window& win) {
       if (!(keep & (1u << t))) x.hw[t] = 0;
     *reinterpret_cast<u32x4*>(vbuf + slot * 16) = x.u;
   }
+}
+
+// One wave-wide direct-to-LDS load: lane i's 16 bytes at src go to dst + 16*i.
+__device__ __forceinline__ void dma16(const bf16* src, char* dst) {
+  __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 0);
 }
 
 // Wait until at most N of this wave's loads are outstanding, then barrier.
@@ -270,22 +274,36 @@ void attn_kernel(AttnArgs a) {
   local /= s.n_qblk;
   const int split = local % s.nsplit;
   const int h = local / s.nsplit;
-  const int w_begin = (int)((int64_t)split * s.nwin_total / s.nsplit);
-  const int w_end = (int)((int64_t)(split + 1) * s.nwin_total / s.nsplit);
-  const int nw = w_end - w_begin;
 
-  const int wave = threadIdx.x >> 6;
+  // The split's segment and window range.
+  const int sg = split >= s.split0[2] ? 2 : (split >= s.split0[1] ? 1 : 0);
+  const int ns_seg = s.split0[sg + 1] - s.split0[sg];
+  const int ls = split - s.split0[sg];
+  const int nwin_seg = s.nwin[sg];
+  const int w_begin = ls * nwin_seg / ns_seg;
+  const int nw = (ls + 1) * nwin_seg / ns_seg - w_begin;    // >= 1
+  Span sp;
+  if (sg == 2) {
+    sp.k = s.kt_u + (int64_t)h * s.npad * HD;
+    sp.v = s.vt_u + (int64_t)h * s.npad * HD;
+    sp.lo = 0;
+    sp.hi = s.n_q;
+  } else {
+    sp.k = s.ring_k + (int64_t)h * s.cap * HD;
+    sp.v = s.ring_v + (int64_t)h * s.cap * HD;
+    sp.lo = sg == 0 ? s.seg_lo[0] : s.seg_lo[1];
+    sp.hi = sg == 0 ? s.seg_hi[0] : s.seg_hi[1];
+  }
+  sp.start0 = (sp.lo & ~15) + w_begin * kAttnWindow;
+  sp.nw = nw;
+  auto win = [&](int j) { return window_of<HD>(sp, j); };
+
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
-  const int j = lane & 31, g = lane >> 5;
+  const int j32 = lane & 31, g = lane >> 5;
   const int row0 = qblk * kAttnBlockM + wave * kAttnRowsPerWave;
-  const bool active = __builtin_amdgcn_readfirstlane(row0) < s.n_q;   // wave-uniform
-  const int qrow = row0 + j;
-
-  const bf16* ring_k = s.ring_k + (int64_t)h * s.cap * HD;
-  const bf16* ring_v = s.ring_v + (int64_t)h * s.cap * HD;
-  const bf16* unit_k = s.kt_u + (int64_t)h * s.npad * HD;
-  const bf16* unit_v = s.vt_u + (int64_t)h * s.npad * HD;
-  auto window = [&](int w) { return window_at(s, ring_k, ring_v, unit_k, unit_v, w, HD); };
+  const bool active = row0 < s.n_q;                   // wave-uniform
+  const int qrow = row0 + j32;
 
   // Loop-invariant lane offsets of the window loads.
   int koff[T::K_PER_WAVE], voff[T::V_PER_WAVE];
@@ -295,31 +313,27 @@ void attn_kernel(AttnArgs a) {
     const int key = (wave + kAttnWaves * i) * (1024 / (2 * HD)) + lane / CPR;
     koff[i] = key * HD + ((lane % CPR) ^ kswz<HD>(key)) * 8;
   }
-  // QK operand reads: lane (g, rho) wants key 32kb + perm_k(rho), chunk 2kc+g;
-  // byte offsets within the K tile for kb = 0 (kb adds 64*HD).
-  int kroff[T::KC];
-#pragma unroll
-  for (int kc = 0; kc < T::KC; ++kc)
-    kroff[kc] = perm_k(j) * 2 * HD + ((2 * kc + g) ^ kswz<HD>(perm_k(j))) * 16;
-  auto kread = [&](const char* kt, int kb, int kc) {
-    return *reinterpret_cast<const bf16x8*>(kt + kb * 64 * HD + kroff[kc]);
-  };
-  const int sigma = (j & 3) | (((j >> 3) & 3) << 2) | (((j >> 2) & 1) << 4);
+  const int sigma = (j32 & 3) | (((j32 >> 3) & 3) << 2) | (((j32 >> 2) & 1) << 4);
 #pragma unroll
   for (int i = 0; i < T::V_PER_WAVE; ++i) {
     const int b = wave + kAttnWaves * i;
     voff[i] = (b / T::HB) * 16 * HD + ((b % T::HB) * 32 + sigma) * 16 + g * 8;
   }
-
-  // Windows i..i+3 of the pipeline (window i+3 is loaded in iteration i).
-  Window W[4];
+  // QK operand reads: lane (g, rho) wants key 32kb + perm_k(rho), chunk 2kc+g;
+  // byte offsets within the K tile for kb = 0 (kb adds 64*HD).
+  int kroff[T::KC];
 #pragma unroll
-  for (int t = 0; t < 4; ++t) W[t] = window(w_begin + min(t, nw - 1));
+  for (int kc = 0; kc < T::KC; ++kc)
+    kroff[kc] = perm_k(j32) * 2 * HD + ((2 * kc + g) ^ kswz<HD>(perm_k(j32))) * 16;
+  auto kread = [&](const char* kt, int kb, int kc) {
+    return *reinterpret_cast<const bf16x8*>(kt + kb * 64 * HD + kroff[kc]);
+  };
 
   // Prologue: K(0), V(0), K(1), V(1), K(2).
-  load_window<HD>(W[0], kbuf(0), vbuf(0), true, true, koff, voff);
-  if (nw > 1) load_window<HD>(W[1], kbuf(1), vbuf(1), true, true, koff, voff);
-  if (nw > 2) load_window<HD>(W[2], kbuf(2), vbuf(2), true, false, koff, voff);
+  const Window w0 = win(0);
+  load_window<HD>(w0, kbuf(0), vbuf(0), true, true, koff, voff, wave);
+  if (nw > 1) load_window<HD>(win(1), kbuf(1), vbuf(1), true, true, koff, voff, wave);
+  if (nw > 2) load_window<HD>(win(2), kbuf(2), vbuf(2), true, false, koff, voff, wave);
 
   // Q^T operand: lane (j, g) holds query row0+j, features 16kc+8g..+7.
   bf16x8 qr[T::KC];
@@ -336,6 +350,8 @@ void attn_kernel(AttnArgs a) {
   f32x16 s_cur[2];
 
   wait_loads_and_sync<0>();
+  // Window 0's invalid values are zeroed here; step 0's barrier publishes it.
+  if (!w0.full) zero_invalid_v<HD>(vbuf(0), w0);
   if (active) {
     s_cur[0] = s_cur[1] = f32x16{};
 #pragma unroll
@@ -343,44 +359,56 @@ void attn_kernel(AttnArgs a) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
         s_cur[kb] = mfma32x32x16(kread(kbuf(0), kb, kc), qr[kc], s_cur[kb]);
-    if (!W[0].full) mask_scores(s_cur, W[0]);
+    if (!w0.full) mask_scores(s_cur, w0);
     maybe_rescale<T::HB>(row_max(s_cur, scale_log2), o, m_run, l_run);
   }
 
-  // Iteration i: softmax and P*V of window i, scores of window i+1; loads of
-  // K(i+3) and V(i+2) in flight.  s_cur holds window i's (masked) scores with
-  // m_run already updated for them.  Blocks (A) and (B) are branch-free so
-  // their MFMAs interleave with VALU work; everything specific to partial
-  // windows happens in rare, uniform branches.
-  int stage = 0;                                  // i % 3
-  for (int i = 0; i < nw; ++i) {
-    // Loads of window i+1's K and window i's V were issued in iteration i-2
-    // (or the prologue); those of iteration i-1 may still be in flight.
-    if (i == 0) {
-      // the prologue waited for everything
-    } else if (i + 2 < nw) {
+  // Step j: softmax and P*V of window j, scores of window j+1, with the loads
+  // of K(j+3) and V(j+2) in flight.  On entry s_cur holds window j's (masked)
+  // scores with m_run already updated for them; K(j+1) and V(j) were issued
+  // in step j-2 (or the prologue), K(j+2) and V(j+1) in step j-1.
+  // Steady steps (j + 5 <= nw) touch only full windows, issue every load and
+  // wait for a constant count: no branch but the rare rescale.  The last
+  // steps (TAIL) handle partial windows and the end of the pipeline.
+  // `stage` = j % 3 (a literal in the steady loop, folded after inlining).
+  auto step = [&](const int j, const int stage, const bool TAIL) __attribute__((always_inline)) {
+    const int st1 = stage == 2 ? 0 : stage + 1;   // (j+1) % 3
+    const int st2 = st1 == 2 ? 0 : st1 + 1;       // (j+2) % 3
+    if (!TAIL) {
       wait_loads_and_sync<T::K_PER_WAVE + T::V_PER_WAVE>();
-    } else if (i + 1 < nw) {
-      wait_loads_and_sync<T::V_PER_WAVE>();
+      // K(j+3) -> the buffer of K(j) (read by QK(j) in step j-1);
+      // V(j+2) -> the buffer of V(j-1) (read by P*V(j-1)).
+      const bf16* kp = sp.k + (int64_t)(sp.start0 + (j + 3) * kAttnWindow) * HD;
+      const bf16* vp = sp.v + (int64_t)(sp.start0 + (j + 2) * kAttnWindow) * HD;
+#pragma unroll
+      for (int i = 0; i < T::K_PER_WAVE; ++i)
+        dma16(kp + koff[i], kbuf(stage) + (wave + kAttnWaves * i) * 1024);
+#pragma unroll
+      for (int i = 0; i < T::V_PER_WAVE; ++i)
+        dma16(vp + voff[i], vbuf(st2) + (wave + kAttnWaves * i) * 1024);
     } else {
-      wait_loads_and_sync<0>();
+      if (j + 2 < nw)
+        wait_loads_and_sync<T::K_PER_WAVE + T::V_PER_WAVE>();
+      else if (j + 1 < nw)
+        wait_loads_and_sync<T::V_PER_WAVE>();
+      else
+        wait_loads_and_sync<0>();
+      if (j > 0) {
+        const Window wj = win(j);
+        if (!wj.full) {
+          zero_invalid_v<HD>(vbuf(stage), wj);
+          __syncthreads();
+        }
+      }
+      if (j + 3 < nw) load_window<HD>(win(j + 3), kbuf(stage), vbuf(st2), true, false, koff, voff, wave);
+      if (j + 2 < nw) load_window<HD>(win(j + 2), kbuf(stage), vbuf(st2), false, true, koff, voff, wave);
     }
-    const int st1 = stage == 2 ? 0 : stage + 1;   // (i+1) % 3
-    const int st2 = st1 == 2 ? 0 : st1 + 1;       // (i+2) % 3
-    if (!W[0].full) {
-      zero_invalid_v<HD>(vbuf(stage), W[0]);
-      __syncthreads();
-    }
-    // K(i+3) -> the buffer of K(i) (consumed by QK(i) in iteration i-1);
-    // V(i+2) -> the buffer of V(i-1) (consumed by P*V(i-1)).
-    load_window<HD>(W[3], kbuf(stage), vbuf(st2), i + 3 < nw, false, koff, voff);
-    load_window<HD>(W[2], kbuf(stage), vbuf(st2), false, i + 2 < nw, koff, voff);
     if (active) {
       // (A) For each half kb of the window (32 keys): the shifted scores
-      //     (FMA) are read out of s[kb], then the scores of window i+1 are
+      //     (FMA) are read out of s[kb], then the scores of window j+1 are
       //     accumulated into the same registers while the exponentials, the
-      //     bf16 packing and the row sums of window i proceed.  On the last
-      //     window the new scores read a stale in-bounds K buffer and are
+      //     bf16 packing and the row sums of window j proceed.  In the last
+      //     step the new scores read a stale in-bounds K buffer and are
       //     discarded.
       const char* kl = kbuf(st1);
       uint32_t pw[4][4];
@@ -418,7 +446,7 @@ void attn_kernel(AttnArgs a) {
           __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
         }
       }
-      // (B) P*V of window i, and the row maximum of window i+1.  The V
+      // (B) P*V of window j, and the row maximum of window j+1.  The V
       //     operands of chunk c+1 are read while chunk c's MFMAs run.
       const bf16x8* vl = reinterpret_cast<const bf16x8*>(vbuf(stage));
       bf16x8 va[2][T::HB];
@@ -440,22 +468,28 @@ void attn_kernel(AttnArgs a) {
       // Keep the row-sum updates inside this block (they would otherwise be
       // sunk past it).
       __asm__ volatile("" ::"v"(l_run));
-      // (C) window i+1: mask a partial window, then the lazy rescale (which
-      //     applies to O accumulated through window i).
-      if (i + 1 < nw) {
-        if (!W[1].full) {
-          mask_scores(s_cur, W[1]);
+      // (C) window j+1: mask a partial window, then the lazy rescale (which
+      //     applies to O accumulated through window j).
+      if (!TAIL) {
+        maybe_rescale<T::HB>(mx, o, m_run, l_run);
+      } else if (j + 1 < nw) {
+        const Window w1 = win(j + 1);
+        if (!w1.full) {
+          mask_scores(s_cur, w1);
           mx = row_max(s_cur, scale_log2);
         }
         maybe_rescale<T::HB>(mx, o, m_run, l_run);
       }
     }
-    W[0] = W[1];
-    W[1] = W[2];
-    W[2] = W[3];
-    if (i + 4 < nw) W[3] = window(w_begin + i + 4);
-    stage = st1;
+  };
+
+  int j = 0;
+  for (; j + 7 <= nw; j += 3) {        // steps j, j+1, j+2 are all steady
+    step(j, 0, false);
+    step(j + 1, 1, false);
+    step(j + 2, 2, false);
   }
+  for (; j < nw; ++j) step(j, j % 3, true);
 
   if (!active) return;
   const float l_tot = sum_xor32(l_run);

@@ -101,7 +101,7 @@ struct AttnSess {
   int32_t seg_lo[2];  // valid ring slots: [seg_lo[i], seg_hi[i])
   int32_t seg_hi[2];
   int32_t nwin[3];    // 64-key windows over ring seg 0, ring seg 1, unit keys
-  int32_t nwin_total;
+  int32_t split0[4];  // key splits of segment t: [split0[t], split0[t+1]); split0[3] = nsplit
   int32_t n_qblk;
   int32_t nsplit;
   int32_t item0;
