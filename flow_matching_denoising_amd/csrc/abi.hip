@@ -96,8 +96,11 @@ int check_cache(const fmd_kv_cache* c, int idx) {
     return fail(FMD_E_SHAPE, "session %d: head_dim %d (must be 64 or 128)", idx, c->head_dim);
   if (c->n_heads < 1 || c->n_heads > 1024)
     return fail(FMD_E_SHAPE, "session %d: n_heads %d out of range", idx, c->n_heads);
-  if (c->cap_tokens < 16 || c->cap_tokens % 16 != 0 || c->cap_tokens > (int64_t)1 << 30)
-    return fail(FMD_E_SHAPE, "session %d: cap_tokens %lld (positive multiple of 16, <= 2^30)",
+  // One head's ring slice is addressed with 32-bit byte offsets.
+  if (c->cap_tokens < 16 || c->cap_tokens % 16 != 0 ||
+      c->cap_tokens * c->head_dim * 2 > (int64_t)INT32_MAX)
+    return fail(FMD_E_SHAPE,
+                "session %d: cap_tokens %lld (positive multiple of 16, cap*head_dim*2 < 2^31)",
                 idx, (long long)c->cap_tokens);
   if (c->len_tokens < 0 || c->len_tokens > c->cap_tokens || c->head_tokens < 0 ||
       c->head_tokens >= c->cap_tokens)
@@ -120,8 +123,8 @@ int check_step(const fmd_unit_step* u, int idx, bool need_z) {
   if ((rc = check_tensor(u->v_u, idx, "v_u"))) return rc;
   if (need_z && (rc = check_tensor(u->z, idx, "z"))) return rc;
   if (u->n_video < 0 || u->n_audio < 0 || (int64_t)u->n_video + u->n_audio < 1 ||
-      (int64_t)u->n_video + u->n_audio > (1 << 24))
-    return fail(FMD_E_INVAL, "session %d: n_video=%d n_audio=%d (need 1 <= n_q <= 2^24)", idx,
+      (int64_t)u->n_video + u->n_audio > (1 << 22))
+    return fail(FMD_E_INVAL, "session %d: n_video=%d n_audio=%d (need 1 <= n_q <= 2^22)", idx,
                 u->n_video, u->n_audio);
   if (need_z && !(u->h > 0.f && isfinite(u->h)))
     return fail(FMD_E_INVAL, "session %d: step size h=%g must be finite and > 0", idx, u->h);

@@ -76,8 +76,6 @@ struct Tiles {
 };
 
 struct Window {
-  const bf16* k;      // K of the window's first key
-  const bf16* v;      // V block of the window's first key
   int start;          // first key of the window (multiple of 16)
   int lo, hi;         // valid keys [lo, hi) of its segment
   bool full;          // every key of the window is valid
@@ -85,86 +83,89 @@ struct Window {
 
 // The keys one work item covers: windows [0, nw) of one key segment (the
 // valid ring range before the wrap point, the one after it, or the unit's own
-// keys), window j starting at key start0 + 64j of the segment.  In both key
-// layouts key k of a segment sits at element k*HD of the segment's base
-// (K: [keys][HD]; V: [keys/16][HD][16]).  Keys outside [lo, hi) are not part
-// of the segment; only the first and the last window of a segment can hold
-// such keys.  Every value involved is wave-uniform (scalar).
+// keys), window j starting at key start0 + 64j of the segment.  Keys outside
+// [lo, hi) are not part of the segment; only the first and the last window of
+// a segment can hold such keys.  Every value involved is wave-uniform.
 struct Span {
-  const bf16* k;
-  const bf16* v;
   int start0, lo, hi, nw;
 };
 
-template <int HD>
 __device__ __forceinline__ Window window_of(const Span& sp, int j) {
   Window r;
   r.start = sp.start0 + j * kAttnWindow;
-  r.k = sp.k + (int64_t)r.start * HD;
-  r.v = sp.v + (int64_t)r.start * HD;
   r.lo = sp.lo;
   r.hi = sp.hi;
   r.full = r.start >= sp.lo && r.start + kAttnWindow <= sp.hi;
   return r;
 }
 
-// Direct-to-LDS loads of one window; the hardware puts lane i's 16 bytes at
-// base + 16*i of the wave's 1 KiB destination.  K: the window's keys are kept
-// row by row (key k at byte 2*HD*k), each wave instruction reading 1 KiB of
-// whole rows (512/HD keys); the 16-byte chunk c of key k sits at chunk position
+// Window loads go global -> LDS through buffer resources (MUBUF loads with
+// the lds bit): one resource per head and key segment, whose size is the
+// segment's storage (cap or npad keys), so that a lane whose range-checked
+// offset falls past it reads zeros instead of faulting.  In both key layouts
+// key k sits at byte 2*HD*k of the segment (K: [keys][HD]; V:
+// [keys/16][HD][16]).  The hardware puts lane i's 16 bytes at M0 + 16*i.
+//
+// The load is issued from inline assembly on purpose: it has no register
+// outputs, and the compiler, which cannot tell one LDS stage buffer from
+// another, would otherwise wait for every LDS load in flight before each LDS
+// read.  The kernel orders these loads itself: s_waitcnt vmcnt(N) and a
+// barrier before any wave reads a tile (wait_loads_and_sync), and a barrier
+// between the last read of a buffer and the next load into it.
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+constexpr int kRsrcWord3 = 0x00020000;   // raw buffer, 32-bit data format
+
+__device__ __forceinline__ i32x4 make_rsrc(const bf16* base, int bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  i32x4 r;
+  r.x = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+  r.y = __builtin_amdgcn_readfirstlane((int)((uint32_t)(a >> 32) & 0xFFFFu));   // stride 0
+  r.z = __builtin_amdgcn_readfirstlane(bytes);                                   // num_records
+  r.w = kRsrcWord3;
+  return r;
+}
+
+// One wave instruction: 16 bytes per lane from rs at voff + soff to
+// dst + 16*lane.  voff (per lane) is range-checked, soff is not.  dst is
+// wave-uniform.
+__device__ __forceinline__ void dma16(const i32x4& rs, int voff, int soff, char* dst) {
+  const uint32_t m0 =
+      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)dst;
+  // One wait state between the M0 write and the LDS DMA that reads it.
+  __asm__ volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+                   :
+                   : "s"(m0), "v"(voff), "s"(rs), "s"(soff)
+                   : "memory", "m0");
+}
+
+// Direct-to-LDS loads of one window.  K: the window's keys are kept row by
+// row (key k at byte 2*HD*k), each wave instruction reading 1 KiB of whole
+// rows (512/HD keys); the 16-byte chunk c of key k sits at chunk position
 // c ^ kswz(k) of its row, so that the QK operand reads (16 lanes = 16 keys of
 // one chunk per LDS cycle) hit 16 different bank groups.  V^T: block
 // b = c*HB + hb, lane (g, e) -> feature 32hb + sigma(e), keys 16c + 8g .. +7,
 // which is one contiguous 1 KiB of the [keys/16][HD][16] layout per
-// instruction.  koff/voff are the lane offsets (elements, loop-invariant).
-// In a partial window every lane still loads (so each wave issues the same
-// number of loads), from an address clamped into the valid range; scores of
-// invalid keys are masked and their values zeroed in LDS before use.
-template <int HD>
-__device__ __forceinline__ void load_window(const Window& w, char* kdst, char* vdst, bool do_k,
-                                            bool do_v, const int (&koff)[Tiles<HD>::K_PER_WAVE],
-                                            const int (&voff)[Tiles<HD>::V_PER_WAVE],
-                                            int wave) {
-  using T = Tiles<HD>;
-  if (w.full) {
-    if (do_k)
+// instruction.  koff/voff are those lane offsets in bytes (loop-invariant).
+// CHECKED loads put the window offset into the range-checked lane offset
+// (first and last windows of a segment, which may reach past its storage);
+// the others pass it as the scalar offset.  Scores of keys outside [lo, hi)
+// are masked and their values zeroed in LDS before use.
+template <int HD, bool CHECKED, int N>
+__device__ __forceinline__ void load_tile(const i32x4& rs, int start, char* dst,
+                                          const int (&off)[N], int wave) {
+  const int woff = start * HD * 2;
 #pragma unroll
-      for (int i = 0; i < T::K_PER_WAVE; ++i)
-        __builtin_amdgcn_global_load_lds(w.k + koff[i], kdst + (wave + kAttnWaves * i) * 1024,
-                                         16, 0, 0);
-    if (do_v)
-#pragma unroll
-      for (int i = 0; i < T::V_PER_WAVE; ++i)
-        __builtin_amdgcn_global_load_lds(w.v + voff[i], vdst + (wave + kAttnWaves * i) * 1024,
-                                         16, 0, 0);
-  } else {
-    if (do_k)
-#pragma unroll
-      for (int i = 0; i < T::K_PER_WAVE; ++i) {
-        const int rel = koff[i] / HD;              // key within the window
-        const int col = koff[i] - rel * HD;
-        const int key = min(max(w.start + rel, w.lo), w.hi - 1);
-        __builtin_amdgcn_global_load_lds(w.k + (key - w.start) * HD + col,
-                                         kdst + (wave + kAttnWaves * i) * 1024, 16, 0, 0);
-      }
-    if (do_v)
-#pragma unroll
-      for (int i = 0; i < T::V_PER_WAVE; ++i) {
-        // voff = c*16*HD + feat*16 + 8g: chunk of 8 keys starting at 16c + 8g.
-        const int c = voff[i] / (16 * HD);
-        const int rem = voff[i] - c * 16 * HD;
-        const int feat = rem >> 4, g8 = rem & 15;
-        int key0 = w.start + c * 16 + g8;
-        key0 = min(max(key0, w.lo & ~7), (w.hi - 1) & ~7);    // an in-range 8-key chunk
-        const int rel = key0 - w.start;
-        __builtin_amdgcn_global_load_lds(w.v + (rel & ~15) * HD + feat * 16 + (rel & 15),
-                                         vdst + (wave + kAttnWaves * i) * 1024, 16, 0, 0);
-      }
+  for (int i = 0; i < N; ++i) {
+    char* d = dst + (wave + kAttnWaves * i) * 1024;
+    if (CHECKED)
+      dma16(rs, off[i] + woff, 0, d);
+    else
+      dma16(rs, off[i], woff, d);
   }
 }
 
 // Zero, in a window's V tile in LDS, the values of keys outside [lo, hi)
-// (they came from clamped loads or other ring slots, which may hold anything).
+// (ring slots outside the valid range may hold anything).
 // P is 0 for those keys, but 0 * NaN would poison O.  Partial windows only.
 template <int HD>
 __device__ __forceinline__ void zero_invalid_v(char* vbuf, const Window& win) {
@@ -185,11 +186,6 @@ __device__ __forceinline__ void zero_invalid_v(char* vbuf, const Window& win) {
       if (!(keep & (1u << t))) x.hw[t] = 0;
     *reinterpret_cast<u32x4*>(vbuf + slot * 16) = x.u;
   }
-}
-
-// One wave-wide direct-to-LDS load: lane i's 16 bytes at src go to dst + 16*i.
-__device__ __forceinline__ void dma16(const bf16* src, char* dst) {
-  __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 0);
 }
 
 // Wait until at most N of this wave's loads are outstanding, then barrier.
@@ -283,20 +279,21 @@ void attn_kernel(AttnArgs a) {
   const int w_begin = ls * nwin_seg / ns_seg;
   const int nw = (ls + 1) * nwin_seg / ns_seg - w_begin;    // >= 1
   Span sp;
+  i32x4 rk, rv;
   if (sg == 2) {
-    sp.k = s.kt_u + (int64_t)h * s.npad * HD;
-    sp.v = s.vt_u + (int64_t)h * s.npad * HD;
+    rk = make_rsrc(s.kt_u + (int64_t)h * s.npad * HD, s.npad * HD * 2);
+    rv = make_rsrc(s.vt_u + (int64_t)h * s.npad * HD, s.npad * HD * 2);
     sp.lo = 0;
     sp.hi = s.n_q;
   } else {
-    sp.k = s.ring_k + (int64_t)h * s.cap * HD;
-    sp.v = s.ring_v + (int64_t)h * s.cap * HD;
+    rk = make_rsrc(s.ring_k + (int64_t)h * s.cap * HD, (int)s.cap * HD * 2);
+    rv = make_rsrc(s.ring_v + (int64_t)h * s.cap * HD, (int)s.cap * HD * 2);
     sp.lo = sg == 0 ? s.seg_lo[0] : s.seg_lo[1];
     sp.hi = sg == 0 ? s.seg_hi[0] : s.seg_hi[1];
   }
   sp.start0 = (sp.lo & ~15) + w_begin * kAttnWindow;
   sp.nw = nw;
-  auto win = [&](int j) { return window_of<HD>(sp, j); };
+  auto win = [&](int j) { return window_of(sp, j); };
 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
@@ -305,19 +302,19 @@ void attn_kernel(AttnArgs a) {
   const bool active = row0 < s.n_q;                   // wave-uniform
   const int qrow = row0 + j32;
 
-  // Loop-invariant lane offsets of the window loads.
+  // Loop-invariant lane offsets (bytes) of the window loads.
   int koff[T::K_PER_WAVE], voff[T::V_PER_WAVE];
 #pragma unroll
   for (int i = 0; i < T::K_PER_WAVE; ++i) {
     constexpr int CPR = HD / 8;                   // 16-byte chunks per key row
     const int key = (wave + kAttnWaves * i) * (1024 / (2 * HD)) + lane / CPR;
-    koff[i] = key * HD + ((lane % CPR) ^ kswz<HD>(key)) * 8;
+    koff[i] = (key * HD + ((lane % CPR) ^ kswz<HD>(key)) * 8) * 2;
   }
   const int sigma = (j32 & 3) | (((j32 >> 3) & 3) << 2) | (((j32 >> 2) & 1) << 4);
 #pragma unroll
   for (int i = 0; i < T::V_PER_WAVE; ++i) {
     const int b = wave + kAttnWaves * i;
-    voff[i] = (b / T::HB) * 16 * HD + ((b % T::HB) * 32 + sigma) * 16 + g * 8;
+    voff[i] = ((b / T::HB) * 16 * HD + ((b % T::HB) * 32 + sigma) * 16 + g * 8) * 2;
   }
   // QK operand reads: lane (g, rho) wants key 32kb + perm_k(rho), chunk 2kc+g;
   // byte offsets within the K tile for kb = 0 (kb adds 64*HD).
@@ -331,9 +328,13 @@ void attn_kernel(AttnArgs a) {
 
   // Prologue: K(0), V(0), K(1), V(1), K(2).
   const Window w0 = win(0);
-  load_window<HD>(w0, kbuf(0), vbuf(0), true, true, koff, voff, wave);
-  if (nw > 1) load_window<HD>(win(1), kbuf(1), vbuf(1), true, true, koff, voff, wave);
-  if (nw > 2) load_window<HD>(win(2), kbuf(2), vbuf(2), true, false, koff, voff, wave);
+  load_tile<HD, true>(rk, w0.start, kbuf(0), koff, wave);
+  load_tile<HD, true>(rv, w0.start, vbuf(0), voff, wave);
+  if (nw > 1) {
+    load_tile<HD, true>(rk, w0.start + kAttnWindow, kbuf(1), koff, wave);
+    load_tile<HD, true>(rv, w0.start + kAttnWindow, vbuf(1), voff, wave);
+  }
+  if (nw > 2) load_tile<HD, true>(rk, w0.start + 2 * kAttnWindow, kbuf(2), koff, wave);
 
   // Q^T operand: lane (j, g) holds query row0+j, features 16kc+8g..+7.
   bf16x8 qr[T::KC];
@@ -378,14 +379,8 @@ void attn_kernel(AttnArgs a) {
       wait_loads_and_sync<T::K_PER_WAVE + T::V_PER_WAVE>();
       // K(j+3) -> the buffer of K(j) (read by QK(j) in step j-1);
       // V(j+2) -> the buffer of V(j-1) (read by P*V(j-1)).
-      const bf16* kp = sp.k + (int64_t)(sp.start0 + (j + 3) * kAttnWindow) * HD;
-      const bf16* vp = sp.v + (int64_t)(sp.start0 + (j + 2) * kAttnWindow) * HD;
-#pragma unroll
-      for (int i = 0; i < T::K_PER_WAVE; ++i)
-        dma16(kp + koff[i], kbuf(stage) + (wave + kAttnWaves * i) * 1024);
-#pragma unroll
-      for (int i = 0; i < T::V_PER_WAVE; ++i)
-        dma16(vp + voff[i], vbuf(st2) + (wave + kAttnWaves * i) * 1024);
+      load_tile<HD, false>(rk, sp.start0 + (j + 3) * kAttnWindow, kbuf(stage), koff, wave);
+      load_tile<HD, false>(rv, sp.start0 + (j + 2) * kAttnWindow, vbuf(st2), voff, wave);
     } else {
       if (j + 2 < nw)
         wait_loads_and_sync<T::K_PER_WAVE + T::V_PER_WAVE>();
@@ -400,74 +395,90 @@ void attn_kernel(AttnArgs a) {
           __syncthreads();
         }
       }
-      if (j + 3 < nw) load_window<HD>(win(j + 3), kbuf(stage), vbuf(st2), true, false, koff, voff, wave);
-      if (j + 2 < nw) load_window<HD>(win(j + 2), kbuf(stage), vbuf(st2), false, true, koff, voff, wave);
+      if (j + 3 < nw)
+        load_tile<HD, true>(rk, sp.start0 + (j + 3) * kAttnWindow, kbuf(stage), koff, wave);
+      if (j + 2 < nw)
+        load_tile<HD, true>(rv, sp.start0 + (j + 2) * kAttnWindow, vbuf(st2), voff, wave);
     }
     if (active) {
-      // (A) For each half kb of the window (32 keys): the shifted scores
-      //     (FMA) are read out of s[kb], then the scores of window j+1 are
-      //     accumulated into the same registers while the exponentials, the
-      //     bf16 packing and the row sums of window j proceed.  In the last
-      //     step the new scores read a stale in-bounds K buffer and are
-      //     discarded.
+      // One step is NQK + NPV MFMA slots, issued in this order: the QK
+      // product of window j+1 (half kb = 0, then 1; C starts at zero), then
+      // the P*V product of window j (16-key chunks c = 0..3).  Each slot
+      // issues the LDS read of the operand D slots ahead (a ring of D+1
+      // registers), its MFMA, and a share of the softmax VALU work of window
+      // j, so that the matrix core and the VALU stay busy together instead of
+      // alternating phases:
+      //   x0/x1   shifted scores of window j (half 0 before slot 0; half 1
+      //           spread over the slots of half 0, before its scores are
+      //           overwritten);
+      //   E(g)    two exp2, one bf16 pack and one row-sum dot2 (group g =
+      //           8 kb + 4 c2 + t -> P chunk 2kb + c2, keys 8t'..), each done
+      //           before the P*V chunk that needs it;
+      //   max     the row maximum of window j+1's scores, after their MFMAs.
+      // sched_barrier(0) after each slot keeps this order.
+      constexpr int NQK = 2 * T::KC;
+      constexpr int NPV = 4 * T::HB;
+      constexpr int N = NQK + NPV;
+      constexpr int D = 3;                  // operand read distance (slots)
+      constexpr int R = D + 1;              // operand ring size
       const char* kl = kbuf(st1);
-      uint32_t pw[4][4];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        // All K operands of this half are read up front so their LDS latency
-        // overlaps (one wait instead of one per MFMA).
-        bf16x8 ka[T::KC];
-#pragma unroll
-        for (int kc = 0; kc < T::KC; ++kc) ka[kc] = kread(kl, kb, kc);
-        float x[16];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) x[r] = __builtin_fmaf(s_cur[kb][r], scale_log2, -m_run);
-        __builtin_amdgcn_sched_barrier(0);   // keep the reads issued ahead of the MFMAs
-        s_cur[kb] = f32x16{};
-#pragma unroll
-        for (int kc = 0; kc < T::KC; ++kc) s_cur[kb] = mfma32x32x16(ka[kc], qr[kc], s_cur[kb]);
-#pragma unroll
-        for (int c2 = 0; c2 < 2; ++c2) {
-#pragma unroll
-          for (int t = 0; t < 4; ++t) {
-            const float e0 = __builtin_amdgcn_exp2f(x[c2 * 8 + 2 * t]);
-            const float e1 = __builtin_amdgcn_exp2f(x[c2 * 8 + 2 * t + 1]);
-            const uint32_t w2 = pack_bf16(e0, e1);
-            pw[kb * 2 + c2][t] = w2;
-            l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w2),
-                                                    __builtin_bit_cast(bf16x2_t, 0x3F803F80u),
-                                                    l_run, false);
-          }
-        }
-        // Each MFMA followed by VALU work (exp/pack/row sum).
-#pragma unroll
-        for (int t = 0; t < T::KC; ++t) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
-        }
-      }
-      // (B) P*V of window j, and the row maximum of window j+1.  The V
-      //     operands of chunk c+1 are read while chunk c's MFMAs run.
       const bf16x8* vl = reinterpret_cast<const bf16x8*>(vbuf(stage));
-      bf16x8 va[2][T::HB];
+      auto operand = [&](int i) {
+        return i < NQK ? kread(kl, i / T::KC, i % T::KC)
+                       : vl[((i - NQK) / T::HB * T::HB + (i - NQK) % T::HB) * 64 + lane];
+      };
+      float x0[16], x1[16];
 #pragma unroll
-      for (int hb = 0; hb < T::HB; ++hb) va[0][hb] = vl[hb * 64 + lane];
+      for (int r = 0; r < 16; ++r) x0[r] = __builtin_fmaf(s_cur[0][r], scale_log2, -m_run);
+      bf16x8 opr[R];
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        if (c + 1 < 4)
+      for (int i = 0; i < D; ++i) opr[i] = operand(i);
+      uint32_t pw[4][4];
+      float mxa = kNegInf, mxb = kNegInf;
+      // Slot of E group g, of the r-th FMA of x1, of the k-th max op of half kb.
+      auto e_slot = [](int g) {
+        return T::KC == 8 ? (g < 8 ? 2 * g : 9 + 2 * (g - 8)) : (g < 8 ? g : 5 + (g - 8));
+      };
+      auto f1_slot = [](int r) { return r * T::KC / 16; };
+      auto max_slot = [](int kb, int k) {
+        return (kb == 0 ? T::KC : NQK) + 3 + (T::KC == 8 ? k : k / 2);
+      };
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-          for (int hb = 0; hb < T::HB; ++hb)
-            va[(c + 1) & 1][hb] = vl[((c + 1) * T::HB + hb) * 64 + lane];
-        __builtin_amdgcn_sched_barrier(0);   // chunk c+1's reads go out before chunk c's MFMAs
-        const u32x4 pv4 = {pw[c][0], pw[c][1], pw[c][2], pw[c][3]};
-        const bf16x8 pc = __builtin_bit_cast(bf16x8, pv4);
+      for (int i = 0; i < N; ++i) {
+        if (i + D < N) opr[(i + D) % R] = operand(i + D);
+        if (i < NQK) {
+          const int kb = i / T::KC, kc = i % T::KC;
+          s_cur[kb] = mfma32x32x16(opr[i % R], qr[kc], kc == 0 ? f32x16{} : s_cur[kb]);
+        } else {
+          const int c = (i - NQK) / T::HB, hb = (i - NQK) % T::HB;
+          const u32x4 pv4 = {pw[c][0], pw[c][1], pw[c][2], pw[c][3]};
+          o[hb] = mfma32x32x16(opr[i % R], __builtin_bit_cast(bf16x8, pv4), o[hb]);
+        }
 #pragma unroll
-        for (int hb = 0; hb < T::HB; ++hb) o[hb] = mfma32x32x16(va[c & 1][hb], pc, o[hb]);
+        for (int r = 0; r < 16; ++r)
+          if (f1_slot(r) == i) x1[r] = __builtin_fmaf(s_cur[1][r], scale_log2, -m_run);
+#pragma unroll
+        for (int g = 0; g < 16; ++g) {
+          if (e_slot(g) != i) continue;
+          const int kb = g >> 3, c2 = (g >> 2) & 1, t = g & 3;
+          const float* xv = kb == 0 ? x0 : x1;
+          const float e0 = __builtin_amdgcn_exp2f(xv[c2 * 8 + 2 * t]);
+          const float e1 = __builtin_amdgcn_exp2f(xv[c2 * 8 + 2 * t + 1]);
+          const uint32_t w2 = pack_bf16(e0, e1);
+          pw[kb * 2 + c2][t] = w2;
+          l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w2),
+                                                  __builtin_bit_cast(bf16x2_t, 0x3F803F80u),
+                                                  l_run, false);
+        }
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          if (max_slot(0, k) == i) mxa = max3f(mxa, s_cur[0][2 * k], s_cur[0][2 * k + 1]);
+          if (max_slot(1, k) == i) mxb = max3f(mxb, s_cur[1][2 * k], s_cur[1][2 * k + 1]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
       }
-      float mx = row_max(s_cur, scale_log2);
-      // Keep the row-sum updates inside this block (they would otherwise be
-      // sunk past it).
-      __asm__ volatile("" ::"v"(l_run));
+      float mx = max_xor32(fmaxf(mxa, mxb)) * scale_log2;
       // (C) window j+1: mask a partial window, then the lazy rescale (which
       //     applies to O accumulated through window j).
       if (!TAIL) {

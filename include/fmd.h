@@ -64,7 +64,9 @@ typedef enum {
  *       stored feature-major: element (h, slot p, e) is at
  *       ((h*(cap/16) + p/16)*head_dim + e)*16 + p%16)
  *   head_dim   : 64 or 128
- *   cap_tokens : ring capacity in tokens, a positive multiple of 16
+ *   cap_tokens : ring capacity in tokens, a positive multiple of 16, with
+ *                cap_tokens*head_dim*2 < 2^31 (one head's slice is addressed
+ *                with 32-bit byte offsets)
  *   len_tokens : valid tokens, 0..cap_tokens
  *   head_tokens: slot the next token goes to, 0..cap_tokens-1
  * The valid tokens are the len_tokens slots just before head_tokens (mod cap).
@@ -103,7 +105,7 @@ int fmd_kv_append_batched(fmd_kv_cache* const* caches, const void* const* k_slic
  * One session's inputs for ONE solver step.
  *   cache     : the session's ring in its post-append state (read only)
  *   q, k_u, v_u: bf16 [n_q][n_heads][head_dim], the unit's queries and its own
- *               keys/values, n_q = n_video + n_audio, rows video then audio
+ *               keys/values, n_q = n_video + n_audio (1..2^22), rows video then audio
  *   z         : fp32 [n_q][n_heads*head_dim], updated in place
  *   h         : positive step size; the step is z <- z - h * v
  */

@@ -51,6 +51,7 @@ def _append(c, T, ks=FAKE + 0x200000, vs=FAKE + 0x300000):
 
 @pytest.mark.parametrize("mut,code", [
     (dict(hd=96), -2), (dict(hd=0), -2), (dict(cap=100), -2), (dict(cap=0), -2),
+    (dict(hd=128, cap=1 << 23, ln=0, head=0), -2),
     (dict(H=0), -2), (dict(ln=129), -1), (dict(head=128), -1), (dict(head=-1), -1),
     (dict(k=FAKE + 8), -4), (dict(v=0), -1),
 ])
@@ -112,6 +113,7 @@ def test_workspace_bytes_is_host_arithmetic():
 
 @pytest.mark.parametrize("kw,code", [
     (dict(n_video=0, n_audio=0), -1), (dict(n_video=-1), -1), (dict(q=FAKE + 4), -4),
+    (dict(n_video=1 << 22, n_audio=1), -1),
     (dict(q=0), -1),
 ])
 def test_step_validation(kw, code):
