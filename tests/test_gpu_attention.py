@@ -70,6 +70,17 @@ def test_attention_key_splits_agree(split):
     assert_close(got, ref, f"O split={split}")
 
 
+@pytest.mark.parametrize("length", [1, 59, 64, 130, 200, 250, 320, 400, 450, 510, 580, 640, 700,
+                                    760, 1000])
+def test_attention_window_counts(length):
+    # One split per key segment; the ring segment starts off a 16-slot block
+    # so that its first and last 64-key windows are partial.  1..17 windows
+    # walk the pipeline's prologue, steady and last-step paths.
+    head = (5 + length) % 2048
+    got, ref = _attn_case(1, 128, 2048, length, head, 40, seed=length, split=1)
+    assert_close(got, ref, f"O length={length}")
+
+
 def test_single_key_returns_value_exactly():
     rng = np.random.default_rng(1)
     H, hd = 3, 128
