@@ -206,25 +206,53 @@ int env_int(const char* name, int dflt) {
   return atoi(v);
 }
 
-// Key splits: enough work items to keep every CU busy for several rounds,
-// with at least kMinWindows windows per item.  Depends only on the shapes.
-void choose_splits(std::vector<SessPlan>& plans, int H) {
+// Key splits.  Work items of one launch are dispatched to the CUs in rounds;
+// with items of about equal length, a launch whose item count is a multiple
+// of the CU count leaves no CU idle in its last round.  The item size is
+// chosen among candidates of 1..16 rounds (at least kMinWindows windows per
+// item) by that round efficiency, with a small penalty per split for the
+// combine pass, which reads every split's partial output once.  Depends only
+// on the shapes.  FMD_ATTN_SPLIT forces a split count per session,
+// FMD_ATTN_TARGET_ITEMS a target item count (both for experiments).
+int plan_split_count(const SessPlan& p, double per_item) {
   constexpr int kMinWindows = 16;
-  const int target_items = env_int("FMD_ATTN_TARGET_ITEMS", 4 * kTargetCUs);
+  int ns = (int)ceil(p.nwin_total / (per_item > 1 ? per_item : 1.0));
+  ns = std::min(ns, std::max(1, p.nwin_total / kMinWindows));
+  return std::max(1, std::min(ns, p.nwin_total));
+}
+
+void choose_splits(std::vector<SessPlan>& plans, int H) {
   const int forced = env_int("FMD_ATTN_SPLIT", 0);
+  if (forced > 0) {
+    for (auto& p : plans) set_splits(p, forced);
+    return;
+  }
   double work = 0;
   for (auto& p : plans) work += (double)H * p.n_qblk * p.nwin_total;
-  const double per_item = work / target_items;
-  for (auto& p : plans) {
-    int ns;
-    if (forced > 0) {
-      ns = forced;
-    } else {
-      ns = (int)ceil(p.nwin_total / (per_item > 1 ? per_item : 1.0));
-      ns = std::min(ns, std::max(1, p.nwin_total / kMinWindows));
+  const int target_env = env_int("FMD_ATTN_TARGET_ITEMS", 0);
+  double best_cost = 1e30, best_per_item = work;
+  for (int rounds = 1; rounds <= 16; ++rounds) {
+    const int target = target_env > 0 ? target_env : rounds * kTargetCUs;
+    const double per_item = work / target;
+    // Ring-segment items are the long ones (the unit's own keys are a
+    // short segment of their own); count their rounds.
+    double long_items = 0, split_sum = 0;
+    for (auto& p : plans) {
+      SessPlan q = p;
+      set_splits(q, plan_split_count(p, per_item));
+      long_items += (double)H * p.n_qblk * q.split0[2];
+      split_sum += q.nsplit;
     }
-    set_splits(p, std::max(1, std::min(ns, p.nwin_total)));
+    const double r = long_items / kTargetCUs;
+    const double eff = r > 0 ? r / ceil(r) : 1.0;
+    const double cost = 1.0 / eff + 0.004 * split_sum / plans.size();
+    if (cost < best_cost - 1e-9) {
+      best_cost = cost;
+      best_per_item = per_item;
+    }
+    if (target_env > 0) break;
   }
+  for (auto& p : plans) set_splits(p, plan_split_count(p, best_per_item));
 }
 
 // Workspace layout, sessions in order.  With o_external, O goes to the
