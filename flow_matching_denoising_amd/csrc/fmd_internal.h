@@ -160,8 +160,8 @@ constexpr int kAttnRowsPerWave = 32;
 constexpr int kAttnBlockM = kAttnWaves * kAttnRowsPerWave;   // 256 query rows per block
 constexpr int kAttnWindow = 64;                              // keys per window
 
-// Projection tiling: 256 rows x 128 output features per block.
-constexpr int kProjTile = 256;
+// Projection tiling: 160 rows x 128 output features per block.
+constexpr int kProjTile = 160;
 constexpr int kProjTileN = 128;
 
 }  // namespace fmd

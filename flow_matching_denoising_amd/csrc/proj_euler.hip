@@ -7,36 +7,68 @@
 // velocity network is reduced here to one dense output projection of the
 // attention output; sampling runs tau from 1 to 0 with positive step sizes h.
 //
-// Tile 256 rows x 128 output features, k step 64, 8 waves as 4 x 2, each wave
-// 64 x 64 = 2 x 2 MFMA 32x32 tiles, fp32 accumulators.  Large tiles keep the
-// L2->CU traffic near 47 B/clk per CU at full MFMA rate.  O and W rows are both
+// Tile 160 rows x 128 output features, k step 64, 4 waves (one per SIMD);
+// wave w owns output features 32w..32w+31 of the tile for all 160 rows (five
+// MFMA 32x32 accumulators).  160-row tiles split a 928-row unit into 6 row
+// tiles, so a 5120-wide projection is 240 work-groups: one balanced round on
+// 256 CUs (256-row tiles would leave 96 CUs idle).  O and W rows are both
 // k-contiguous ([n_q][d] and [d_out][d_in]).  Operands go global -> LDS with
-// global_load_lds_dwordx4, one 1 KiB block (8 rows x 64 k) per wave
-// instruction, each row read whole (128 contiguous bytes): gathering the MFMA
-// operand order directly (32 rows x 32 bytes per instruction) runs at about a
-// third of the L2 bandwidth.  Inside a block, the 16-byte chunk c of row r is
-// stored at chunk position c ^ ((r >> 1) & 7), which keeps the ds_read_b128
-// operand reads (16 lanes = 16 rows of one chunk per LDS cycle) free of bank
-// conflicts; the per-lane read offsets are loop-invariant.  Three LDS stages
-// (144 KiB) keep two k steps of loads in flight.  Item order inside a session:
-// output-feature tile major, row tile minor, so the row tiles that share one
-// slab of W are adjacent and run on the same XCD.
+// MUBUF loads (lds bit), one 1 KiB block (8 rows x 64 k) per wave
+// instruction, each row read whole (128 contiguous bytes).  Inside a block,
+// the 16-byte chunk c of row r is stored at chunk position c ^ ((r >> 1) & 7),
+// which keeps the ds_read_b128 operand reads (16 lanes = 16 rows of one
+// chunk per LDS cycle) free of bank conflicts.  The buffer resources cover
+// exactly the tile's valid rows, so rows past n_q (or past d for W) read as
+// zeros.  Three LDS stages (108 KiB) keep two k steps of loads in flight.
+// Item order inside a session: output-feature tile major, row tile minor, so
+// the row tiles that share one slab of W are adjacent and run on the same XCD.
 #include "fmd_internal.h"
 
 namespace fmd {
 
 namespace {
 
-constexpr int BM = kProjTile;                       // 256 rows
+constexpr int BM = kProjTile;                       // 160 rows
 constexpr int BN = kProjTileN;                      // 128 output features
 constexpr int BK = 64;
-constexpr int WAVES = 8;
+constexpr int WAVES = 4;
+constexpr int MT = BM / 32;                         // 5 row tiles of 32
 constexpr int STAGES = 3;
-constexpr int A_BLOCKS = (BM / 32) * (BK / 16);     // 32 operand blocks of 1 KiB
-constexpr int B_BLOCKS = (BN / 32) * (BK / 16);     // 16
+constexpr int A_BLOCKS = BM / 8;                    // 20 blocks of 8 rows x 64 k
+constexpr int B_BLOCKS = BN / 8;                    // 16
 constexpr int STAGE_BYTES = (A_BLOCKS + B_BLOCKS) * 1024;
-constexpr int LOADS_PER_WAVE = (A_BLOCKS + B_BLOCKS) / WAVES;   // 6
-constexpr int LDS_BYTES = STAGES * STAGE_BYTES;     // 144 KiB
+constexpr int LOADS_PER_WAVE = (A_BLOCKS + B_BLOCKS) / WAVES;   // 9
+constexpr int LDS_BYTES = STAGES * STAGE_BYTES;     // 108 KiB
+static_assert(A_BLOCKS % WAVES == 0 && B_BLOCKS % WAVES == 0, "loads must split evenly over waves");
+static_assert(BN == 32 * WAVES, "one 32-feature column tile per wave");
+
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+constexpr int kRsrcWord3 = 0x00020000;   // raw buffer, 32-bit data format
+
+__device__ __forceinline__ i32x4 make_rsrc(const bf16* base, int bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  i32x4 r;
+  r.x = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+  r.y = __builtin_amdgcn_readfirstlane((int)((uint32_t)(a >> 32) & 0xFFFFu));   // stride 0
+  r.z = __builtin_amdgcn_readfirstlane(bytes);                                   // num_records
+  r.w = kRsrcWord3;
+  return r;
+}
+
+// One wave instruction: 16 bytes per lane from rs at voff + soff to
+// dst + 16*lane (dst wave-uniform; voff range-checked).  Issued from inline
+// assembly so that the compiler does not make every LDS read wait for every
+// LDS load in flight; the kernel orders them itself (vmcnt wait + barrier
+// before reading a stage, barrier before reloading it).  One wait state
+// separates the M0 write from the load that reads it.
+__device__ __forceinline__ void dma16(const i32x4& rs, int voff, int soff, char* dst) {
+  const uint32_t m0 =
+      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)dst;
+  __asm__ volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+                   :
+                   : "s"(m0), "v"(voff), "s"(rs), "s"(soff)
+                   : "memory", "m0");
+}
 
 template <int N>
 __device__ __forceinline__ void wait_loads_and_sync() {
@@ -56,42 +88,42 @@ __global__ __launch_bounds__(WAVES * 64) void proj_kernel(ProjArgs a) {
   for (int i = 1; i < kMaxSessPerLaunch; ++i)
     if (i < a.n_sess && item >= a.s[i].item0) si = i;
   const ProjSess& s = a.s[si];
+  // Session fields are read once (stores to z could otherwise force reloads).
+  float* const z = s.z;
+  const int n_q = s.n_q;
+  const float hstep = s.h;
   const int d = a.d;
   const int local = item - s.item0;
   const int mt = local % s.n_mtiles;
   const int nt = local / s.n_mtiles;
   const int m0 = mt * BM, n0 = nt * BN;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int wm = wave >> 1, wn = wave & 1;        // 4 x 2 waves of 64 x 64
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
   const int r = lane & 31, g = lane >> 5;
 
-  // Loop-invariant load sources: wave w fills 1 KiB blocks w, w+8, ... (blocks
-  // 0..31: A = O rows, 32..47: B = W rows; block b holds 8 consecutive rows of
-  // its operand, lane i -> row i/8, k chunk (i%8) ^ swizzle(row)).  Rows past
-  // n_q (O) or d (W) are clamped to the last row: computed, never stored.
-  const bf16* src[LOADS_PER_WAVE];
+  // The tile's rows of O and W; rows past n_q (past d) read as zeros.
+  const i32x4 ra = make_rsrc(s.o + (int64_t)m0 * d, min(BM, n_q - m0) * d * 2);
+  const i32x4 rb = make_rsrc(a.w + (int64_t)n0 * d, min(BN, d - n0) * d * 2);
+
+  // Loop-invariant lane offsets (bytes): wave w fills 1 KiB blocks w, w+4, ...
+  // (blocks 0..19: A, 20..35: B); block b holds 8 consecutive rows of its
+  // operand, lane i -> row i/8, k chunk (i%8) ^ swizzle(row).
+  int voff[LOADS_PER_WAVE];
 #pragma unroll
   for (int i = 0; i < LOADS_PER_WAVE; ++i) {
     const int b = wave + WAVES * i;
-    const int rib = lane >> 3;                       // row within the block
-    if (b < A_BLOCKS) {
-      const int rt = b * 8 + rib;                    // row within the A tile
-      const int chunk = (lane & 7) ^ ((rt >> 1) & 7);
-      const int row = min(m0 + rt, s.n_q - 1);
-      src[i] = s.o + (int64_t)row * d + chunk * 8;
-    } else {
-      const int rt = (b - A_BLOCKS) * 8 + rib;       // row within the B tile
-      const int chunk = (lane & 7) ^ ((rt >> 1) & 7);
-      const int row = min(n0 + rt, d - 1);           // d may be an odd multiple of 64
-      src[i] = a.w + (int64_t)row * d + chunk * 8;
-    }
+    const int rt = (i < A_BLOCKS / WAVES ? b : b - A_BLOCKS) * 8 + (lane >> 3);
+    const int chunk = (lane & 7) ^ ((rt >> 1) & 7);
+    voff[i] = rt * d * 2 + chunk * 16;
   }
-  auto load_stage = [&](int kt, int st) {
+  auto load_stage = [&](int kt, int st) __attribute__((always_inline)) {
     char* base = lds + st * STAGE_BYTES;
 #pragma unroll
-    for (int i = 0; i < LOADS_PER_WAVE; ++i)
-      __builtin_amdgcn_global_load_lds(src[i] + kt * BK, base + (wave + WAVES * i) * 1024, 16, 0,
-                                       0);
+    for (int i = 0; i < LOADS_PER_WAVE; ++i) {
+      // Blocks wave + 4i: i < 5 are A blocks for every wave.
+      dma16(i < A_BLOCKS / WAVES ? ra : rb, voff[i], kt * BK * 2,
+            base + (wave + WAVES * i) * 1024);
+    }
   };
   // Operand reads: lane (g, r) of a 32-row tile wants row r, k chunk 2kc+g;
   // byte offset within the tile (tile bases are compile-time immediates).
@@ -100,7 +132,9 @@ __global__ __launch_bounds__(WAVES * 64) void proj_kernel(ProjArgs a) {
   for (int kc = 0; kc < 4; ++kc)
     roff[kc] = (r >> 3) * 1024 + ((r & 7) * 8 + ((2 * kc + g) ^ ((r >> 1) & 7))) * 16;
 
-  f32x16 acc[2][2] = {{f32x16{}, f32x16{}}, {f32x16{}, f32x16{}}};
+  f32x16 acc[MT];
+#pragma unroll
+  for (int i = 0; i < MT; ++i) acc[i] = f32x16{};
   const int nk = d / BK;
   load_stage(0, 0);
   if (nk > 1) load_stage(1, 1);
@@ -113,42 +147,38 @@ __global__ __launch_bounds__(WAVES * 64) void proj_kernel(ProjArgs a) {
     const int st2 = st == 0 ? 2 : st - 1;       // (kt+2) % 3: the buffer of k step kt-1
     if (kt + 2 < nk) load_stage(kt + 2, st2);
     const char* al = lds + st * STAGE_BYTES;
-    const char* bl = al + A_BLOCKS * 1024;
-    bf16x8 av[4][2], bv[4][2];
+    const char* bl = al + A_BLOCKS * 1024 + wave * 4096;
 #pragma unroll
-    for (int kc = 0; kc < 4; ++kc)
+    for (int kc = 0; kc < 4; ++kc) {
+      const bf16x8 bv = *reinterpret_cast<const bf16x8*>(bl + roff[kc]);
+      bf16x8 av[MT];
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        av[kc][i] = *reinterpret_cast<const bf16x8*>(al + (2 * wm + i) * 4096 + roff[kc]);
-        bv[kc][i] = *reinterpret_cast<const bf16x8*>(bl + (2 * wn + i) * 4096 + roff[kc]);
-      }
+      for (int i = 0; i < MT; ++i) av[i] = *reinterpret_cast<const bf16x8*>(al + i * 4096 + roff[kc]);
 #pragma unroll
-    for (int kc = 0; kc < 4; ++kc)
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int jn = 0; jn < 2; ++jn)
-          acc[i][jn] = mfma32x32x16(av[kc][i], bv[kc][jn], acc[i][jn]);
+      for (int i = 0; i < MT; ++i) acc[i] = mfma32x32x16(av[i], bv, acc[i]);
+    }
     st = st == 2 ? 0 : st + 1;
   }
 
   // Epilogue: z[m][n] -= h * v[m][n].  C layout: lane (col r, group g),
-  // register q -> row 8*(q/4) + 4*g + q%4 of the 32x32 tile.
-  const float hstep = s.h;
+  // register q -> row 8*(q/4) + 4*g + q%4 of the 32x32 tile.  All of a row
+  // tile's z values are loaded before any is stored, so the loads overlap.
+  const int n = n0 + wave * 32 + r;
+  if (n >= d) return;
+  float* const zc = z + n;
+  const bool full = m0 + BM <= n_q;                // uniform
 #pragma unroll
-  for (int jn = 0; jn < 2; ++jn) {
-    const int n = n0 + (2 * wn + jn) * 32 + r;
-    if (n >= d) continue;
+  for (int i = 0; i < MT; ++i) {
+    float zv[16];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
+    for (int q = 0; q < 16; ++q) {
+      const int m = m0 + i * 32 + (q >> 2) * 8 + g * 4 + (q & 3);
+      zv[q] = (full || m < n_q) ? zc[(int64_t)m * d] : 0.f;
+    }
 #pragma unroll
-      for (int q = 0; q < 16; ++q) {
-        const int m = m0 + (2 * wm + i) * 32 + (q >> 2) * 8 + g * 4 + (q & 3);
-        if (m < s.n_q) {
-          float* zp = s.z + (int64_t)m * d + n;
-          *zp = *zp - hstep * acc[i][jn][q];
-        }
-      }
+    for (int q = 0; q < 16; ++q) {
+      const int m = m0 + i * 32 + (q >> 2) * 8 + g * 4 + (q & 3);
+      if (full || m < n_q) zc[(int64_t)m * d] = zv[q] - hstep * acc[i][q];
     }
   }
 }
