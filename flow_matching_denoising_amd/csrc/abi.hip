@@ -268,7 +268,7 @@ size_t layout_workspace(std::vector<SessPlan>& plans, int H, int hd, bool o_exte
     if (!o_external) off = align256(off + (size_t)p.n_q * H * hd * 2);
     p.off_opart = p.off_lse = off;
     if (p.nsplit > 1) {
-      off = align256(off + (size_t)p.nsplit * p.n_q * H * hd * 4);
+      off = align256(off + (size_t)p.nsplit * p.n_q * H * hd * 2);
       p.off_lse = off;
       off = align256(off + (size_t)p.nsplit * p.n_q * H * 4);
     }
@@ -349,7 +349,7 @@ int enqueue_steps(const fmd_unit_step* units, int n, const std::vector<SessPlan>
       as.ring_k = static_cast<const bf16*>(c->k);
       as.ring_v = static_cast<const bf16*>(c->v);
       as.o = o;
-      as.opart = reinterpret_cast<float*>(ws + p.off_opart);
+      as.opart = reinterpret_cast<bf16*>(ws + p.off_opart);
       as.lse = reinterpret_cast<float*>(ws + p.off_lse);
       as.cap = c->cap_tokens;
       as.n_q = p.n_q;

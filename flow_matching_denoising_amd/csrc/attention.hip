@@ -506,33 +506,25 @@ void attn_kernel(AttnArgs a) {
   const float l_tot = sum_xor32(l_run);
   if (qrow >= s.n_q) return;
   const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
-  if (s.nsplit == 1) {
+  // nsplit == 1: the final O; else this split's normalised partial (bf16)
+  // and its log-sum-exp, merged by the combine kernel.
+  bf16* const dst_row = s.nsplit == 1 ? s.o + ((int64_t)qrow * H + h) * HD
+                                      : s.opart + (((int64_t)split * s.n_q + qrow) * H + h) * HD;
 #pragma unroll
-    for (int hb = 0; hb < T::HB; ++hb) {
-      union { bf16x8 v[2]; bf16 b[16]; } u;
+  for (int hb = 0; hb < T::HB; ++hb) {
+    union { bf16x8 v[2]; bf16 b[16]; } u;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) u.b[r] = (bf16)(o[hb][r] * inv);
-      bf16* dst = s.o + ((int64_t)qrow * H + h) * HD + hb * 32 + g * 16;
-      reinterpret_cast<bf16x8*>(dst)[0] = u.v[0];
-      reinterpret_cast<bf16x8*>(dst)[1] = u.v[1];
-    }
-  } else {
-    const int64_t rowh = ((int64_t)split * s.n_q + qrow) * H + h;
-#pragma unroll
-    for (int hb = 0; hb < T::HB; ++hb) {
-      float* dst = s.opart + rowh * HD + hb * 32 + g * 16;
-#pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        f32x4 v = {o[hb][r4 * 4 + 0] * inv, o[hb][r4 * 4 + 1] * inv,
-                   o[hb][r4 * 4 + 2] * inv, o[hb][r4 * 4 + 3] * inv};
-        reinterpret_cast<f32x4*>(dst)[r4] = v;
-      }
-    }
-    if (g == 0) s.lse[rowh] = l_tot > 0.f ? m_run + __log2f(l_tot) : kNegInf;
+    for (int r = 0; r < 16; ++r) u.b[r] = (bf16)(o[hb][r] * inv);
+    bf16* dst = dst_row + hb * 32 + g * 16;
+    reinterpret_cast<bf16x8*>(dst)[0] = u.v[0];
+    reinterpret_cast<bf16x8*>(dst)[1] = u.v[1];
   }
+  if (s.nsplit > 1 && g == 0)
+    s.lse[((int64_t)split * s.n_q + qrow) * H + h] = l_tot > 0.f ? m_run + __log2f(l_tot) : kNegInf;
 }
 
-// Merge key-split partials: O = sum_s w_s o_s / sum_s w_s, w_s = 2^(lse_s - max).
+// Merge key-split partials: O = sum_s w_s o_s / sum_s w_s, w_s = 2^(lse_s - max)
+// (o_s: bf16 partials, each normalised by its own row sum).
 // One thread per (row, head, 8 features).
 template <int HD>
 __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
@@ -548,22 +540,40 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
   const int64_t rh = grp - s.item0;                 // row * H + head
   const int64_t stride = (int64_t)s.n_q * a.H;      // between splits
   const int e0 = (threadIdx.x % TPR) * 8;
+  const float* lse = s.lse + rh;
+  const bf16* part = s.opart + rh * HD + e0;
+  const int ns = s.nsplit;
   float mx = kNegInf;
-  for (int k = 0; k < s.nsplit; ++k) mx = fmaxf(mx, s.lse[k * stride + rh]);
+  for (int k = 0; k < ns; ++k) mx = fmaxf(mx, lse[k * stride]);
+  if (mx == kNegInf) mx = 0.f;             // no key at all: every weight is 0
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   float wsum = 0.f;
-  for (int k = 0; k < s.nsplit; ++k) {
-    const float w = __builtin_amdgcn_exp2f(s.lse[k * stride + rh] - mx);
-    wsum += w;
-    const f32x4* src = reinterpret_cast<const f32x4*>(s.opart + (k * stride + rh) * HD + e0);
-    const f32x4 x0 = src[0], x1 = src[1];
+  // Four splits per round, their loads issued together.
+  int k = 0;
+  for (; k + 4 <= ns; k += 4) {
+    float l[4];
+    bf16x8 x[4];
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      acc[t] += w * x0[t];
-      acc[4 + t] += w * x1[t];
+    for (int u = 0; u < 4; ++u) {
+      l[u] = lse[(k + u) * stride];
+      x[u] = *reinterpret_cast<const bf16x8*>(part + (k + u) * stride * HD);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const float w = __builtin_amdgcn_exp2f(l[u] - mx);
+      wsum += w;
+#pragma unroll
+      for (int t = 0; t < 8; ++t) acc[t] += w * (float)x[u][t];
     }
   }
-  const float inv = 1.0f / wsum;
+  for (; k < ns; ++k) {
+    const float w = __builtin_amdgcn_exp2f(lse[k * stride] - mx);
+    wsum += w;
+    const bf16x8 x = *reinterpret_cast<const bf16x8*>(part + k * stride * HD);
+#pragma unroll
+    for (int t = 0; t < 8; ++t) acc[t] += w * (float)x[t];
+  }
+  const float inv = wsum > 0.f ? 1.0f / wsum : 0.f;
   bf16x8 out;
 #pragma unroll
   for (int t = 0; t < 8; ++t) out[t] = (bf16)(acc[t] * inv);

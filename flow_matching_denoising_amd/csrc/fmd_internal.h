@@ -93,7 +93,7 @@ struct AttnSess {
   const bf16* ring_k; // [H][cap][hd]
   const bf16* ring_v; // [H][cap/16][hd][16]
   bf16* o;            // [n_q][H][hd]            (when nsplit == 1)
-  float* opart;       // [nsplit][n_q][H][hd]    (when nsplit > 1)
+  bf16* opart;        // [nsplit][n_q][H][hd]    (when nsplit > 1)
   float* lse;         // [nsplit][n_q][H]
   int64_t cap;
   int32_t n_q;
@@ -115,7 +115,7 @@ struct AttnArgs {
 };
 
 struct CombineSess {
-  const float* opart;
+  const bf16* opart;
   const float* lse;
   bf16* o;
   int32_t n_q;
