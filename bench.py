@@ -44,7 +44,29 @@ def _args():
     ap.add_argument("--workload", default="v02_unit")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--quiet", action="store_true")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
+                    help="only run a plain device-to-device copy of BYTES bytes (three "
+                         "launches), the known-size reference for HBM byte counters")
     return ap.parse_args()
+
+
+def copy_probe(nbytes):
+    """A plain copy kernel of known size: each launch reads and writes nbytes."""
+    import torch
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda:0").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    times = []
+    for _ in range(3):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        dst.copy_(src)
+        b.record()
+        torch.cuda.synchronize()
+        times.append(a.elapsed_time(b) * 1e-3)
+    t = min(times)
+    print(json.dumps({"copy_probe_bytes": nbytes, "launches": 3, "best_s": t,
+                      "read_plus_write_GBps": round(2 * nbytes / t / 1e9, 1)}), flush=True)
 
 
 def _log(args, *a):
@@ -100,6 +122,9 @@ def cpu_baseline(wl, ui, args):
 
 def main():
     args = _args()
+    if args.copy_probe:
+        copy_probe(args.copy_probe)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on exactly one GPU: the denoise step here is a single-GPU "
               "kernel path (multi-GPU sharding is design-only); use --gpus 1.", file=sys.stderr)
