@@ -89,6 +89,52 @@ def _attn_traffic():
         return None
 
 
+def append_batch_probe(launches=20):
+    """The batched ring append at the 8-session shape (rings of 8..128 units of
+    944 tokens, 40 heads x 128, per-session append offsets): one launch appends
+    all 8 slices (309 MB read + written).  Timed with HIP events recorded on the
+    launch stream; every launch appends at the same offsets.  The rings' contents
+    do not affect the append, so they are left uninitialised."""
+    import torch
+
+    import flow_matching_denoising_amd as fmd
+    import workload
+
+    wl = workload.get("v02_batch8")
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device=dev).manual_seed(5)
+    caches, ks, vs, states = [], [], [], []
+    for s in wl.sessions:
+        caches.append(fmd.KVCache(s.n_heads, s.head_dim, s.cap_tokens, device=dev,
+                                  len_tokens=s.len_before, head_tokens=s.head_before))
+        shape = (s.slice_tokens, s.n_heads, s.head_dim)
+        ks.append(torch.randn(shape, generator=g, device=dev).to(torch.bfloat16))
+        vs.append(torch.randn(shape, generator=g, device=dev).to(torch.bfloat16))
+        states.append((s.len_before, s.head_before))
+
+    def once():
+        for c, (ln, hd_) in zip(caches, states):
+            c.set_state(ln, hd_)
+        fmd.kv_append_batched(caches, ks, vs)
+
+    for _ in range(3):
+        once()
+    torch.cuda.synchronize()
+    fmd.profile_enable(True)
+    for _ in range(launches):
+        once()
+    torch.cuda.synchronize()
+    ms, n = fmd.profile_read("append")
+    fmd.profile_enable(False)
+    avg_s = ms / n / 1e3
+    nbytes = wl.append_bytes()
+    del caches, ks, vs
+    torch.cuda.empty_cache()
+    return {"workload": "v02_batch8", "bytes_per_launch": nbytes, "launches": n,
+            "avg_launch_us": round(avg_s * 1e6, 2), "GBps": round(nbytes / avg_s / 1e9, 1),
+            "frac_hbm": round(nbytes / avg_s / 1e9 / HBM_PEAK_GBS, 4)}
+
+
 def cpu_baseline(wl, ui, args):
     """The oracle, as it stands, on a bounded sample of one unit."""
     import numpy as np
@@ -238,6 +284,9 @@ def main():
         "proj_TFLOPs": round(proj_tflops, 1) if proj_tflops else None,
         "unit_layers_per_160ms": round(UNIT_BUDGET_S / (ms_per_step / 1e3 / n_sess), 2),
     }
+    del caches, ios
+    torch.cuda.empty_cache()
+    out["append_batch8"] = append_batch_probe()
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, ui, args)
     print(json.dumps(out), flush=True)

@@ -173,3 +173,51 @@ def test_v02_unit_full_size_sampled_rows():
                         n_audio=s.n_audio)
     o = host_f64(fmd.attention([unit]))[rows]
     assert_close(o, O, "v02_unit sampled O (last step)")
+
+
+def _sampled_unit_check(name, rows, sessions=None):
+    """Full-size unit (append + every step) in the benchmark's launch
+    configuration (all sessions in one call); the oracle computes sampled rows
+    of every head of the chosen sessions, step by step, for dz = z - eps."""
+    wl = workload.get(name)
+    ui = workload.make_inputs(wl, poison_invalid=True)
+    caches, ios, zs = [], [], []
+    for si in ui.sessions:
+        c = make_cache(fmd, si.shape, si.ring_k, si.ring_v)
+        z = torch.from_numpy(si.eps.copy()).to(DEV)
+        caches.append(c)
+        zs.append(z)
+        ios.append(_unit_io(ui, si, c, z))
+    fmd.denoise_unit(ios, dev_bf16(ui.w_o))
+    torch.cuda.synchronize()
+    W = oracle.bf16_bits_to_f64(ui.w_o)
+    for b, (si, c) in enumerate(zip(ui.sessions, caches)):
+        s = si.shape
+        assert (c.len_tokens, c.head_tokens) == (s.len_after, s.head_after), \
+            f"{name} session {b} ring state"
+    for b in (range(len(ui.sessions)) if sessions is None else sessions):
+        si, c, z = ui.sessions[b], caches[b], zs[b]
+        s = si.shape
+        rk, rv, ln, hd_ = oracle.kv_append(si.ring_k, si.ring_v, s.len_before, s.head_before,
+                                           si.slice_k, si.slice_v)[:4]
+        assert (c.len_tokens, c.head_tokens) == (ln, hd_), f"{name} session {b} ring state"
+        dz_ref = np.zeros((len(rows), s.d))
+        for st in range(s.n_steps):
+            O = oracle.attention(si.q[st], rk, rv, ln, hd_, si.k_u[st], si.v_u[st], rows=rows)
+            dz_ref -= s.h[st] * (O.reshape(len(rows), -1) @ W.T)
+        print(f"{name} session {b}: {s.len_after} cached keys, oracle done", flush=True)
+        dz = host_f64(z)[rows] - si.eps[rows]
+        assert_close(dz, dz_ref, f"{name} session {b} sampled dz")
+
+
+def test_v02_long_wrapped_ring_sampled_rows():
+    # 256-unit ring (241,664 keys) that has wrapped, appended at a non-zero
+    # offset: the valid keys are two ring segments.
+    _sampled_unit_check("v02_long", [0, 255, 511, 767, 800, 919, 920, 927])
+
+
+def test_v02_batch8_ragged_sessions_sampled_rows():
+    # 8 sessions with ragged ring lengths (8..128 units) and per-session
+    # append offsets, one batched call as the benchmark would time it; the
+    # oracle checks the shortest ring, a long one and the longest (wrapped).
+    _sampled_unit_check("v02_batch8", [0, 300, 767, 919, 927], sessions=[1, 3, 5])
