@@ -188,10 +188,17 @@ __device__ __forceinline__ void zero_invalid_v(char* vbuf, const Window& win) {
   }
 }
 
+// s_waitcnt immediate (gfx9 encoding): vmcnt in bits 3:0 and 15:14,
+// expcnt (left at its maximum, 7) in bits 6:4, lgkmcnt in bits 11:8.
+constexpr int vmcnt_imm(int vm, int lgkm) {
+  return (vm & 15) | ((vm >> 4) << 14) | (7 << 4) | (lgkm << 8);
+}
+
 // Wait until at most N of this wave's loads are outstanding, then barrier.
 template <int N>
 __device__ __forceinline__ void wait_loads_and_sync() {
-  __builtin_amdgcn_s_waitcnt(0x0F70 | N);   // vmcnt(N); expcnt/lgkmcnt unconstrained
+  static_assert(N >= 0 && N < 64, "vmcnt is six bits");
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(N, 15));   // vmcnt(N); lgkmcnt unconstrained
   __asm__ volatile("" ::: "memory");
   __syncthreads();
   __asm__ volatile("" ::: "memory");

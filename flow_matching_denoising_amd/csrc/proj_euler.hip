@@ -70,9 +70,16 @@ __device__ __forceinline__ void dma16(const i32x4& rs, int voff, int soff, char*
                    : "memory", "m0");
 }
 
+// s_waitcnt immediate (gfx9 encoding): vmcnt in bits 3:0 and 15:14,
+// expcnt (left at its maximum, 7) in bits 6:4, lgkmcnt in bits 11:8.
+constexpr int vmcnt_imm(int vm, int lgkm) {
+  return (vm & 15) | ((vm >> 4) << 14) | (7 << 4) | (lgkm << 8);
+}
+
 template <int N>
 __device__ __forceinline__ void wait_loads_and_sync() {
-  __builtin_amdgcn_s_waitcnt(0x0F70 | N);   // vmcnt(N); expcnt/lgkmcnt unconstrained
+  static_assert(N >= 0 && N < 64, "vmcnt is six bits");
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(N, 15));   // vmcnt(N); lgkmcnt unconstrained
   __asm__ volatile("" ::: "memory");
   __syncthreads();
   __asm__ volatile("" ::: "memory");
@@ -136,28 +143,69 @@ __global__ __launch_bounds__(WAVES * 64) void proj_kernel(ProjArgs a) {
 #pragma unroll
   for (int i = 0; i < MT; ++i) acc[i] = f32x16{};
   const int nk = d / BK;
+  // Pipeline: three LDS stages, k step t in buffer t % 3.  The barrier that
+  // publishes k step t+1 sits DA slots before the end of k step t, right
+  // after every wave has issued its last read of buffer t: the reads of
+  // k step t+1's first operands then overlap the last MFMAs of k step t, and
+  // the DMA of k step t+3 (into buffer t % 3) is issued after that barrier.
+  // MFMA slot sl = kc*MT + i multiplies A fragment (kc, i) by B fragment kc;
+  // every slot issues the read of the A fragment DA slots ahead (and the B
+  // fragment of a k chunk that starts there), continuing into the next k step.
+  constexpr int NS = 4 * MT;            // slots per k step
+  constexpr int DA = 3, RA = 4;         // A read distance and ring size
+  static_assert(NS % RA == 0 && NS / MT % 2 == 0 && DA < MT, "operand rings");
+  auto aread = [&](const char* al, int sl) {
+    return *reinterpret_cast<const bf16x8*>(al + (sl % MT) * 4096 + roff[sl / MT]);
+  };
+  auto bread = [&](const char* al, int kc) {
+    return *reinterpret_cast<const bf16x8*>(al + A_BLOCKS * 1024 + wave * 4096 + roff[kc]);
+  };
   load_stage(0, 0);
   if (nk > 1) load_stage(1, 1);
+  if (nk > 2) load_stage(2, 2);
+  if (nk > 2)
+    wait_loads_and_sync<2 * LOADS_PER_WAVE>();
+  else if (nk > 1)
+    wait_loads_and_sync<LOADS_PER_WAVE>();
+  else
+    wait_loads_and_sync<0>();
+  bf16x8 ar[RA], br[2];
+  br[0] = bread(lds, 0);
+#pragma unroll
+  for (int sl = 0; sl < DA; ++sl) ar[sl % RA] = aread(lds, sl);
   int st = 0;
   for (int kt = 0; kt < nk; ++kt) {
-    if (kt + 1 < nk)
-      wait_loads_and_sync<LOADS_PER_WAVE>();    // k step kt landed; kt+1 may be in flight
-    else
-      wait_loads_and_sync<0>();
-    const int st2 = st == 0 ? 2 : st - 1;       // (kt+2) % 3: the buffer of k step kt-1
-    if (kt + 2 < nk) load_stage(kt + 2, st2);
+    const int stn = st == 2 ? 0 : st + 1;       // buffer of k step kt+1
     const char* al = lds + st * STAGE_BYTES;
-    const char* bl = al + A_BLOCKS * 1024 + wave * 4096;
+    const char* aln = lds + stn * STAGE_BYTES;
+    const bool more = kt + 1 < nk;
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int kc = 0; kc < 4; ++kc) {
-      const bf16x8 bv = *reinterpret_cast<const bf16x8*>(bl + roff[kc]);
-      bf16x8 av[MT];
-#pragma unroll
-      for (int i = 0; i < MT; ++i) av[i] = *reinterpret_cast<const bf16x8*>(al + i * 4096 + roff[kc]);
-#pragma unroll
-      for (int i = 0; i < MT; ++i) acc[i] = mfma32x32x16(av[i], bv, acc[i]);
+    for (int sl = 0; sl < NS; ++sl) {
+      if (sl == NS - DA && more) {
+        // This wave's reads of buffer st are all issued; wait for them and
+        // for k step kt+1's DMA, then barrier.
+        if (kt + 2 < nk)
+          __builtin_amdgcn_s_waitcnt(vmcnt_imm(LOADS_PER_WAVE, 0));
+        else
+          __builtin_amdgcn_s_waitcnt(vmcnt_imm(0, 0));
+        __asm__ volatile("" ::: "memory");
+        __syncthreads();
+        __asm__ volatile("" ::: "memory");
+        if (kt + 3 < nk) load_stage(kt + 3, st);
+      }
+      const int nx = sl + DA;
+      if (nx < NS) {
+        ar[nx % RA] = aread(al, nx);
+        if (nx % MT == 0) br[(nx / MT) & 1] = bread(al, nx / MT);
+      } else if (more) {
+        ar[nx % RA] = aread(aln, nx - NS);
+        if ((nx - NS) % MT == 0) br[((nx - NS) / MT) & 1] = bread(aln, (nx - NS) / MT);
+      }
+      acc[sl % MT] = mfma32x32x16(ar[sl % RA], br[(sl / MT) & 1], acc[sl % MT]);
+      __builtin_amdgcn_sched_barrier(0);
     }
-    st = st == 2 ? 0 : st + 1;
+    st = stn;
   }
 
   // Epilogue: z[m][n] -= h * v[m][n].  C layout: lane (col r, group g),
