@@ -22,6 +22,9 @@ sections):
    path has a constant velocity, integrated by an ODE solver over a few steps
    [same page, 3.4; Fig. 2: the performer receives the slice, then only runs
    the flow-matching solver].
+5. ``qkv.qkv_projection`` / ``qkv.denoise_unit_qkv`` -- the same solver with
+   the unit's Q, K, V projected from the current latent at every step
+   [same page, 3.4: f_theta is evaluated on the noisy latents it integrates].
 
 Everything is float64 unless a function says otherwise.  bf16 inputs arrive as
 uint16 bit patterns and are widened exactly by ``ring.bf16_bits_to_f64``.
@@ -35,3 +38,4 @@ parity unpinned for that composition as a whole.
 from .ring import bf16_bits_to_f64, kv_append, valid_slots  # noqa: F401
 from .attention import attention, attention_naive  # noqa: F401
 from .flow import velocity, euler_step, denoise_step, denoise_unit  # noqa: F401
+from .qkv import round_to_bf16, f64_to_bf16_bits, qkv_projection, denoise_unit_qkv  # noqa: F401

@@ -146,3 +146,67 @@ def check_values_one(attention_fn, seed=2, H=2, hd=16, cap=40, n_q=7):
     vu = np.full((n_q, H, hd), one, dtype=np.uint16)
     o = attention_fn(q, rk, rv, 33, 5, ku, vu)
     return float(np.max(np.abs(o - 1.0)))
+
+
+# ---------------------------------------------------------------------------
+# Per-step Q/K/V projected from z.
+# ---------------------------------------------------------------------------
+def brute_qkv(z, w_bits, n_heads):
+    """Scalar-loop [Q | K_u | V_u] = bf16(bf16(z) W^T), bf16 rounding by torch."""
+    def rb(x):
+        return torch.tensor(float(x), dtype=torch.float64).to(torch.float32).to(
+            torch.bfloat16).to(torch.float64).item()
+    z = np.asarray(z, dtype=np.float64)
+    n, d = z.shape
+    W = widen(w_bits)
+    zb = [[rb(z[i, k]) for k in range(d)] for i in range(n)]
+    out = np.zeros((3, n, d))
+    for t in range(3):
+        for i in range(n):
+            for c in range(d):
+                out[t, i, c] = rb(sum(zb[i][k] * W[t * d + c, k] for k in range(d)))
+    hd = d // n_heads
+    return [out[t].reshape(n, n_heads, hd) for t in range(3)]
+
+
+def check_qkv_uniform_closed_form(unit_qkv_fn, hs=(0.5, 0.25, 0.125), seed=3, H=2, hd=8,
+                                  cap=32, length=24, head=5, n_q=6):
+    """W_q = 0 and W_v = 0: every query scores 0 on every key, so O is the plain
+    mean of all seen values, the unit's own values being 0: O = (sum of the
+    valid ring values) / (length + n_q), the same at every step whatever z is.
+    Then z_final = eps - (sum h) * O_flat W_o^T.  Returns max |error|."""
+    rng = np.random.default_rng(seed)
+    d = H * hd
+    ring_k = random_bits(rng, (H, cap, hd))
+    ring_v = random_bits(rng, (H, cap, hd))
+    w = np.zeros((3 * d, d), dtype=np.uint16)
+    w[d:2 * d] = random_bits(rng, (d, d))          # W_k nonzero: must not matter
+    w_o = random_bits(rng, (d, d), scale=d ** -0.5)
+    eps = rng.standard_normal((n_q, d))
+    slots = [(head - length + i) % cap for i in range(length)]
+    mean_v = widen(ring_v)[:, slots, :].sum(axis=1) / (length + n_q)   # [H][hd]
+    v = np.tile(mean_v.reshape(1, d), (n_q, 1)) @ widen(w_o).T
+    expect = eps - sum(hs) * v
+    got = unit_qkv_fn(ring_k, ring_v, length, head, None, None, eps, list(hs), w, w_o, H)["z"]
+    return float(np.max(np.abs(got - expect)))
+
+
+def check_qkv_mean_decay(unit_qkv_fn, hs=(0.5, 0.5), seed=4, H=2, hd=8, n_q=16):
+    """Empty cache, W_q = W_k = 0, W_v = I, W_o = I: every query attends
+    uniformly to the unit's own values V_u = bf16(z), so the velocity of every
+    row is the column mean of bf16(z) and each step maps z_i -> z_i - h mean(z).
+    The deviations from the mean are invariant and the mean decays by (1 - h)
+    per step: after the steps it is prod(1 - h) * mean(eps) (rounding of z to
+    bf16 perturbs this by ~2^-9 of |z|).  A solver that kept projecting from
+    eps would decay it by (1 - sum h) instead.  Returns max |error|."""
+    rng = np.random.default_rng(seed)
+    d = H * hd
+    eps = rng.standard_normal((n_q, d)) + 0.5
+    w = np.zeros((3 * d, d), dtype=np.uint16)
+    w[2 * d:] = bits(np.eye(d))
+    w_o = bits(np.eye(d))
+    ring = np.zeros((H, 16, hd), dtype=np.uint16)
+    mean0 = eps.mean(axis=0, keepdims=True)
+    expect = (eps - mean0) + np.prod([1.0 - h for h in hs]) * mean0
+    got = unit_qkv_fn(ring, ring, 0, 0, None, None, eps, list(hs), w, w_o, H)["z"]
+    return float(np.max(np.abs(got - expect)))

@@ -70,3 +70,44 @@ def test_untransposed_projection_is_caught():
     w = random_bits(rng, (6, 6))
     wrong = o @ oracle.bf16_bits_to_f64(w)           # mistake: O @ W instead of O @ W^T
     assert np.max(np.abs(wrong - brute_velocity(o, w))) > 1e-3
+
+
+qkv_mod = importlib.import_module("oracle.qkv")
+
+
+def test_projection_from_eps_is_caught(monkeypatch):
+    # mistake: every step projects Q, K, V from the starting latent eps
+    from tests.pins import check_qkv_mean_decay
+    orig = qkv_mod.qkv_projection
+    first = {}
+
+    def from_first(z, w, n_heads):
+        key = id(w)
+        first.setdefault(key, np.array(z, dtype=np.float64))
+        return orig(first[key], w, n_heads)
+    monkeypatch.setattr(qkv_mod, "qkv_projection", from_first)
+    assert check_qkv_mean_decay(oracle.denoise_unit_qkv) > 5e-2
+
+
+def test_swapped_query_and_key_thirds_is_caught(monkeypatch):
+    # mistake: the first third of W_qkv taken as the keys, the second as queries
+    from tests.pins import check_qkv_uniform_closed_form
+    orig = qkv_mod.qkv_projection
+
+    def swapped(z, w, n_heads):
+        q, k, v = orig(z, w, n_heads)
+        return k, q, v
+    monkeypatch.setattr(qkv_mod, "qkv_projection", swapped)
+    assert check_qkv_uniform_closed_form(oracle.denoise_unit_qkv) > 1e-3
+
+
+def test_unrounded_latent_in_projection_is_caught(monkeypatch):
+    # mistake: z fed to the projection in full precision (no bf16 rounding)
+    from tests.pins import brute_qkv
+    monkeypatch.setattr(qkv_mod, "round_to_bf16", lambda x: np.asarray(x, dtype=np.float64))
+    rng = np.random.default_rng(1)
+    z = rng.standard_normal((4, 6))
+    w = random_bits(rng, (18, 6))
+    got = qkv_mod.qkv_projection(z, w, 2)
+    want = brute_qkv(z, w, 2)
+    assert max(np.max(np.abs(oracle.bf16_bits_to_f64(g) - w_)) for g, w_ in zip(got, want)) > 0

@@ -34,7 +34,7 @@ BF16_NAN = np.uint16(0x7FC0)
 # Stable ids so the stream of a tensor never depends on the draw order.
 _TENSOR_IDS = {
     "ring_k": 1, "ring_v": 2, "slice_k": 3, "slice_v": 4,
-    "q": 5, "k_u": 6, "v_u": 7, "eps": 8, "z0": 9, "w_o": 10,
+    "q": 5, "k_u": 6, "v_u": 7, "eps": 8, "z0": 9, "w_o": 10, "w_qkv": 11,
 }
 
 
@@ -260,6 +260,17 @@ def projection_weight(seed, d: int, head_dim: int):
     def one(b):
         return round_to_bf16_bits(
             _normal_f32(seed, 0, "w_o", b, (head_dim, d), scale=d ** -0.5))
+    return np.ascontiguousarray(np.concatenate(_per_head(one, n_blocks), axis=0))
+
+
+def qkv_weight(seed, d: int, head_dim: int):
+    """bf16 [3d][d] ([d_out][d_in]), N(0, 1/d): the map from the latent to the
+    unit's Q, K_u, V_u; drawn per block of head_dim output rows."""
+    n_blocks = 3 * d // head_dim
+
+    def one(b):
+        return round_to_bf16_bits(
+            _normal_f32(seed, 0, "w_qkv", b, (head_dim, d), scale=d ** -0.5))
     return np.ascontiguousarray(np.concatenate(_per_head(one, n_blocks), axis=0))
 
 
