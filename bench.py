@@ -13,7 +13,10 @@ Prints ONE JSON line (rank 0, N=1).  Besides throughput it reports:
   launch stream during the timed region, against the bf16 dense MFMA peak;
 * cpu_baseline: the CPU oracle timed on a bounded sample of the same workload
   (one full solver step: attention of every head, the projection and the Euler
-  update), scaled to the unit's solver steps.
+  update), scaled to the unit's solver steps;
+* qkv_unit: the same unit with the z-dependent solver (Q, K_u, V_u projected
+  from the latent at every step);
+* append_batch8: the batched ring append at the 8-session shape.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 """
@@ -87,6 +90,52 @@ def _attn_traffic():
         return float(t["hbm_bytes_per_launch"])
     except (OSError, ValueError, KeyError):
         return None
+
+
+def qkv_unit_probe(wl, ui, caches, states, w_o, units=10, warmup=2):
+    """The z-dependent solver on the same workload: every step first projects
+    the unit's Q, K_u, V_u from the current latent (bf16 [3d][d] weights, one
+    GEMM of n_q x 3d x d), then runs the step.  Same rings, same append."""
+    import numpy as np
+    import torch
+
+    import flow_matching_denoising_amd as fmd
+    import workload
+
+    dev = torch.device("cuda:0")
+    w_qkv = torch.from_numpy(workload.qkv_weight(wl.seed, wl.d, wl.head_dim).view(np.int16)).view(
+        torch.bfloat16).to(dev)
+    ios = []
+    for si, c in zip(ui.sessions, caches):
+        s = si.shape
+        z = torch.from_numpy(si.eps.copy()).to(dev)
+        sk = torch.from_numpy(si.slice_k.view(np.int16)).view(torch.bfloat16).to(dev)
+        sv = torch.from_numpy(si.slice_v.view(np.int16)).view(torch.bfloat16).to(dev)
+        ios.append(fmd.UnitQkvIO(c, sk, sv, z, list(s.h), n_audio=s.n_audio))
+    ws = fmd.alloc_workspace(fmd.unit_qkv_workspace_bytes(ios), dev)
+
+    def one():
+        for c, (ln, hd_) in zip(caches, states):
+            c.set_state(ln, hd_)
+        fmd.denoise_unit_qkv(ios, w_qkv, w_o, ws)
+
+    for _ in range(warmup):
+        one()
+    torch.cuda.synchronize()
+    fmd.profile_enable(True)
+    t0 = time.perf_counter()
+    for _ in range(units):
+        one()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms, n = fmd.profile_read("qkv")
+    fmd.profile_enable(False)
+    s0 = wl.sessions[0]
+    qkv_flops = 2.0 * sum(s.n_q for s in wl.sessions) * 3 * s0.d * s0.d
+    return {"workload": wl.name, "units_per_s": round(len(ui.sessions) * units / wall, 3),
+            "ms_per_unit": round(wall / units * 1e3, 4),
+            "qkv_gemm_us": round(ms / n * 1e3, 2),
+            "qkv_gemm_TFLOPs": round(qkv_flops / (ms / n / 1e3) / 1e12, 1)}
 
 
 def append_batch_probe(launches=20):
@@ -284,6 +333,7 @@ def main():
         "proj_TFLOPs": round(proj_tflops, 1) if proj_tflops else None,
         "unit_layers_per_160ms": round(UNIT_BUDGET_S / (ms_per_step / 1e3 / n_sess), 2),
     }
+    out["qkv_unit"] = qkv_unit_probe(wl, ui, caches, states, w_o)
     del caches, ios
     torch.cuda.empty_cache()
     out["append_batch8"] = append_batch_probe()

@@ -6,8 +6,8 @@ for device memory and streams.  There is no fallback: if the library is not
 built, importing this package raises ``ImportError``.
 
 Names follow the C ABI: ``kv_append``, ``kv_append_batched``, ``attention``,
-``denoise_step``, ``denoise_unit``, ``workspace_bytes``,
-``unit_workspace_bytes``.
+``denoise_step``, ``denoise_unit``, ``denoise_unit_qkv``, ``workspace_bytes``,
+``unit_workspace_bytes``, ``unit_qkv_workspace_bytes``.
 """
 from __future__ import annotations
 
@@ -30,7 +30,7 @@ FMD_MAX_SESSIONS = 64
 FMD_CACHE_BLOCK = 16
 STATUS = {0: "FMD_OK", -1: "FMD_E_INVAL", -2: "FMD_E_SHAPE", -3: "FMD_E_CAPACITY",
           -4: "FMD_E_ALIGN", -5: "FMD_E_WORKSPACE", -6: "FMD_E_HIP"}
-KERNEL_CLASSES = {"append": 0, "vt": 1, "attn": 2, "combine": 3, "proj": 4}
+KERNEL_CLASSES = {"append": 0, "vt": 1, "attn": 2, "combine": 3, "proj": 4, "qkv": 5, "cvt": 6}
 
 
 class FmdError(RuntimeError):
@@ -62,6 +62,13 @@ class _UnitIO(ctypes.Structure):
                 ("h", ctypes.POINTER(ctypes.c_float))]
 
 
+class _UnitQkvIO(ctypes.Structure):
+    _fields_ = [("cache", ctypes.POINTER(_Cache)), ("k_slice", ctypes.c_void_p),
+                ("v_slice", ctypes.c_void_p), ("slice_tokens", ctypes.c_int64),
+                ("z", ctypes.c_void_p), ("n_video", ctypes.c_int32), ("n_audio", ctypes.c_int32),
+                ("h", ctypes.POINTER(ctypes.c_float))]
+
+
 def _sig(name, restype, *argtypes):
     f = getattr(_lib, name)
     f.restype = restype
@@ -84,6 +91,10 @@ _unit_workspace_bytes = _sig("fmd_unit_workspace_bytes", ctypes.c_int, ctypes.PO
                              _i32, ctypes.POINTER(_sz))
 _denoise_unit = _sig("fmd_denoise_unit", ctypes.c_int, ctypes.POINTER(_UnitIO), _i32, _i32, _vp,
                      _vp, _sz, _vp)
+_unit_qkv_workspace_bytes = _sig("fmd_unit_qkv_workspace_bytes", ctypes.c_int,
+                                 ctypes.POINTER(_UnitQkvIO), _i32, ctypes.POINTER(_sz))
+_denoise_unit_qkv = _sig("fmd_denoise_unit_qkv", ctypes.c_int, ctypes.POINTER(_UnitQkvIO), _i32,
+                         _i32, _vp, _vp, _vp, _sz, _vp)
 _strerror = _sig("fmd_strerror", ctypes.c_char_p, ctypes.c_int)
 _last_error = _sig("fmd_last_error", ctypes.c_char_p)
 _profile_enable = _sig("fmd_profile_enable", ctypes.c_int, ctypes.c_int)
@@ -92,7 +103,8 @@ _profile_read = _sig("fmd_profile_read", ctypes.c_int, ctypes.c_int,
 _version = _sig("fmd_version", ctypes.c_char_p)
 
 EXPORTED = ["fmd_kv_append", "fmd_kv_append_batched", "fmd_workspace_bytes", "fmd_denoise_step",
-            "fmd_attention", "fmd_unit_workspace_bytes", "fmd_denoise_unit", "fmd_strerror",
+            "fmd_attention", "fmd_unit_workspace_bytes", "fmd_denoise_unit",
+            "fmd_unit_qkv_workspace_bytes", "fmd_denoise_unit_qkv", "fmd_strerror",
             "fmd_last_error", "fmd_profile_enable", "fmd_profile_read", "fmd_version"]
 
 
@@ -304,6 +316,54 @@ def denoise_unit(sessions, w_o, workspace=None, stream=None):
                          workspace.numel(), _stream_ptr(stream)))
     # The library advanced each cache's (len, head) in the struct array it was
     # given; the array holds pointers to the caches' own structs, so nothing to copy.
+
+
+class UnitQkvIO:
+    """One session's inputs for a unit of the z-dependent solver (see
+    ``fmd_unit_qkv_io``): Q, K_u, V_u are projected from z by the library at
+    every step.  z: float32 [n_q][d], eps in, final latent out; h: step sizes."""
+
+    def __init__(self, cache: KVCache, k_slice, v_slice, z, h, n_audio=0):
+        self.cache, self.k_slice, self.v_slice, self.z = cache, k_slice, v_slice, z
+        self.h = (ctypes.c_float * len(h))(*[float(x) for x in h])
+        self.n_steps = len(h)
+        self.n_q = z.shape[0]
+        self.n_audio = n_audio
+
+    def _struct(self):
+        T = 0 if self.k_slice is None else self.k_slice.shape[0]
+        return _UnitQkvIO(ctypes.pointer(self.cache._c),
+                          _ptr(self.k_slice, torch.bfloat16, "k_slice", allow_none=True),
+                          _ptr(self.v_slice, torch.bfloat16, "v_slice", allow_none=True), T,
+                          _ptr(self.z, torch.float32, "z"), self.n_q - self.n_audio, self.n_audio,
+                          ctypes.cast(self.h, ctypes.POINTER(ctypes.c_float)))
+
+
+def _qkv_array(sessions):
+    n = len(sessions)
+    return (_UnitQkvIO * n)(*[s._struct() for s in sessions]), n
+
+
+def unit_qkv_workspace_bytes(sessions) -> int:
+    arr, n = _qkv_array(sessions)
+    out = _sz(0)
+    _check(_unit_qkv_workspace_bytes(arr, n, ctypes.byref(out)))
+    return out.value
+
+
+def denoise_unit_qkv(sessions, w_qkv, w_o, workspace=None, stream=None):
+    """Append every session's slice, then run the S solver steps, each
+    projecting the unit's Q, K_u, V_u from the current latent (W_qkv bf16
+    [3d][d])."""
+    n_steps = sessions[0].n_steps
+    if any(s.n_steps != n_steps for s in sessions):
+        raise ValueError("all sessions must have the same number of steps")
+    if workspace is None:
+        workspace = alloc_workspace(unit_qkv_workspace_bytes(sessions), sessions[0].z.device)
+    arr, n = _qkv_array(sessions)
+    _check(_denoise_unit_qkv(arr, n, n_steps, _ptr(w_qkv, torch.bfloat16, "w_qkv"),
+                             _ptr(w_o, torch.bfloat16, "w_o"), workspace.data_ptr(),
+                             workspace.numel(), _stream_ptr(stream)))
 
 
 def profile_enable(on: bool = True):

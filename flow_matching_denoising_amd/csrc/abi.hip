@@ -311,8 +311,11 @@ int check_workspace(void* ws, size_t have, size_t need) {
 
 // Enqueue the step kernels (validation already done).  o_out != nullptr:
 // attention only, O to the caller's buffer.
+// zb_out (optional, per session): where the projection epilogue also writes
+// bf16(z) after the update (the next step's input to the Q/K/V projection).
 int enqueue_steps(const fmd_unit_step* units, int n, const std::vector<SessPlan>& plans,
-                  const void* w_o, char* ws, bf16* o_out, hipStream_t st) {
+                  const void* w_o, char* ws, bf16* o_out, hipStream_t st,
+                  bf16* const* zb_out = nullptr) {
   const int H = units[0].cache->n_heads, hd = units[0].cache->head_dim;
   const int d = H * hd;
   const float scale_log2 = (float)(1.4426950408889634 / sqrt((double)hd));
@@ -327,6 +330,7 @@ int enqueue_steps(const fmd_unit_step* units, int n, const std::vector<SessPlan>
     va.H = aa.H = ca.H = H;
     aa.scale_log2 = scale_log2;
     pa.d = d;
+    pa.n_out = d;
     pa.w = static_cast<const bf16*>(w_o);
     bool any_split = false;
     for (int k = 0; k < cn; ++k) {
@@ -373,7 +377,8 @@ int enqueue_steps(const fmd_unit_step* units, int n, const std::vector<SessPlan>
 
       const int mtiles = (p.n_q + kProjTile - 1) / kProjTile;
       const int ntiles = (d + kProjTileN - 1) / kProjTileN;
-      pa.s[k] = ProjSess{o, u.z, p.n_q, mtiles, pa.items, u.h};
+      pa.s[k] = ProjSess{o, u.z, zb_out ? zb_out[c0 + k] : nullptr, {nullptr, nullptr, nullptr},
+                         p.n_q, mtiles, pa.items, u.h};
       pa.items += mtiles * ntiles;
     }
     // Sessions without splits take no combine items; the combine kernel finds
@@ -386,7 +391,7 @@ int enqueue_steps(const fmd_unit_step* units, int n, const std::vector<SessPlan>
         (rc = timed_launch(FMD_KERNEL_COMBINE, st, [&] { return launch_combine(ca, hd, st); })))
       return rc;
     if (!o_out &&
-        (rc = timed_launch(FMD_KERNEL_PROJ, st, [&] { return launch_proj(pa, st); })))
+        (rc = timed_launch(FMD_KERNEL_PROJ, st, [&] { return launch_proj(pa, kProjEuler, st); })))
       return rc;
   }
   return FMD_OK;
@@ -628,6 +633,178 @@ int fmd_denoise_unit(fmd_unit_io* sessions, int32_t n_sessions, int32_t n_steps,
     }
     if ((rc = enqueue_steps(steps.data(), n_sessions, plans, w_o, static_cast<char*>(workspace),
                             nullptr, st)))
+      return rc;
+  }
+  return FMD_OK;
+}
+
+// ---------------------------------------------------------------------------
+// The z-dependent solver: Q, K_u, V_u projected from the latent every step.
+// ---------------------------------------------------------------------------
+static int validate_unit_qkv(const fmd_unit_qkv_io* ss, int n, int n_steps) {
+  if (!ss) return fail(FMD_E_INVAL, "sessions is NULL");
+  if (n < 1 || n > FMD_MAX_SESSIONS)
+    return fail(FMD_E_INVAL, "n_sessions=%d (must be 1..%d)", n, FMD_MAX_SESSIONS);
+  if (n_steps < 1) return fail(FMD_E_INVAL, "n_steps=%d (must be >= 1)", n_steps);
+  int rc;
+  for (int i = 0; i < n; ++i) {
+    const fmd_unit_qkv_io& s = ss[i];
+    if ((rc = check_cache(s.cache, i))) return rc;
+    if (i && (rc = check_same_shape(ss[0].cache, s.cache, i))) return rc;
+    for (int j = 0; j < i; ++j)
+      if (ss[j].cache == s.cache) return fail(FMD_E_INVAL, "session %d: same cache as %d", i, j);
+    if (s.slice_tokens < 0)
+      return fail(FMD_E_INVAL, "session %d: slice_tokens %lld", i, (long long)s.slice_tokens);
+    if (s.slice_tokens > 0 &&
+        (rc = check_append(s.cache, s.k_slice, s.v_slice, s.slice_tokens, i)))
+      return rc;
+    if ((rc = check_tensor(s.z, i, "z"))) return rc;
+    if (s.n_video < 0 || s.n_audio < 0 || (int64_t)s.n_video + s.n_audio < 1 ||
+        (int64_t)s.n_video + s.n_audio > (1 << 22))
+      return fail(FMD_E_INVAL, "session %d: n_video=%d n_audio=%d (need 1 <= n_q <= 2^22)", i,
+                  s.n_video, s.n_audio);
+    if (!s.h) return fail(FMD_E_INVAL, "session %d: h is NULL", i);
+    for (int k = 0; k < n_steps; ++k)
+      if (!(s.h[k] > 0.f && isfinite(s.h[k])))
+        return fail(FMD_E_INVAL, "session %d: h[%d]=%g must be finite and > 0", i, k, s.h[k]);
+  }
+  return FMD_OK;
+}
+
+// Workspace: per session bf16(z), Q, K_u, V_u ([n_q][d] each), then the
+// step workspace of fmd_denoise_step for the post-append rings.
+struct QkvLayout {
+  std::vector<fmd_kv_cache> after;
+  std::vector<fmd_unit_step> steps;
+  std::vector<SessPlan> plans;
+  std::vector<size_t> off;       // per session: zb, then q, k, v at +1..3 * slab
+  size_t slab_total = 0, bytes = 0;
+};
+
+static void layout_unit_qkv(const fmd_unit_qkv_io* ss, int n, QkvLayout& L) {
+  const int d = ss[0].cache->n_heads * ss[0].cache->head_dim;
+  L.after.resize(n);
+  L.steps.resize(n);
+  L.off.resize(n);
+  size_t off = 0;
+  for (int i = 0; i < n; ++i) {
+    const int n_q = ss[i].n_video + ss[i].n_audio;
+    L.off[i] = off;
+    off += 4 * align256((size_t)n_q * d * 2);
+    L.after[i] = *ss[i].cache;
+    if (ss[i].slice_tokens > 0) {
+      L.after[i].head_tokens = (L.after[i].head_tokens + ss[i].slice_tokens) % L.after[i].cap_tokens;
+      L.after[i].len_tokens =
+          std::min(L.after[i].len_tokens + ss[i].slice_tokens, L.after[i].cap_tokens);
+    }
+    // q/k_u/v_u are placeholders here (set per call); planning needs shapes only.
+    L.steps[i] = fmd_unit_step{&L.after[i], ss[i].z, ss[i].z, ss[i].z, ss[i].z, ss[i].n_video,
+                               ss[i].n_audio, ss[i].h[0]};
+  }
+  L.slab_total = off;
+  size_t step_bytes = 0;
+  plan_steps(L.steps.data(), n, false, L.plans, &step_bytes);
+  L.bytes = L.slab_total + step_bytes;
+}
+
+int fmd_unit_qkv_workspace_bytes(const fmd_unit_qkv_io* sessions, int32_t n_sessions,
+                                 size_t* out_bytes) {
+  g_last_error.clear();
+  if (!out_bytes) return fail(FMD_E_INVAL, "out_bytes is NULL");
+  int rc = validate_unit_qkv(sessions, n_sessions, 1);
+  if (rc) return rc;
+  QkvLayout L;
+  layout_unit_qkv(sessions, n_sessions, L);
+  *out_bytes = L.bytes;
+  return FMD_OK;
+}
+
+int fmd_denoise_unit_qkv(fmd_unit_qkv_io* sessions, int32_t n_sessions, int32_t n_steps,
+                         const void* w_qkv, const void* w_o, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  g_last_error.clear();
+  int rc = validate_unit_qkv(sessions, n_sessions, n_steps);
+  if (rc) return rc;
+  if ((rc = check_tensor(w_qkv, 0, "w_qkv"))) return rc;
+  if ((rc = check_tensor(w_o, 0, "w_o"))) return rc;
+  QkvLayout L;
+  layout_unit_qkv(sessions, n_sessions, L);
+  if ((rc = check_workspace(workspace, workspace_bytes, L.bytes))) return rc;
+
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  const int H = sessions[0].cache->n_heads, hd = sessions[0].cache->head_dim;
+  const int d = H * hd;
+  std::vector<bf16*> zb(n_sessions), q(n_sessions), k(n_sessions), v(n_sessions);
+  for (int i = 0; i < n_sessions; ++i) {
+    const int n_q = sessions[i].n_video + sessions[i].n_audio;
+    const size_t slab = align256((size_t)n_q * d * 2);
+    zb[i] = reinterpret_cast<bf16*>(ws + L.off[i]);
+    q[i] = reinterpret_cast<bf16*>(ws + L.off[i] + slab);
+    k[i] = reinterpret_cast<bf16*>(ws + L.off[i] + 2 * slab);
+    v[i] = reinterpret_cast<bf16*>(ws + L.off[i] + 3 * slab);
+  }
+
+  std::vector<fmd_kv_cache*> caches;
+  std::vector<const void*> ks, vs;
+  std::vector<int64_t> ts;
+  for (int i = 0; i < n_sessions; ++i) {
+    if (sessions[i].slice_tokens > 0) {
+      caches.push_back(sessions[i].cache);
+      ks.push_back(sessions[i].k_slice);
+      vs.push_back(sessions[i].v_slice);
+      ts.push_back(sessions[i].slice_tokens);
+    }
+  }
+  if (!caches.empty() &&
+      (rc = enqueue_appends(caches.data(), ks.data(), vs.data(), ts.data(), (int)caches.size(), st)))
+    return rc;
+
+  for (int c0 = 0; c0 < n_sessions; c0 += kMaxSessPerLaunch) {
+    const int cn = std::min(kMaxSessPerLaunch, n_sessions - c0);
+    CvtArgs ca = {};
+    ca.n_sess = cn;
+    for (int j = 0; j < cn; ++j) {
+      const int i = c0 + j;
+      const int64_t ne = (int64_t)(sessions[i].n_video + sessions[i].n_audio) * d;
+      ca.s[j] = CvtSess{sessions[i].z, zb[i], ne, ca.items};
+      ca.items += ne / 8;
+    }
+    if ((rc = timed_launch(FMD_KERNEL_CVT, st, [&] { return launch_cvt(ca, st); }))) return rc;
+  }
+
+  char* step_ws = ws + L.slab_total;
+  for (int s = 0; s < n_steps; ++s) {
+    for (int c0 = 0; c0 < n_sessions; c0 += kMaxSessPerLaunch) {
+      const int cn = std::min(kMaxSessPerLaunch, n_sessions - c0);
+      ProjArgs pa = {};
+      pa.n_sess = cn;
+      pa.d = d;
+      pa.n_out = 3 * d;
+      pa.w = static_cast<const bf16*>(w_qkv);
+      const int ntiles = (3 * d + kProjTileN - 1) / kProjTileN;
+      for (int j = 0; j < cn; ++j) {
+        const int i = c0 + j;
+        const int n_q = sessions[i].n_video + sessions[i].n_audio;
+        const int mtiles = (n_q + kProjTile - 1) / kProjTile;
+        pa.s[j] = ProjSess{zb[i], nullptr, nullptr, {q[i], k[i], v[i]}, n_q, mtiles, pa.items,
+                           0.f};
+        pa.items += mtiles * ntiles;
+      }
+      if ((rc = timed_launch(FMD_KERNEL_QKV, st, [&] { return launch_proj(pa, kProjQkv, st); })))
+        return rc;
+    }
+    for (int i = 0; i < n_sessions; ++i) {
+      L.steps[i].cache = sessions[i].cache;   // now in its post-append state
+      L.steps[i].q = q[i];
+      L.steps[i].k_u = k[i];
+      L.steps[i].v_u = v[i];
+      L.steps[i].z = sessions[i].z;
+      L.steps[i].h = sessions[i].h[s];
+    }
+    // The last step needs no bf16 copy of its result.
+    if ((rc = enqueue_steps(L.steps.data(), n_sessions, L.plans, w_o, step_ws, nullptr, st,
+                            s + 1 < n_steps ? zb.data() : nullptr)))
       return rc;
   }
   return FMD_OK;

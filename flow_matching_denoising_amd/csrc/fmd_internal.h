@@ -130,9 +130,20 @@ struct CombineArgs {
   int32_t items;
 };
 
+// Projection GEMM  Y = A * W^T  (A [n_q][d] bf16, W [n_out][d] bf16 =
+// [d_out][d_in], fp32 accumulation), with one of two epilogues:
+//   kProjEuler: n_out = d; z <- z - h * Y (fp32, in place), and, if zb is set,
+//               zb <- bf16(z) (the next step's projection input);
+//   kProjQkv:   n_out = 3d; column c of Y goes to out[c / d], column c % d,
+//               rounded to bf16 (the unit's Q, K_u, V_u).
+constexpr int kProjEuler = 0;
+constexpr int kProjQkv = 1;
+
 struct ProjSess {
-  const bf16* o;      // [n_q][d]
-  float* z;           // [n_q][d]
+  const bf16* a;      // [n_q][d]
+  float* z;           // kProjEuler: [n_q][d]
+  bf16* zb;           // kProjEuler: [n_q][d] or nullptr
+  bf16* out[3];       // kProjQkv: Q, K_u, V_u, each [n_q][d]
   int32_t n_q;
   int32_t n_mtiles;
   int32_t item0;
@@ -140,10 +151,24 @@ struct ProjSess {
 };
 struct ProjArgs {
   ProjSess s[kMaxSessPerLaunch];
-  const bf16* w;      // [d][d], [d_out][d_in]
+  const bf16* w;      // [n_out][d], [d_out][d_in]
   int32_t n_sess;
   int32_t d;
+  int32_t n_out;
   int32_t items;
+};
+
+// bf16 copy of the latent: zb = bf16(z), [n_q][d] per session.
+struct CvtSess {
+  const float* z;
+  bf16* zb;
+  int64_t n;          // elements (n_q * d), a multiple of 8
+  int64_t item0;      // first 8-element group of this session
+};
+struct CvtArgs {
+  CvtSess s[kMaxSessPerLaunch];
+  int32_t n_sess;
+  int64_t items;      // 8-element groups in total
 };
 
 // Host-side launchers (defined next to their kernels).
@@ -151,7 +176,8 @@ hipError_t launch_append(const AppendArgs& a, int head_dim, hipStream_t st);
 hipError_t launch_vt(const VtArgs& a, int head_dim, hipStream_t st);
 hipError_t launch_attn(const AttnArgs& a, int head_dim, hipStream_t st);
 hipError_t launch_combine(const CombineArgs& a, int head_dim, hipStream_t st);
-hipError_t launch_proj(const ProjArgs& a, hipStream_t st);
+hipError_t launch_proj(const ProjArgs& a, int mode, hipStream_t st);
+hipError_t launch_cvt(const CvtArgs& a, hipStream_t st);
 
 // Attention tiling shared by host planning and the kernel.
 constexpr int kAttnWaves = 8;

@@ -1,5 +1,6 @@
 // Velocity projection v = O * W^T on bf16 MFMA, with the rectified-flow Euler
-// update z <- z - h * v fused into the epilogue.
+// update z <- z - h * v fused into the epilogue; the same GEMM, with a bf16
+// store epilogue, projects the latent to the unit's Q, K_u and V_u.
 //
 // One network predicts the velocity of both modalities, and along the linear
 // interpolation path that velocity is constant, so an ODE solver integrates
@@ -87,6 +88,7 @@ __device__ __forceinline__ void wait_loads_and_sync() {
 
 }  // namespace
 
+template <int MODE>
 __global__ __launch_bounds__(WAVES * 64) void proj_kernel(ProjArgs a) {
   extern __shared__ __attribute__((aligned(1024))) char lds[];
   const int item = xcd_remap(blockIdx.x, a.items);
@@ -109,8 +111,9 @@ __global__ __launch_bounds__(WAVES * 64) void proj_kernel(ProjArgs a) {
   const int r = lane & 31, g = lane >> 5;
 
   // The tile's rows of O and W; rows past n_q (past d) read as zeros.
-  const i32x4 ra = make_rsrc(s.o + (int64_t)m0 * d, min(BM, n_q - m0) * d * 2);
-  const i32x4 rb = make_rsrc(a.w + (int64_t)n0 * d, min(BN, d - n0) * d * 2);
+  const int n_out = a.n_out;
+  const i32x4 ra = make_rsrc(s.a + (int64_t)m0 * d, min(BM, n_q - m0) * d * 2);
+  const i32x4 rb = make_rsrc(a.w + (int64_t)n0 * d, min(BN, n_out - n0) * d * 2);
 
   // Loop-invariant lane offsets (bytes): wave w fills 1 KiB blocks w, w+4, ...
   // (blocks 0..19: A, 20..35: B); block b holds 8 consecutive rows of its
@@ -208,36 +211,90 @@ __global__ __launch_bounds__(WAVES * 64) void proj_kernel(ProjArgs a) {
     st = stn;
   }
 
-  // Epilogue: z[m][n] -= h * v[m][n].  C layout: lane (col r, group g),
-  // register q -> row 8*(q/4) + 4*g + q%4 of the 32x32 tile.  All of a row
-  // tile's z values are loaded before any is stored, so the loads overlap.
+  // Epilogue.  C layout: lane (col r, group g), register q -> row
+  // 8*(q/4) + 4*g + q%4 of the 32x32 tile.
   const int n = n0 + wave * 32 + r;
-  if (n >= d) return;
-  float* const zc = z + n;
+  if (n >= n_out) return;
   const bool full = m0 + BM <= n_q;                // uniform
+  if constexpr (MODE == kProjEuler) {
+    // z[m][n] -= h * y[m][n] (and zb = bf16(z)).  All of a row tile's z
+    // values are loaded before any is stored, so the loads overlap.
+    float* const zc = z + n;
+    bf16* const zbc = s.zb ? s.zb + n : nullptr;
 #pragma unroll
-  for (int i = 0; i < MT; ++i) {
-    float zv[16];
+    for (int i = 0; i < MT; ++i) {
+      float zv[16];
 #pragma unroll
-    for (int q = 0; q < 16; ++q) {
-      const int m = m0 + i * 32 + (q >> 2) * 8 + g * 4 + (q & 3);
-      zv[q] = (full || m < n_q) ? zc[(int64_t)m * d] : 0.f;
+      for (int q = 0; q < 16; ++q) {
+        const int m = m0 + i * 32 + (q >> 2) * 8 + g * 4 + (q & 3);
+        zv[q] = (full || m < n_q) ? zc[(int64_t)m * d] : 0.f;
+      }
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        const int m = m0 + i * 32 + (q >> 2) * 8 + g * 4 + (q & 3);
+        if (full || m < n_q) {
+          const float zn = zv[q] - hstep * acc[i][q];
+          zc[(int64_t)m * d] = zn;
+          if (zbc) zbc[(int64_t)m * d] = (bf16)zn;
+        }
+      }
     }
+  } else {
+    // Column n of Y is column n % d of Q, K_u or V_u, rounded to bf16.
+    const int t = n >= 2 * d ? 2 : (n >= d ? 1 : 0);
+    bf16* const oc = s.out[t] + (n - t * d);
 #pragma unroll
-    for (int q = 0; q < 16; ++q) {
-      const int m = m0 + i * 32 + (q >> 2) * 8 + g * 4 + (q & 3);
-      if (full || m < n_q) zc[(int64_t)m * d] = zv[q] - hstep * acc[i][q];
-    }
+    for (int i = 0; i < MT; ++i)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        const int m = m0 + i * 32 + (q >> 2) * 8 + g * 4 + (q & 3);
+        if (full || m < n_q) oc[(int64_t)m * d] = (bf16)acc[i][q];
+      }
   }
 }
 
-hipError_t launch_proj(const ProjArgs& a, hipStream_t st) {
+// zb = bf16(z) (round to nearest even), 8 elements per thread.
+__global__ __launch_bounds__(256) void cvt_kernel(CvtArgs a) {
+  const int64_t grp = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (grp >= a.items) return;
+  int si = 0;
+#pragma unroll
+  for (int i = 1; i < kMaxSessPerLaunch; ++i)
+    if (i < a.n_sess && grp >= a.s[i].item0) si = i;
+  const CvtSess& s = a.s[si];
+  const int64_t e = (grp - s.item0) * 8;
+  const f32x4 x0 = *reinterpret_cast<const f32x4*>(s.z + e);
+  const f32x4 x1 = *reinterpret_cast<const f32x4*>(s.z + e + 4);
+  bf16x8 y;
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    y[t] = (bf16)x0[t];
+    y[4 + t] = (bf16)x1[t];
+  }
+  *reinterpret_cast<bf16x8*>(s.zb + e) = y;
+}
+
+hipError_t launch_proj(const ProjArgs& a, int mode, hipStream_t st) {
   if (a.items <= 0) return hipSuccess;
-  static const hipError_t attr_err = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(&proj_kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
-      LDS_BYTES);
+  static const hipError_t attr_err = [] {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&proj_kernel<kProjEuler>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES);
+    if (e == hipSuccess)
+      e = hipFuncSetAttribute(reinterpret_cast<const void*>(&proj_kernel<kProjQkv>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES);
+    return e;
+  }();
   if (attr_err != hipSuccess) return attr_err;
-  hipLaunchKernelGGL(proj_kernel, dim3(a.items), dim3(WAVES * 64), LDS_BYTES, st, a);
+  if (mode == kProjEuler)
+    hipLaunchKernelGGL(proj_kernel<kProjEuler>, dim3(a.items), dim3(WAVES * 64), LDS_BYTES, st, a);
+  else
+    hipLaunchKernelGGL(proj_kernel<kProjQkv>, dim3(a.items), dim3(WAVES * 64), LDS_BYTES, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_cvt(const CvtArgs& a, hipStream_t st) {
+  if (a.items <= 0) return hipSuccess;
+  hipLaunchKernelGGL(cvt_kernel, dim3((unsigned)((a.items + 255) / 256)), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 

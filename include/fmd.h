@@ -183,6 +183,45 @@ int fmd_denoise_unit(fmd_unit_io* sessions, int32_t n_sessions, int32_t n_steps,
                      const void* w_o, void* workspace, size_t workspace_bytes,
                      void* stream);
 
+/*
+ * The solver with the unit's queries, keys and values re-derived from the
+ * latent at every step: the velocity network is evaluated on the noisy
+ * latents it integrates [Wan-Streamer (gongshangzheng blog), 3.4 条件流匹配:
+ * f_theta on the unit's noisy audio and video latents; 3.3 Block-Causal
+ * Transformer: those tokens attend to the clean history and to each other].
+ * Per step s, for every session:
+ *   [Q | K_u | V_u] = bf16( bf16(z) * W_qkv^T ),  W_qkv bf16 [3d][d] stored
+ *       [d_out][d_in]; output column h*hd + e of each third is head h,
+ *       feature e (bf16 rounding: nearest, ties to even);
+ *   then the step of fmd_denoise_step with those Q, K_u, V_u and h[s].
+ * One session's inputs (no per-step Q/K/V: they come from z):
+ *   cache          : the session's ring (state before the append; updated)
+ *   k_slice/v_slice: bf16 [slice_tokens][n_heads][head_dim]; 0 tokens = no append
+ *   z              : fp32 [n_q][d], eps on entry, the final latent on exit
+ *   h              : HOST array [n_steps] of positive step sizes
+ */
+typedef struct fmd_unit_qkv_io {
+  fmd_kv_cache* cache;
+  const void* k_slice;
+  const void* v_slice;
+  int64_t slice_tokens;
+  float* z;
+  int32_t n_video;
+  int32_t n_audio;
+  const float* h;
+} fmd_unit_qkv_io;
+
+/* Workspace bytes fmd_denoise_unit_qkv needs (pure host arithmetic). */
+int fmd_unit_qkv_workspace_bytes(const fmd_unit_qkv_io* sessions, int32_t n_sessions,
+                                 size_t* out_bytes);
+
+/* One denoised unit of the z-dependent solver for n_sessions sessions: one
+ * batched append, then n_steps steps as above.  w_qkv: bf16 [3d][d]; w_o:
+ * bf16 [d][d].  Errors: as fmd_denoise_unit. */
+int fmd_denoise_unit_qkv(fmd_unit_qkv_io* sessions, int32_t n_sessions, int32_t n_steps,
+                         const void* w_qkv, const void* w_o, void* workspace,
+                         size_t workspace_bytes, void* stream);
+
 /* Static description of a status code (never NULL). */
 const char* fmd_strerror(int status);
 
@@ -196,7 +235,9 @@ enum {
   FMD_KERNEL_ATTN = 2,      /* attention main kernel */
   FMD_KERNEL_COMBINE = 3,   /* merge of key-split partial results */
   FMD_KERNEL_PROJ = 4,      /* projection GEMM with the Euler update */
-  FMD_KERNEL_COUNT = 5
+  FMD_KERNEL_QKV = 5,       /* projection of the latent to Q, K_u, V_u */
+  FMD_KERNEL_CVT = 6,       /* bf16 copy of the starting latent */
+  FMD_KERNEL_COUNT = 7
 };
 
 /* Per-launch timing with HIP events recorded on the launch stream around

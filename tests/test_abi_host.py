@@ -180,3 +180,40 @@ def test_device_code_has_no_packed_fp32_arithmetic():
             asm = open(out).read()
             assert not re.search(r"v_pk_(add|mul|fma)_f32", asm), name
             assert "scratch_" not in asm, f"{name}: register spills to scratch"
+
+
+def test_denoise_unit_qkv_validation_leaves_state():
+    from flow_matching_denoising_amd import _UnitQkvIO
+    c = _cache()
+    h = (ctypes.c_float * 2)(0.5, -0.5)
+    io = _UnitQkvIO(ctypes.pointer(c), FAKE, FAKE, 32, FAKE, 12, 4,
+                    ctypes.cast(h, ctypes.POINTER(ctypes.c_float)))
+    arr = (_UnitQkvIO * 1)(io)
+    run = fmd._denoise_unit_qkv
+    assert run(arr, 1, 2, FAKE, FAKE, FAKE, 1 << 30, None) == -1       # h[1] < 0
+    assert run(arr, 1, 0, FAKE, FAKE, FAKE, 1 << 30, None) == -1       # no steps
+    h[1] = 0.5
+    assert run(arr, 1, 2, 0, FAKE, FAKE, 1 << 30, None) == -1          # no W_qkv
+    assert run(arr, 1, 2, FAKE + 8, FAKE, FAKE, 1 << 30, None) == -4   # misaligned W_qkv
+    assert run(arr, 1, 2, FAKE, FAKE, FAKE, 16, None) == -5            # workspace too small
+    io.slice_tokens = 200
+    arr = (_UnitQkvIO * 1)(io)
+    assert run(arr, 1, 2, FAKE, FAKE, FAKE, 1 << 30, None) == -3       # slice > cap
+    io.slice_tokens = 32
+    io.z = 0
+    arr = (_UnitQkvIO * 1)(io)
+    assert run(arr, 1, 2, FAKE, FAKE, FAKE, 1 << 30, None) == -1       # no z
+    assert (c.len_tokens, c.head_tokens) == (96, 96)
+
+
+def test_unit_qkv_workspace_holds_projections_and_step():
+    from flow_matching_denoising_amd import _UnitQkvIO
+    c = _cache(H=40, hd=128, cap=60416, ln=60416, head=0)
+    h = (ctypes.c_float * 1)(1.0)
+    io = _UnitQkvIO(ctypes.pointer(c), 0, 0, 0, FAKE, 920, 8,
+                    ctypes.cast(h, ctypes.POINTER(ctypes.c_float)))
+    out = ctypes.c_size_t(0)
+    assert fmd._unit_qkv_workspace_bytes((_UnitQkvIO * 1)(io), 1, ctypes.byref(out)) == 0
+    _, step = _ws([_step(c, 920, 8)])
+    # bf16 z, Q, K_u, V_u (4 x 928 x 5120 bf16) on top of the step workspace.
+    assert out.value >= step + 4 * 928 * 5120 * 2
