@@ -25,6 +25,9 @@ sections):
 5. ``qkv.qkv_projection`` / ``qkv.denoise_unit_qkv`` -- the same solver with
    the unit's Q, K, V projected from the current latent at every step
    [same page, 3.4: f_theta is evaluated on the noisy latents it integrates].
+6. ``cfg.denoise_unit_cfg`` -- the classifier-free-guided sampler of the
+   teacher: conditional and unconditional branches, guided velocity
+   v_u + g (v_c - v_u) [same page, training stages, Stage 3].
 
 Everything is float64 unless a function says otherwise.  bf16 inputs arrive as
 uint16 bit patterns and are widened exactly by ``ring.bf16_bits_to_f64``.
@@ -39,3 +42,4 @@ from .ring import bf16_bits_to_f64, kv_append, valid_slots  # noqa: F401
 from .attention import attention, attention_naive  # noqa: F401
 from .flow import velocity, euler_step, denoise_step, denoise_unit  # noqa: F401
 from .qkv import round_to_bf16, f64_to_bf16_bits, qkv_projection, denoise_unit_qkv  # noqa: F401
+from .cfg import guided_velocity, denoise_unit_cfg  # noqa: F401

@@ -210,3 +210,57 @@ def check_qkv_mean_decay(unit_qkv_fn, hs=(0.5, 0.5), seed=4, H=2, hd=8, n_q=16):
     expect = (eps - mean0) + np.prod([1.0 - h for h in hs]) * mean0
     got = unit_qkv_fn(ring, ring, 0, 0, None, None, eps, list(hs), w, w_o, H)["z"]
     return float(np.max(np.abs(got - expect)))
+
+
+# ---------------------------------------------------------------------------
+# Classifier-free-guided sampling (two branches, guidance scale g).
+# ---------------------------------------------------------------------------
+def check_cfg_uniform_closed_form(unit_cfg_fn, g=3.0, hs=(0.5, 0.25), seed=5, H=2, hd=8,
+                                  cap=64, n_q=6):
+    """W_q = 0 and W_v = 0: in each branch every query attends uniformly to all
+    seen values, the unit's own being 0, so O_b = (sum of the branch's valid
+    ring values + its appended slice) / (len_b + T_b + n_q) at every step.  The
+    branches differ in length, start and slice; nothing is evicted (cap is
+    large).  Then z_final = eps - (sum h) (v_u + g (v_c - v_u)), v_b = O_b W_o^T.
+    Returns max |error|."""
+    rng = np.random.default_rng(seed)
+    d = H * hd
+    w = np.zeros((3 * d, d), dtype=np.uint16)
+    w[d:2 * d] = random_bits(rng, (d, d))          # W_k nonzero: must not matter
+    w_o = random_bits(rng, (d, d), scale=d ** -0.5)
+    eps = rng.standard_normal((n_q, d))
+    branches, means = [], []
+    for length, head, T in ((20, 50, 7), (33, 9, 4)):
+        ring_k = random_bits(rng, (H, cap, hd))
+        ring_v = random_bits(rng, (H, cap, hd))
+        sk = random_bits(rng, (T, H, hd))
+        sv = random_bits(rng, (T, H, hd))
+        slots = [(head - length + i) % cap for i in range(length)]
+        total = widen(ring_v)[:, slots, :].sum(axis=1) + widen(sv).sum(axis=0)   # [H][hd]
+        means.append(total / (length + T + n_q))
+        branches.append(dict(ring_k=ring_k, ring_v=ring_v, length=length, head=head,
+                             slice_k=sk, slice_v=sv))
+    W = widen(w_o)
+    v_c, v_u = (np.tile(m.reshape(1, d), (n_q, 1)) @ W.T for m in means)
+    expect = eps - sum(hs) * (v_u + g * (v_c - v_u))
+    got = unit_cfg_fn(branches[0], branches[1], eps, list(hs), g, w, w_o, H)["z"]
+    return float(np.max(np.abs(got - expect)))
+
+
+def check_cfg_mean_decay(unit_cfg_fn, g=4.0, hs=(0.5, 0.5), seed=6, H=2, hd=8, n_q=16):
+    """Both caches empty, W_q = W_k = 0, W_v = I, W_o = I: both branches see only
+    the unit's own values, so v_c = v_u = mean(bf16(z)) and guidance changes
+    nothing whatever g is; each step maps z_i -> z_i - h mean(z), the mean decays
+    by prod(1 - h) (up to the bf16 rounding of z).  Returns max |error|."""
+    rng = np.random.default_rng(seed)
+    d = H * hd
+    eps = rng.standard_normal((n_q, d)) + 0.5
+    w = np.zeros((3 * d, d), dtype=np.uint16)
+    w[2 * d:] = bits(np.eye(d))
+    w_o = bits(np.eye(d))
+    empty = dict(ring_k=np.zeros((H, 16, hd), dtype=np.uint16),
+                 ring_v=np.zeros((H, 16, hd), dtype=np.uint16), length=0, head=3)
+    mean0 = eps.mean(axis=0, keepdims=True)
+    expect = (eps - mean0) + np.prod([1.0 - h for h in hs]) * mean0
+    got = unit_cfg_fn(empty, dict(empty), eps, list(hs), g, w, w_o, H)["z"]
+    return float(np.max(np.abs(got - expect)))

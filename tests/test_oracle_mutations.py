@@ -111,3 +111,48 @@ def test_unrounded_latent_in_projection_is_caught(monkeypatch):
     got = qkv_mod.qkv_projection(z, w, 2)
     want = brute_qkv(z, w, 2)
     assert max(np.max(np.abs(oracle.bf16_bits_to_f64(g) - w_)) for g, w_ in zip(got, want)) > 0
+
+
+cfg_mod = importlib.import_module("oracle.cfg")
+
+
+def test_swapped_guidance_branches_is_caught(monkeypatch):
+    # mistake: the guidance extrapolates from the conditional branch instead
+    from tests.pins import check_cfg_uniform_closed_form
+    monkeypatch.setattr(cfg_mod, "guided_velocity", lambda v_c, v_u, g: v_c + g * (v_u - v_c))
+    assert check_cfg_uniform_closed_form(oracle.denoise_unit_cfg) > 1e-3
+
+
+def test_other_guidance_convention_is_caught(monkeypatch):
+    # mistake: v_c + g (v_c - v_u), the convention whose scale is offset by one
+    from tests.pins import check_cfg_uniform_closed_form
+    monkeypatch.setattr(cfg_mod, "guided_velocity", lambda v_c, v_u, g: v_c + g * (v_c - v_u))
+    assert check_cfg_uniform_closed_form(oracle.denoise_unit_cfg) > 1e-3
+
+
+def test_slice_appended_to_one_branch_only_is_caught(monkeypatch):
+    # mistake: the unconditional branch skips its slice
+    from tests.pins import check_cfg_uniform_closed_form
+    orig = cfg_mod._branch
+    calls = []
+
+    def first_only(b):
+        calls.append(1)
+        if len(calls) % 2 == 0:
+            b = dict(b, slice_k=None, slice_v=None)
+        return orig(b)
+    monkeypatch.setattr(cfg_mod, "_branch", first_only)
+    assert check_cfg_uniform_closed_form(oracle.denoise_unit_cfg) > 1e-3
+
+
+def test_guided_projection_from_eps_is_caught(monkeypatch):
+    # mistake: Q, K_u, V_u projected from eps at every step
+    from tests.pins import check_cfg_mean_decay
+    orig = cfg_mod.qkv_projection
+    first = {}
+
+    def from_first(z, w, H):
+        first.setdefault("z", np.array(z))
+        return orig(first["z"], w, H)
+    monkeypatch.setattr(cfg_mod, "qkv_projection", from_first)
+    assert check_cfg_mean_decay(oracle.denoise_unit_cfg) > 5e-2
