@@ -16,6 +16,8 @@ Prints ONE JSON line (rank 0, N=1).  Besides throughput it reports:
   update), scaled to the unit's solver steps;
 * qkv_unit: the same unit with the z-dependent solver (Q, K_u, V_u projected
   from the latent at every step);
+* cfg_unit: the guided teacher's sampler (conditional + unconditional rings,
+  16 steps, guidance 5) on the 640x368-class unit;
 * append_batch8: the batched ring append at the 8-session shape.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
@@ -136,6 +138,72 @@ def qkv_unit_probe(wl, ui, caches, states, w_o, units=10, warmup=2):
             "ms_per_unit": round(wall / units * 1e3, 4),
             "qkv_gemm_us": round(ms / n * 1e3, 2),
             "qkv_gemm_TFLOPs": round(qkv_flops / (ms / n / 1e3) / 1e12, 1)}
+
+
+def cfg_unit_probe(units=3, warmup=1):
+    """The guided (teacher) sampler on its 640x368-class workload: conditional
+    and unconditional 60,416-key rings, both appended, 16 steps; per step one
+    Q/K/V projection, attention over both branches (one launch), the guided
+    mix and one projection with the Euler update."""
+    import numpy as np
+    import torch
+
+    import flow_matching_denoising_amd as fmd
+    import workload
+
+    wl = workload.get("v02_cfg_unit")
+    dev = torch.device("cuda:0")
+
+    def bf(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    ui = workload.make_inputs(wl, reuse_step_inputs=True)
+    w_qkv = bf(workload.qkv_weight(wl.seed, wl.d, wl.head_dim))
+    w_o = bf(ui.w_o)
+    ios, caches = [], []
+    for i, si in enumerate(ui.sessions):
+        s = si.shape
+        un = workload.uncond_inputs(wl, i)
+        st = dict(len_tokens=s.len_before, head_tokens=s.head_before)
+        cc = fmd.KVCache(s.n_heads, s.head_dim, s.cap_tokens, device=dev, k=bf(si.ring_k),
+                         v=fmd.KVCache.logical_to_device_v(bf(si.ring_v)), **st)
+        uc = fmd.KVCache(s.n_heads, s.head_dim, s.cap_tokens, device=dev, k=bf(un.ring_k),
+                         v=fmd.KVCache.logical_to_device_v(bf(un.ring_v)), **st)
+        z = torch.from_numpy(si.eps.copy()).to(dev)
+        ios.append(fmd.UnitCfgIO(cc, uc, z, list(s.h), workload.CFG_GUIDANCE,
+                                 cond_slice=(bf(si.slice_k), bf(si.slice_v)),
+                                 uncond_slice=(bf(un.slice_k), bf(un.slice_v)),
+                                 n_audio=s.n_audio))
+        caches.append((cc, uc, (s.len_before, s.head_before), z, si.eps))
+    ws = fmd.alloc_workspace(fmd.unit_cfg_workspace_bytes(ios), dev)
+
+    def one():
+        for cc, uc, (ln, hd_), z, eps in caches:
+            cc.set_state(ln, hd_)
+            uc.set_state(ln, hd_)
+        fmd.denoise_unit_cfg(ios, w_qkv, w_o, ws)
+
+    for _ in range(warmup):
+        one()
+    torch.cuda.synchronize()
+    fmd.profile_enable(True)
+    t0 = time.perf_counter()
+    for _ in range(units):
+        one()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kt = {k: fmd.profile_read(k) for k in ("attn", "mix", "proj", "qkv", "combine")}
+    fmd.profile_enable(False)
+    attn_ms, attn_n = kt["attn"]
+    attn_flops = 2 * wl.attention_flops_per_step()        # both branches in one launch
+    s0 = wl.sessions[0]
+    return {"workload": wl.name, "solver_steps": s0.n_steps, "guidance": workload.CFG_GUIDANCE,
+            "units_per_s": round(len(ui.sessions) * units / wall, 3),
+            "ms_per_unit": round(wall / units * 1e3, 3),
+            "attn_us": round(attn_ms / attn_n * 1e3, 2),
+            "attn_TFLOPs": round(attn_flops / (attn_ms / attn_n / 1e3) / 1e12, 1),
+            "per_kernel_us": {k: (round(v[0] / v[1] * 1e3, 2) if v[1] else None)
+                              for k, v in kt.items()}}
 
 
 def append_batch_probe(launches=20):
@@ -335,6 +403,8 @@ def main():
     }
     out["qkv_unit"] = qkv_unit_probe(wl, ui, caches, states, w_o)
     del caches, ios
+    torch.cuda.empty_cache()
+    out["cfg_unit"] = cfg_unit_probe()
     torch.cuda.empty_cache()
     out["append_batch8"] = append_batch_probe()
     if not args.no_cpu_baseline:

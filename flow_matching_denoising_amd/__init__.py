@@ -30,7 +30,8 @@ FMD_MAX_SESSIONS = 64
 FMD_CACHE_BLOCK = 16
 STATUS = {0: "FMD_OK", -1: "FMD_E_INVAL", -2: "FMD_E_SHAPE", -3: "FMD_E_CAPACITY",
           -4: "FMD_E_ALIGN", -5: "FMD_E_WORKSPACE", -6: "FMD_E_HIP"}
-KERNEL_CLASSES = {"append": 0, "vt": 1, "attn": 2, "combine": 3, "proj": 4, "qkv": 5, "cvt": 6}
+KERNEL_CLASSES = {"append": 0, "vt": 1, "attn": 2, "combine": 3, "proj": 4, "qkv": 5, "cvt": 6,
+                  "mix": 7}
 
 
 class FmdError(RuntimeError):
@@ -69,6 +70,16 @@ class _UnitQkvIO(ctypes.Structure):
                 ("h", ctypes.POINTER(ctypes.c_float))]
 
 
+class _UnitCfgIO(ctypes.Structure):
+    _fields_ = [("cond", ctypes.POINTER(_Cache)), ("uncond", ctypes.POINTER(_Cache)),
+                ("cond_k_slice", ctypes.c_void_p), ("cond_v_slice", ctypes.c_void_p),
+                ("cond_slice_tokens", ctypes.c_int64),
+                ("uncond_k_slice", ctypes.c_void_p), ("uncond_v_slice", ctypes.c_void_p),
+                ("uncond_slice_tokens", ctypes.c_int64),
+                ("z", ctypes.c_void_p), ("n_video", ctypes.c_int32), ("n_audio", ctypes.c_int32),
+                ("h", ctypes.POINTER(ctypes.c_float)), ("guidance", ctypes.c_float)]
+
+
 def _sig(name, restype, *argtypes):
     f = getattr(_lib, name)
     f.restype = restype
@@ -95,6 +106,10 @@ _unit_qkv_workspace_bytes = _sig("fmd_unit_qkv_workspace_bytes", ctypes.c_int,
                                  ctypes.POINTER(_UnitQkvIO), _i32, ctypes.POINTER(_sz))
 _denoise_unit_qkv = _sig("fmd_denoise_unit_qkv", ctypes.c_int, ctypes.POINTER(_UnitQkvIO), _i32,
                          _i32, _vp, _vp, _vp, _sz, _vp)
+_unit_cfg_workspace_bytes = _sig("fmd_unit_cfg_workspace_bytes", ctypes.c_int,
+                                 ctypes.POINTER(_UnitCfgIO), _i32, ctypes.POINTER(_sz))
+_denoise_unit_cfg = _sig("fmd_denoise_unit_cfg", ctypes.c_int, ctypes.POINTER(_UnitCfgIO), _i32,
+                         _i32, _vp, _vp, _vp, _sz, _vp)
 _strerror = _sig("fmd_strerror", ctypes.c_char_p, ctypes.c_int)
 _last_error = _sig("fmd_last_error", ctypes.c_char_p)
 _profile_enable = _sig("fmd_profile_enable", ctypes.c_int, ctypes.c_int)
@@ -104,7 +119,8 @@ _version = _sig("fmd_version", ctypes.c_char_p)
 
 EXPORTED = ["fmd_kv_append", "fmd_kv_append_batched", "fmd_workspace_bytes", "fmd_denoise_step",
             "fmd_attention", "fmd_unit_workspace_bytes", "fmd_denoise_unit",
-            "fmd_unit_qkv_workspace_bytes", "fmd_denoise_unit_qkv", "fmd_strerror",
+            "fmd_unit_qkv_workspace_bytes", "fmd_denoise_unit_qkv",
+            "fmd_unit_cfg_workspace_bytes", "fmd_denoise_unit_cfg", "fmd_strerror",
             "fmd_last_error", "fmd_profile_enable", "fmd_profile_read", "fmd_version"]
 
 
@@ -362,6 +378,62 @@ def denoise_unit_qkv(sessions, w_qkv, w_o, workspace=None, stream=None):
         workspace = alloc_workspace(unit_qkv_workspace_bytes(sessions), sessions[0].z.device)
     arr, n = _qkv_array(sessions)
     _check(_denoise_unit_qkv(arr, n, n_steps, _ptr(w_qkv, torch.bfloat16, "w_qkv"),
+                             _ptr(w_o, torch.bfloat16, "w_o"), workspace.data_ptr(),
+                             workspace.numel(), _stream_ptr(stream)))
+
+
+class UnitCfgIO:
+    """One unit's inputs for the classifier-free-guided solver (see
+    ``fmd_unit_cfg_io``): the conditional and the unconditional branch's caches
+    and slices, the latent z (float32 [n_q][d], eps in, final latent out), the
+    step sizes h and the guidance scale g."""
+
+    def __init__(self, cond: KVCache, uncond: KVCache, z, h, guidance, cond_slice=(None, None),
+                 uncond_slice=(None, None), n_audio=0):
+        self.cond, self.uncond, self.z = cond, uncond, z
+        self.cond_slice, self.uncond_slice = cond_slice, uncond_slice
+        self.h = (ctypes.c_float * len(h))(*[float(x) for x in h])
+        self.n_steps = len(h)
+        self.n_q = z.shape[0]
+        self.n_audio = n_audio
+        self.guidance = float(guidance)
+
+    def _struct(self):
+        def sl(pair, name):
+            k, v = pair
+            T = 0 if k is None else k.shape[0]
+            return (_ptr(k, torch.bfloat16, name + "_k_slice", allow_none=True),
+                    _ptr(v, torch.bfloat16, name + "_v_slice", allow_none=True), T)
+        return _UnitCfgIO(ctypes.pointer(self.cond._c), ctypes.pointer(self.uncond._c),
+                          *sl(self.cond_slice, "cond"), *sl(self.uncond_slice, "uncond"),
+                          _ptr(self.z, torch.float32, "z"), self.n_q - self.n_audio, self.n_audio,
+                          ctypes.cast(self.h, ctypes.POINTER(ctypes.c_float)), self.guidance)
+
+
+def _cfg_array(sessions):
+    n = len(sessions)
+    return (_UnitCfgIO * n)(*[s._struct() for s in sessions]), n
+
+
+def unit_cfg_workspace_bytes(sessions) -> int:
+    arr, n = _cfg_array(sessions)
+    out = _sz(0)
+    _check(_unit_cfg_workspace_bytes(arr, n, ctypes.byref(out)))
+    return out.value
+
+
+def denoise_unit_cfg(sessions, w_qkv, w_o, workspace=None, stream=None):
+    """Append every branch's slice, then run the S guided solver steps: per
+    step one Q/K/V projection of each unit's latent, attention over both
+    branches' caches, the guided mix and one projection with the Euler
+    update."""
+    n_steps = sessions[0].n_steps
+    if any(s.n_steps != n_steps for s in sessions):
+        raise ValueError("all sessions must have the same number of steps")
+    if workspace is None:
+        workspace = alloc_workspace(unit_cfg_workspace_bytes(sessions), sessions[0].z.device)
+    arr, n = _cfg_array(sessions)
+    _check(_denoise_unit_cfg(arr, n, n_steps, _ptr(w_qkv, torch.bfloat16, "w_qkv"),
                              _ptr(w_o, torch.bfloat16, "w_o"), workspace.data_ptr(),
                              workspace.numel(), _stream_ptr(stream)))
 

@@ -311,40 +311,57 @@ int check_workspace(void* ws, size_t have, size_t need) {
 
 // Enqueue the step kernels (validation already done).  o_out != nullptr:
 // attention only, O to the caller's buffer.
-// zb_out (optional, per session): where the projection epilogue also writes
-// bf16(z) after the update (the next step's input to the Q/K/V projection).
+// zb_out (optional, one per projected unit): where the projection epilogue
+// also writes bf16(z) after the update (the next step's input to the Q/K/V
+// projection).
+// guidance != nullptr: the units come in pairs (2i conditional, 2i+1
+// unconditional) that share q, k_u, v_u, z and h; pair i is guided with scale
+// guidance[i].  The pair's unit keys and values are transposed once, both
+// branches attend, their outputs are mixed (in place into the conditional
+// one) and one projection updates z.
 int enqueue_steps(const fmd_unit_step* units, int n, const std::vector<SessPlan>& plans,
                   const void* w_o, char* ws, bf16* o_out, hipStream_t st,
-                  bf16* const* zb_out = nullptr) {
+                  bf16* const* zb_out = nullptr, const float* guidance = nullptr) {
   const int H = units[0].cache->n_heads, hd = units[0].cache->head_dim;
   const int d = H * hd;
   const float scale_log2 = (float)(1.4426950408889634 / sqrt((double)hd));
+  const int per_proj = guidance ? 2 : 1;
   int64_t o_row = 0;
   for (int c0 = 0; c0 < n; c0 += kMaxSessPerLaunch) {
     const int cn = std::min(kMaxSessPerLaunch, n - c0);
     VtArgs va = {};
     AttnArgs aa = {};
     CombineArgs ca = {};
+    MixArgs ma = {};
     ProjArgs pa = {};
-    va.n_sess = aa.n_sess = ca.n_sess = pa.n_sess = cn;
+    va.n_sess = aa.n_sess = ca.n_sess = cn;
+    pa.n_sess = cn / per_proj;
+    ma.n_sess = guidance ? cn / 2 : 0;
     va.H = aa.H = ca.H = H;
     aa.scale_log2 = scale_log2;
     pa.d = d;
     pa.n_out = d;
     pa.w = static_cast<const bf16*>(w_o);
     bool any_split = false;
+    bf16* o_prev = nullptr;
     for (int k = 0; k < cn; ++k) {
       const fmd_unit_step& u = units[c0 + k];
       const SessPlan& p = plans[c0 + k];
       const fmd_kv_cache* c = u.cache;
+      const bool second = guidance && (k & 1);
       bf16* kt = reinterpret_cast<bf16*>(ws + p.off_kt);
       bf16* vt = reinterpret_cast<bf16*>(ws + p.off_vt);
+      if (second) {   // the conditional branch's transposed unit keys/values
+        kt = reinterpret_cast<bf16*>(ws + plans[c0 + k - 1].off_kt);
+        vt = reinterpret_cast<bf16*>(ws + plans[c0 + k - 1].off_vt);
+      }
       bf16* o = o_out ? o_out + o_row * d : reinterpret_cast<bf16*>(ws + p.off_o);
       o_row += p.n_q;
 
+      // A session without transpose work gets an empty range at the current end.
       va.s[k] = VtSess{static_cast<const bf16*>(u.k_u), static_cast<const bf16*>(u.v_u), kt, vt,
                        p.n_q, p.npad / 16, va.items, 0};
-      va.items += H * (p.npad / 16);
+      if (!second) va.items += H * (p.npad / 16);
 
       AttnSess& as = aa.s[k];
       as.q = static_cast<const bf16*>(u.q);
@@ -375,9 +392,17 @@ int enqueue_steps(const fmd_unit_step* units, int n, const std::vector<SessPlan>
         any_split = true;
       }
 
+      if (second) {
+        const int64_t ne = (int64_t)p.n_q * d;
+        ma.s[k / 2] = MixSess{o_prev, o, guidance[(c0 + k) / 2], ne, ma.items};
+        ma.items += ne / 8;
+        continue;
+      }
+      o_prev = o;
+      const int j = k / per_proj, unit = (c0 + k) / per_proj;
       const int mtiles = (p.n_q + kProjTile - 1) / kProjTile;
       const int ntiles = (d + kProjTileN - 1) / kProjTileN;
-      pa.s[k] = ProjSess{o, u.z, zb_out ? zb_out[c0 + k] : nullptr, {nullptr, nullptr, nullptr},
+      pa.s[j] = ProjSess{o, u.z, zb_out ? zb_out[unit] : nullptr, {nullptr, nullptr, nullptr},
                          p.n_q, mtiles, pa.items, u.h};
       pa.items += mtiles * ntiles;
     }
@@ -389,6 +414,9 @@ int enqueue_steps(const fmd_unit_step* units, int n, const std::vector<SessPlan>
       return rc;
     if (any_split &&
         (rc = timed_launch(FMD_KERNEL_COMBINE, st, [&] { return launch_combine(ca, hd, st); })))
+      return rc;
+    if (guidance &&
+        (rc = timed_launch(FMD_KERNEL_MIX, st, [&] { return launch_mix(ma, st); })))
       return rc;
     if (!o_out &&
         (rc = timed_launch(FMD_KERNEL_PROJ, st, [&] { return launch_proj(pa, kProjEuler, st); })))
@@ -638,6 +666,173 @@ int fmd_denoise_unit(fmd_unit_io* sessions, int32_t n_sessions, int32_t n_steps,
   return FMD_OK;
 }
 
+// The z-dependent solver's driver, shared by the plain and the guided form.
+// One solver unit has one latent z and nb caches (nb = 1: plain; nb = 2:
+// branch 0 conditional, branch 1 unconditional); its attention sessions are
+// numbered unit * nb + branch.
+struct SolverUnit {
+  fmd_kv_cache* cache[2];
+  int64_t slice_tokens[2];   // appended before the steps (for planning)
+  float* z;
+  int32_t n_video, n_audio;
+  const float* h;
+  float g;
+};
+
+// Workspace: per unit bf16(z), Q, K_u, V_u ([n_q][d] each), then the step
+// workspace of fmd_denoise_step for all attention sessions' post-append rings.
+struct SolverLayout {
+  std::vector<fmd_kv_cache> after;   // per attention session
+  std::vector<fmd_unit_step> steps;  // per attention session
+  std::vector<SessPlan> plans;
+  std::vector<size_t> off;           // per unit: zb, then q, k, v at +1..3 * slab
+  size_t slab_total = 0, bytes = 0;
+};
+
+static void layout_solver(const std::vector<SolverUnit>& us, int nb, SolverLayout& L) {
+  const int n = (int)us.size();
+  const int d = us[0].cache[0]->n_heads * us[0].cache[0]->head_dim;
+  L.after.resize((size_t)n * nb);
+  L.steps.resize((size_t)n * nb);
+  L.off.resize(n);
+  size_t off = 0;
+  for (int i = 0; i < n; ++i) {
+    const SolverUnit& u = us[i];
+    const int n_q = u.n_video + u.n_audio;
+    L.off[i] = off;
+    off += 4 * align256((size_t)n_q * d * 2);
+    for (int b = 0; b < nb; ++b) {
+      fmd_kv_cache& a = L.after[(size_t)i * nb + b];
+      a = *u.cache[b];
+      if (u.slice_tokens[b] > 0) {
+        a.head_tokens = (a.head_tokens + u.slice_tokens[b]) % a.cap_tokens;
+        a.len_tokens = std::min(a.len_tokens + u.slice_tokens[b], a.cap_tokens);
+      }
+      // q/k_u/v_u are placeholders here (set per step); planning needs shapes only.
+      L.steps[(size_t)i * nb + b] =
+          fmd_unit_step{&a, u.z, u.z, u.z, u.z, u.n_video, u.n_audio, u.h[0]};
+    }
+  }
+  L.slab_total = off;
+  size_t step_bytes = 0;
+  plan_steps(L.steps.data(), n * nb, false, L.plans, &step_bytes);
+  L.bytes = L.slab_total + step_bytes;
+}
+
+// Enqueue the solver (validated, appends already enqueued): a bf16 copy of
+// each starting latent, then per step the Q/K/V projection of every unit and
+// the attention + projection step over all attention sessions.
+static int run_solver(const std::vector<SolverUnit>& us, int nb, int n_steps, const void* w_qkv,
+                      const void* w_o, char* ws, SolverLayout& L, hipStream_t st) {
+  const int n = (int)us.size();
+  const int H = us[0].cache[0]->n_heads, hd = us[0].cache[0]->head_dim;
+  const int d = H * hd;
+  std::vector<bf16*> zb(n), q(n), k(n), v(n);
+  for (int i = 0; i < n; ++i) {
+    const size_t slab = align256((size_t)(us[i].n_video + us[i].n_audio) * d * 2);
+    zb[i] = reinterpret_cast<bf16*>(ws + L.off[i]);
+    q[i] = reinterpret_cast<bf16*>(ws + L.off[i] + slab);
+    k[i] = reinterpret_cast<bf16*>(ws + L.off[i] + 2 * slab);
+    v[i] = reinterpret_cast<bf16*>(ws + L.off[i] + 3 * slab);
+  }
+  int rc;
+  for (int c0 = 0; c0 < n; c0 += kMaxSessPerLaunch) {
+    const int cn = std::min(kMaxSessPerLaunch, n - c0);
+    CvtArgs ca = {};
+    ca.n_sess = cn;
+    for (int j = 0; j < cn; ++j) {
+      const int i = c0 + j;
+      const int64_t ne = (int64_t)(us[i].n_video + us[i].n_audio) * d;
+      ca.s[j] = CvtSess{us[i].z, zb[i], ne, ca.items};
+      ca.items += ne / 8;
+    }
+    if ((rc = timed_launch(FMD_KERNEL_CVT, st, [&] { return launch_cvt(ca, st); }))) return rc;
+  }
+
+  std::vector<float> g(n);
+  for (int i = 0; i < n; ++i) g[i] = us[i].g;
+  char* step_ws = ws + L.slab_total;
+  for (int s = 0; s < n_steps; ++s) {
+    for (int c0 = 0; c0 < n; c0 += kMaxSessPerLaunch) {
+      const int cn = std::min(kMaxSessPerLaunch, n - c0);
+      ProjArgs pa = {};
+      pa.n_sess = cn;
+      pa.d = d;
+      pa.n_out = 3 * d;
+      pa.w = static_cast<const bf16*>(w_qkv);
+      const int ntiles = (3 * d + kProjTileN - 1) / kProjTileN;
+      for (int j = 0; j < cn; ++j) {
+        const int i = c0 + j;
+        const int n_q = us[i].n_video + us[i].n_audio;
+        const int mtiles = (n_q + kProjTile - 1) / kProjTile;
+        pa.s[j] = ProjSess{zb[i], nullptr, nullptr, {q[i], k[i], v[i]}, n_q, mtiles, pa.items,
+                           0.f};
+        pa.items += mtiles * ntiles;
+      }
+      if ((rc = timed_launch(FMD_KERNEL_QKV, st, [&] { return launch_proj(pa, kProjQkv, st); })))
+        return rc;
+    }
+    for (int i = 0; i < n; ++i) {
+      for (int b = 0; b < nb; ++b) {
+        fmd_unit_step& u = L.steps[(size_t)i * nb + b];
+        u.cache = us[i].cache[b];   // now in its post-append state
+        u.q = q[i];
+        u.k_u = k[i];
+        u.v_u = v[i];
+        u.z = us[i].z;
+        u.h = us[i].h[s];
+      }
+    }
+    // The last step needs no bf16 copy of its result.
+    if ((rc = enqueue_steps(L.steps.data(), n * nb, L.plans, w_o, step_ws, nullptr, st,
+                            s + 1 < n_steps ? zb.data() : nullptr,
+                            nb == 2 ? g.data() : nullptr)))
+      return rc;
+  }
+  return FMD_OK;
+}
+
+static int check_unit_latent(const float* z, int32_t n_video, int32_t n_audio, const float* h,
+                             int n_steps, int i) {
+  int rc;
+  if ((rc = check_tensor(z, i, "z"))) return rc;
+  if (n_video < 0 || n_audio < 0 || (int64_t)n_video + n_audio < 1 ||
+      (int64_t)n_video + n_audio > (1 << 22))
+    return fail(FMD_E_INVAL, "session %d: n_video=%d n_audio=%d (need 1 <= n_q <= 2^22)", i,
+                n_video, n_audio);
+  if (!h) return fail(FMD_E_INVAL, "session %d: h is NULL", i);
+  for (int k = 0; k < n_steps; ++k)
+    if (!(h[k] > 0.f && isfinite(h[k])))
+      return fail(FMD_E_INVAL, "session %d: h[%d]=%g must be finite and > 0", i, k, h[k]);
+  return FMD_OK;
+}
+
+static int check_unit_slice(const fmd_kv_cache* c, const void* ks, const void* vs, int64_t T,
+                            int i) {
+  if (T < 0) return fail(FMD_E_INVAL, "session %d: slice_tokens %lld", i, (long long)T);
+  return T > 0 ? check_append(c, ks, vs, T, i) : FMD_OK;
+}
+
+// One batched append of every non-empty slice.
+static int enqueue_unit_appends(const std::vector<fmd_kv_cache*>& caches,
+                                const std::vector<const void*>& ks,
+                                const std::vector<const void*>& vs,
+                                const std::vector<int64_t>& ts, hipStream_t st) {
+  std::vector<fmd_kv_cache*> c;
+  std::vector<const void*> k, v;
+  std::vector<int64_t> t;
+  for (size_t i = 0; i < caches.size(); ++i) {
+    if (ts[i] > 0) {
+      c.push_back(caches[i]);
+      k.push_back(ks[i]);
+      v.push_back(vs[i]);
+      t.push_back(ts[i]);
+    }
+  }
+  if (c.empty()) return FMD_OK;
+  return enqueue_appends(c.data(), k.data(), v.data(), t.data(), (int)c.size(), st);
+}
+
 // ---------------------------------------------------------------------------
 // The z-dependent solver: Q, K_u, V_u projected from the latent every step.
 // ---------------------------------------------------------------------------
@@ -653,58 +848,18 @@ static int validate_unit_qkv(const fmd_unit_qkv_io* ss, int n, int n_steps) {
     if (i && (rc = check_same_shape(ss[0].cache, s.cache, i))) return rc;
     for (int j = 0; j < i; ++j)
       if (ss[j].cache == s.cache) return fail(FMD_E_INVAL, "session %d: same cache as %d", i, j);
-    if (s.slice_tokens < 0)
-      return fail(FMD_E_INVAL, "session %d: slice_tokens %lld", i, (long long)s.slice_tokens);
-    if (s.slice_tokens > 0 &&
-        (rc = check_append(s.cache, s.k_slice, s.v_slice, s.slice_tokens, i)))
-      return rc;
-    if ((rc = check_tensor(s.z, i, "z"))) return rc;
-    if (s.n_video < 0 || s.n_audio < 0 || (int64_t)s.n_video + s.n_audio < 1 ||
-        (int64_t)s.n_video + s.n_audio > (1 << 22))
-      return fail(FMD_E_INVAL, "session %d: n_video=%d n_audio=%d (need 1 <= n_q <= 2^22)", i,
-                  s.n_video, s.n_audio);
-    if (!s.h) return fail(FMD_E_INVAL, "session %d: h is NULL", i);
-    for (int k = 0; k < n_steps; ++k)
-      if (!(s.h[k] > 0.f && isfinite(s.h[k])))
-        return fail(FMD_E_INVAL, "session %d: h[%d]=%g must be finite and > 0", i, k, s.h[k]);
+    if ((rc = check_unit_slice(s.cache, s.k_slice, s.v_slice, s.slice_tokens, i))) return rc;
+    if ((rc = check_unit_latent(s.z, s.n_video, s.n_audio, s.h, n_steps, i))) return rc;
   }
   return FMD_OK;
 }
 
-// Workspace: per session bf16(z), Q, K_u, V_u ([n_q][d] each), then the
-// step workspace of fmd_denoise_step for the post-append rings.
-struct QkvLayout {
-  std::vector<fmd_kv_cache> after;
-  std::vector<fmd_unit_step> steps;
-  std::vector<SessPlan> plans;
-  std::vector<size_t> off;       // per session: zb, then q, k, v at +1..3 * slab
-  size_t slab_total = 0, bytes = 0;
-};
-
-static void layout_unit_qkv(const fmd_unit_qkv_io* ss, int n, QkvLayout& L) {
-  const int d = ss[0].cache->n_heads * ss[0].cache->head_dim;
-  L.after.resize(n);
-  L.steps.resize(n);
-  L.off.resize(n);
-  size_t off = 0;
-  for (int i = 0; i < n; ++i) {
-    const int n_q = ss[i].n_video + ss[i].n_audio;
-    L.off[i] = off;
-    off += 4 * align256((size_t)n_q * d * 2);
-    L.after[i] = *ss[i].cache;
-    if (ss[i].slice_tokens > 0) {
-      L.after[i].head_tokens = (L.after[i].head_tokens + ss[i].slice_tokens) % L.after[i].cap_tokens;
-      L.after[i].len_tokens =
-          std::min(L.after[i].len_tokens + ss[i].slice_tokens, L.after[i].cap_tokens);
-    }
-    // q/k_u/v_u are placeholders here (set per call); planning needs shapes only.
-    L.steps[i] = fmd_unit_step{&L.after[i], ss[i].z, ss[i].z, ss[i].z, ss[i].z, ss[i].n_video,
-                               ss[i].n_audio, ss[i].h[0]};
-  }
-  L.slab_total = off;
-  size_t step_bytes = 0;
-  plan_steps(L.steps.data(), n, false, L.plans, &step_bytes);
-  L.bytes = L.slab_total + step_bytes;
+static std::vector<SolverUnit> qkv_units(const fmd_unit_qkv_io* ss, int n) {
+  std::vector<SolverUnit> us(n);
+  for (int i = 0; i < n; ++i)
+    us[i] = SolverUnit{{ss[i].cache, nullptr}, {ss[i].slice_tokens, 0}, ss[i].z, ss[i].n_video,
+                       ss[i].n_audio, ss[i].h, 1.f};
+  return us;
 }
 
 int fmd_unit_qkv_workspace_bytes(const fmd_unit_qkv_io* sessions, int32_t n_sessions,
@@ -713,8 +868,8 @@ int fmd_unit_qkv_workspace_bytes(const fmd_unit_qkv_io* sessions, int32_t n_sess
   if (!out_bytes) return fail(FMD_E_INVAL, "out_bytes is NULL");
   int rc = validate_unit_qkv(sessions, n_sessions, 1);
   if (rc) return rc;
-  QkvLayout L;
-  layout_unit_qkv(sessions, n_sessions, L);
+  SolverLayout L;
+  layout_solver(qkv_units(sessions, n_sessions), 1, L);
   *out_bytes = L.bytes;
   return FMD_OK;
 }
@@ -727,87 +882,104 @@ int fmd_denoise_unit_qkv(fmd_unit_qkv_io* sessions, int32_t n_sessions, int32_t 
   if (rc) return rc;
   if ((rc = check_tensor(w_qkv, 0, "w_qkv"))) return rc;
   if ((rc = check_tensor(w_o, 0, "w_o"))) return rc;
-  QkvLayout L;
-  layout_unit_qkv(sessions, n_sessions, L);
+  const std::vector<SolverUnit> us = qkv_units(sessions, n_sessions);
+  SolverLayout L;
+  layout_solver(us, 1, L);
   if ((rc = check_workspace(workspace, workspace_bytes, L.bytes))) return rc;
 
   hipStream_t st = static_cast<hipStream_t>(stream);
-  char* ws = static_cast<char*>(workspace);
-  const int H = sessions[0].cache->n_heads, hd = sessions[0].cache->head_dim;
-  const int d = H * hd;
-  std::vector<bf16*> zb(n_sessions), q(n_sessions), k(n_sessions), v(n_sessions);
-  for (int i = 0; i < n_sessions; ++i) {
-    const int n_q = sessions[i].n_video + sessions[i].n_audio;
-    const size_t slab = align256((size_t)n_q * d * 2);
-    zb[i] = reinterpret_cast<bf16*>(ws + L.off[i]);
-    q[i] = reinterpret_cast<bf16*>(ws + L.off[i] + slab);
-    k[i] = reinterpret_cast<bf16*>(ws + L.off[i] + 2 * slab);
-    v[i] = reinterpret_cast<bf16*>(ws + L.off[i] + 3 * slab);
-  }
-
   std::vector<fmd_kv_cache*> caches;
   std::vector<const void*> ks, vs;
   std::vector<int64_t> ts;
   for (int i = 0; i < n_sessions; ++i) {
-    if (sessions[i].slice_tokens > 0) {
-      caches.push_back(sessions[i].cache);
-      ks.push_back(sessions[i].k_slice);
-      vs.push_back(sessions[i].v_slice);
-      ts.push_back(sessions[i].slice_tokens);
-    }
+    caches.push_back(sessions[i].cache);
+    ks.push_back(sessions[i].k_slice);
+    vs.push_back(sessions[i].v_slice);
+    ts.push_back(sessions[i].slice_tokens);
   }
-  if (!caches.empty() &&
-      (rc = enqueue_appends(caches.data(), ks.data(), vs.data(), ts.data(), (int)caches.size(), st)))
-    return rc;
+  if ((rc = enqueue_unit_appends(caches, ks, vs, ts, st))) return rc;
+  return run_solver(us, 1, n_steps, w_qkv, w_o, static_cast<char*>(workspace), L, st);
+}
 
-  for (int c0 = 0; c0 < n_sessions; c0 += kMaxSessPerLaunch) {
-    const int cn = std::min(kMaxSessPerLaunch, n_sessions - c0);
-    CvtArgs ca = {};
-    ca.n_sess = cn;
-    for (int j = 0; j < cn; ++j) {
-      const int i = c0 + j;
-      const int64_t ne = (int64_t)(sessions[i].n_video + sessions[i].n_audio) * d;
-      ca.s[j] = CvtSess{sessions[i].z, zb[i], ne, ca.items};
-      ca.items += ne / 8;
+// ---------------------------------------------------------------------------
+// The classifier-free-guided solver: two branches per unit.
+// ---------------------------------------------------------------------------
+static int validate_unit_cfg(const fmd_unit_cfg_io* ss, int n, int n_steps) {
+  if (!ss) return fail(FMD_E_INVAL, "sessions is NULL");
+  if (n < 1 || n > FMD_MAX_SESSIONS / 2)
+    return fail(FMD_E_INVAL, "n_sessions=%d (must be 1..%d)", n, FMD_MAX_SESSIONS / 2);
+  if (n_steps < 1) return fail(FMD_E_INVAL, "n_steps=%d (must be >= 1)", n_steps);
+  int rc;
+  for (int i = 0; i < n; ++i) {
+    const fmd_unit_cfg_io& s = ss[i];
+    const fmd_kv_cache* cs[2] = {s.cond, s.uncond};
+    for (int b = 0; b < 2; ++b) {
+      if ((rc = check_cache(cs[b], i))) return rc;
+      if ((rc = check_same_shape(ss[0].cond, cs[b], i))) return rc;
+      for (int j = 0; j <= i; ++j)
+        for (int c = 0; c < 2; ++c)
+          if ((j < i || c < b) && (c ? ss[j].uncond : ss[j].cond) == cs[b])
+            return fail(FMD_E_INVAL, "session %d: a cache appears twice", i);
     }
-    if ((rc = timed_launch(FMD_KERNEL_CVT, st, [&] { return launch_cvt(ca, st); }))) return rc;
-  }
-
-  char* step_ws = ws + L.slab_total;
-  for (int s = 0; s < n_steps; ++s) {
-    for (int c0 = 0; c0 < n_sessions; c0 += kMaxSessPerLaunch) {
-      const int cn = std::min(kMaxSessPerLaunch, n_sessions - c0);
-      ProjArgs pa = {};
-      pa.n_sess = cn;
-      pa.d = d;
-      pa.n_out = 3 * d;
-      pa.w = static_cast<const bf16*>(w_qkv);
-      const int ntiles = (3 * d + kProjTileN - 1) / kProjTileN;
-      for (int j = 0; j < cn; ++j) {
-        const int i = c0 + j;
-        const int n_q = sessions[i].n_video + sessions[i].n_audio;
-        const int mtiles = (n_q + kProjTile - 1) / kProjTile;
-        pa.s[j] = ProjSess{zb[i], nullptr, nullptr, {q[i], k[i], v[i]}, n_q, mtiles, pa.items,
-                           0.f};
-        pa.items += mtiles * ntiles;
-      }
-      if ((rc = timed_launch(FMD_KERNEL_QKV, st, [&] { return launch_proj(pa, kProjQkv, st); })))
-        return rc;
-    }
-    for (int i = 0; i < n_sessions; ++i) {
-      L.steps[i].cache = sessions[i].cache;   // now in its post-append state
-      L.steps[i].q = q[i];
-      L.steps[i].k_u = k[i];
-      L.steps[i].v_u = v[i];
-      L.steps[i].z = sessions[i].z;
-      L.steps[i].h = sessions[i].h[s];
-    }
-    // The last step needs no bf16 copy of its result.
-    if ((rc = enqueue_steps(L.steps.data(), n_sessions, L.plans, w_o, step_ws, nullptr, st,
-                            s + 1 < n_steps ? zb.data() : nullptr)))
+    if ((rc = check_unit_slice(s.cond, s.cond_k_slice, s.cond_v_slice, s.cond_slice_tokens, i)))
       return rc;
+    if ((rc = check_unit_slice(s.uncond, s.uncond_k_slice, s.uncond_v_slice,
+                               s.uncond_slice_tokens, i)))
+      return rc;
+    if ((rc = check_unit_latent(s.z, s.n_video, s.n_audio, s.h, n_steps, i))) return rc;
+    if (!isfinite(s.guidance))
+      return fail(FMD_E_INVAL, "session %d: guidance %g is not finite", i, s.guidance);
   }
   return FMD_OK;
+}
+
+static std::vector<SolverUnit> cfg_units(const fmd_unit_cfg_io* ss, int n) {
+  std::vector<SolverUnit> us(n);
+  for (int i = 0; i < n; ++i)
+    us[i] = SolverUnit{{ss[i].cond, ss[i].uncond},
+                       {ss[i].cond_slice_tokens, ss[i].uncond_slice_tokens},
+                       ss[i].z, ss[i].n_video, ss[i].n_audio, ss[i].h, ss[i].guidance};
+  return us;
+}
+
+int fmd_unit_cfg_workspace_bytes(const fmd_unit_cfg_io* sessions, int32_t n_sessions,
+                                 size_t* out_bytes) {
+  g_last_error.clear();
+  if (!out_bytes) return fail(FMD_E_INVAL, "out_bytes is NULL");
+  int rc = validate_unit_cfg(sessions, n_sessions, 1);
+  if (rc) return rc;
+  SolverLayout L;
+  layout_solver(cfg_units(sessions, n_sessions), 2, L);
+  *out_bytes = L.bytes;
+  return FMD_OK;
+}
+
+int fmd_denoise_unit_cfg(fmd_unit_cfg_io* sessions, int32_t n_sessions, int32_t n_steps,
+                         const void* w_qkv, const void* w_o, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  g_last_error.clear();
+  int rc = validate_unit_cfg(sessions, n_sessions, n_steps);
+  if (rc) return rc;
+  if ((rc = check_tensor(w_qkv, 0, "w_qkv"))) return rc;
+  if ((rc = check_tensor(w_o, 0, "w_o"))) return rc;
+  const std::vector<SolverUnit> us = cfg_units(sessions, n_sessions);
+  SolverLayout L;
+  layout_solver(us, 2, L);
+  if ((rc = check_workspace(workspace, workspace_bytes, L.bytes))) return rc;
+
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  std::vector<fmd_kv_cache*> caches;
+  std::vector<const void*> ks, vs;
+  std::vector<int64_t> ts;
+  for (int i = 0; i < n_sessions; ++i) {
+    const fmd_unit_cfg_io& s = sessions[i];
+    caches.insert(caches.end(), {s.cond, s.uncond});
+    ks.insert(ks.end(), {s.cond_k_slice, s.uncond_k_slice});
+    vs.insert(vs.end(), {s.cond_v_slice, s.uncond_v_slice});
+    ts.insert(ts.end(), {s.cond_slice_tokens, s.uncond_slice_tokens});
+  }
+  if ((rc = enqueue_unit_appends(caches, ks, vs, ts, st))) return rc;
+  return run_solver(us, 2, n_steps, w_qkv, w_o, static_cast<char*>(workspace), L, st);
 }
 
 int fmd_profile_enable(int enable) {

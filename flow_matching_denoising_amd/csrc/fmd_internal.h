@@ -171,6 +171,21 @@ struct CvtArgs {
   int64_t items;      // 8-element groups in total
 };
 
+// Classifier-free-guided mix of a unit's two attention outputs, in place into
+// the conditional one: oc = bf16((1 - g) ou + g oc), [n_q][d] per unit.
+struct MixSess {
+  bf16* oc;
+  const bf16* ou;
+  float g;
+  int64_t n;          // elements (n_q * d), a multiple of 8
+  int64_t item0;      // first 8-element group of this unit
+};
+struct MixArgs {
+  MixSess s[kMaxSessPerLaunch];
+  int32_t n_sess;
+  int64_t items;
+};
+
 // Host-side launchers (defined next to their kernels).
 hipError_t launch_append(const AppendArgs& a, int head_dim, hipStream_t st);
 hipError_t launch_vt(const VtArgs& a, int head_dim, hipStream_t st);
@@ -178,6 +193,7 @@ hipError_t launch_attn(const AttnArgs& a, int head_dim, hipStream_t st);
 hipError_t launch_combine(const CombineArgs& a, int head_dim, hipStream_t st);
 hipError_t launch_proj(const ProjArgs& a, int mode, hipStream_t st);
 hipError_t launch_cvt(const CvtArgs& a, hipStream_t st);
+hipError_t launch_mix(const MixArgs& a, hipStream_t st);
 
 // Attention tiling shared by host planning and the kernel.
 constexpr int kAttnWaves = 8;

@@ -274,6 +274,27 @@ __global__ __launch_bounds__(256) void cvt_kernel(CvtArgs a) {
   *reinterpret_cast<bf16x8*>(s.zb + e) = y;
 }
 
+// The guided velocity v_u + g (v_c - v_u) of two branches that share W_o is
+// ((1 - g) O_u + g O_c) W_o^T, so the branches are mixed before the one
+// projection.  (1 - g) ou + g oc keeps g = 1 and g = 0 exact.
+__global__ __launch_bounds__(256) void mix_kernel(MixArgs a) {
+  const int64_t grp = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (grp >= a.items) return;
+  int si = 0;
+#pragma unroll
+  for (int i = 1; i < kMaxSessPerLaunch; ++i)
+    if (i < a.n_sess && grp >= a.s[i].item0) si = i;
+  const MixSess& s = a.s[si];
+  const int64_t e = (grp - s.item0) * 8;
+  const bf16x8 c = *reinterpret_cast<const bf16x8*>(s.oc + e);
+  const bf16x8 u = *reinterpret_cast<const bf16x8*>(s.ou + e);
+  const float g = s.g, g1 = 1.f - s.g;
+  bf16x8 y;
+#pragma unroll
+  for (int t = 0; t < 8; ++t) y[t] = (bf16)fmaf(g, (float)c[t], g1 * (float)u[t]);
+  *reinterpret_cast<bf16x8*>(s.oc + e) = y;
+}
+
 hipError_t launch_proj(const ProjArgs& a, int mode, hipStream_t st) {
   if (a.items <= 0) return hipSuccess;
   static const hipError_t attr_err = [] {
@@ -295,6 +316,12 @@ hipError_t launch_proj(const ProjArgs& a, int mode, hipStream_t st) {
 hipError_t launch_cvt(const CvtArgs& a, hipStream_t st) {
   if (a.items <= 0) return hipSuccess;
   hipLaunchKernelGGL(cvt_kernel, dim3((unsigned)((a.items + 255) / 256)), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_mix(const MixArgs& a, hipStream_t st) {
+  if (a.items <= 0) return hipSuccess;
+  hipLaunchKernelGGL(mix_kernel, dim3((unsigned)((a.items + 255) / 256)), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 

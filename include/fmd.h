@@ -222,6 +222,60 @@ int fmd_denoise_unit_qkv(fmd_unit_qkv_io* sessions, int32_t n_sessions, int32_t 
                          const void* w_qkv, const void* w_o, void* workspace,
                          size_t workspace_bytes, void* stream);
 
+/*
+ * The classifier-free-guided form of the z-dependent solver, as the teacher
+ * samples: the deployed few-step performer is distilled from a stronger
+ * teacher that uses classifier-free guidance and more solver steps
+ * [Wan-Streamer (gongshangzheng blog), training stages, Stage 3 低延迟蒸馏].
+ * Each unit has two branches that differ only in the clean context their
+ * attention reads: a conditional cache and an unconditional cache.  Per step
+ * s, for every unit:
+ *   [Q | K_u | V_u] from bf16(z) as in fmd_denoise_unit_qkv (shared by both
+ *       branches);
+ *   O_c, O_u = attention of those queries over [valid ring ; unit tokens] of
+ *       the conditional and of the unconditional cache;
+ *   v = v_u + g (v_c - v_u) with v_b = O_b W_o^T, computed as
+ *       bf16((1 - g) O_u + g O_c) W_o^T (one projection; g = 1 gives the
+ *       conditional branch alone, g = 0 the unconditional one);
+ *   z <- z - h[s] v.
+ * One unit's inputs:
+ *   cond, uncond   : the two branches' rings (state before the appends;
+ *                    updated); distinct caches of one shape
+ *   cond_/uncond_  : bf16 [slice_tokens][n_heads][head_dim] slices appended to
+ *     k/v_slice      the respective ring first; 0 tokens = no append
+ *   z              : fp32 [n_q][d], eps on entry, the final latent on exit
+ *   h              : HOST array [n_steps] of positive step sizes
+ *   guidance       : the guidance scale g (finite; any sign)
+ */
+typedef struct fmd_unit_cfg_io {
+  fmd_kv_cache* cond;
+  fmd_kv_cache* uncond;
+  const void* cond_k_slice;
+  const void* cond_v_slice;
+  int64_t cond_slice_tokens;
+  const void* uncond_k_slice;
+  const void* uncond_v_slice;
+  int64_t uncond_slice_tokens;
+  float* z;
+  int32_t n_video;
+  int32_t n_audio;
+  const float* h;
+  float guidance;
+} fmd_unit_cfg_io;
+
+/* Workspace bytes fmd_denoise_unit_cfg needs (pure host arithmetic). */
+int fmd_unit_cfg_workspace_bytes(const fmd_unit_cfg_io* sessions, int32_t n_sessions,
+                                 size_t* out_bytes);
+
+/* One denoised unit of the guided solver for n_sessions units (1 ..
+ * FMD_MAX_SESSIONS / 2): one batched append of every slice, then n_steps
+ * steps as above.  w_qkv: bf16 [3d][d]; w_o: bf16 [d][d].  Errors: as
+ * fmd_denoise_unit_qkv; a cache used twice or a non-finite guidance scale ->
+ * FMD_E_INVAL.  Nothing is enqueued when an error is returned. */
+int fmd_denoise_unit_cfg(fmd_unit_cfg_io* sessions, int32_t n_sessions, int32_t n_steps,
+                         const void* w_qkv, const void* w_o, void* workspace,
+                         size_t workspace_bytes, void* stream);
+
 /* Static description of a status code (never NULL). */
 const char* fmd_strerror(int status);
 
@@ -237,7 +291,8 @@ enum {
   FMD_KERNEL_PROJ = 4,      /* projection GEMM with the Euler update */
   FMD_KERNEL_QKV = 5,       /* projection of the latent to Q, K_u, V_u */
   FMD_KERNEL_CVT = 6,       /* bf16 copy of the starting latent */
-  FMD_KERNEL_COUNT = 7
+  FMD_KERNEL_MIX = 7,       /* guided mix of the two branches' outputs */
+  FMD_KERNEL_COUNT = 8
 };
 
 /* Per-launch timing with HIP events recorded on the launch stream around

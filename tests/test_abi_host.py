@@ -217,3 +217,55 @@ def test_unit_qkv_workspace_holds_projections_and_step():
     _, step = _ws([_step(c, 920, 8)])
     # bf16 z, Q, K_u, V_u (4 x 928 x 5120 bf16) on top of the step workspace.
     assert out.value >= step + 4 * 928 * 5120 * 2
+
+
+def _cfg_io(cond, uncond, h, g=5.0, ct=32, ut=0, z=FAKE):
+    from flow_matching_denoising_amd import _UnitCfgIO
+    return _UnitCfgIO(ctypes.pointer(cond), ctypes.pointer(uncond), FAKE, FAKE, ct, FAKE, FAKE,
+                      ut, z, 12, 4, ctypes.cast(h, ctypes.POINTER(ctypes.c_float)), g)
+
+
+def test_denoise_unit_cfg_validation_leaves_state():
+    from flow_matching_denoising_amd import _UnitCfgIO
+    a, b, c = _cache(), _cache(), _cache()
+    h = (ctypes.c_float * 2)(0.5, 0.5)
+    run = fmd._denoise_unit_cfg
+
+    def call(ios, n_steps=2, wq=FAKE, ws=1 << 30):
+        arr = (_UnitCfgIO * len(ios))(*ios)
+        return run(arr, len(ios), n_steps, wq, FAKE, FAKE, ws, None)
+    assert call([_cfg_io(a, a, h)]) == -1                      # same cache for both branches
+    assert call([_cfg_io(a, b, h), _cfg_io(c, a, h)]) == -1    # cache shared across units
+    assert call([_cfg_io(a, b, h, g=float("nan"))]) == -1      # guidance not finite
+    assert call([_cfg_io(a, b, h, g=float("inf"))]) == -1
+    assert call([_cfg_io(a, b, h, ct=200)]) == -3              # slice > cap
+    assert call([_cfg_io(a, b, h, ut=-1)]) == -1               # negative slice
+    assert call([_cfg_io(a, _cache(H=3), h)]) == -2            # branch shapes differ
+    assert call([_cfg_io(a, b, h, z=0)]) == -1                 # no z
+    assert call([_cfg_io(a, b, h)], n_steps=0) == -1
+    assert call([_cfg_io(a, b, h)], wq=0) == -1                # no W_qkv
+    assert call([_cfg_io(a, b, h)], ws=16) == -5               # workspace too small
+    many = [_cache() for _ in range(66)]
+    assert call([_cfg_io(many[2 * i], many[2 * i + 1], h) for i in range(33)]) == -1
+    h[1] = -0.5
+    assert call([_cfg_io(a, b, h)]) == -1                      # h[1] < 0
+    for x in (a, b, c):
+        assert (x.len_tokens, x.head_tokens) == (96, 96)
+
+
+def test_unit_cfg_workspace_holds_both_branches():
+    from flow_matching_denoising_amd import _UnitCfgIO, _UnitQkvIO
+    a = _cache(H=40, hd=128, cap=60416, ln=60416, head=0)
+    b = _cache(H=40, hd=128, cap=60416, ln=60416, head=0)
+    h = (ctypes.c_float * 1)(1.0)
+    io = _cfg_io(a, b, h, ct=0)
+    io.n_video, io.n_audio = 920, 8
+    out = ctypes.c_size_t(0)
+    assert fmd._unit_cfg_workspace_bytes((_UnitCfgIO * 1)(io), 1, ctypes.byref(out)) == 0
+    qio = _UnitQkvIO(ctypes.pointer(a), 0, 0, 0, FAKE, 920, 8,
+                     ctypes.cast(h, ctypes.POINTER(ctypes.c_float)))
+    q = ctypes.c_size_t(0)
+    assert fmd._unit_qkv_workspace_bytes((_UnitQkvIO * 1)(qio), 1, ctypes.byref(q)) == 0
+    # A second attention output (928 x 5120 bf16) and staging on top of the
+    # single-branch workspace.
+    assert out.value >= q.value + 928 * 5120 * 2

@@ -16,7 +16,10 @@ for the thinker's K/V and the VAE latents at the pages' shapes):
   (the projection weight is scaled by ``d**-0.5`` before rounding, i.e. its
   variance is ``1/d``); the start latent ``eps`` stays float32;
 * ring slots that are not valid before the append may be filled with a bf16 NaN
-  (``0x7FC0``) so that any read of them shows in the output.
+  (``0x7FC0``) so that any read of them shows in the output;
+* a guided unit's unconditional branch has the conditional branch's shapes
+  and ring state, its ring and slice drawn from streams of their own
+  (``uncond_*`` tensor ids).
 
 Shapes follow the two resolutions the pages name (192x336 and 640x368 at 25 FPS,
 160 ms units) with the token-count assumptions stated beside each workload.
@@ -35,7 +38,12 @@ BF16_NAN = np.uint16(0x7FC0)
 _TENSOR_IDS = {
     "ring_k": 1, "ring_v": 2, "slice_k": 3, "slice_v": 4,
     "q": 5, "k_u": 6, "v_u": 7, "eps": 8, "z0": 9, "w_o": 10, "w_qkv": 11,
+    "uncond_ring_k": 12, "uncond_ring_v": 13, "uncond_slice_k": 14, "uncond_slice_v": 15,
 }
+
+# Guidance scale of the guided (teacher) sampler's workloads.  The pages give
+# none; the cost of a step does not depend on it.
+CFG_GUIDANCE = 5.0
 
 
 def _threads() -> int:
@@ -198,6 +206,12 @@ def _build():
         "640x368-class unit against a 256-unit ring (241,664 keys) that has "
         "wrapped, append offset 100 units, 4 steps of 0.25",
         3, (_unit_session(40, 128, 920, 8, 944, 256, 256, 100, (0.25,) * 4),))
+    w["v02_cfg_unit"] = Workload(
+        "v02_cfg_unit",
+        "640x368-class unit sampled by the guided teacher: conditional and "
+        "unconditional 64-unit rings of 944-token slices (60,416 keys each) filled "
+        "by this unit's appends, 16 steps of 1/16, guidance scale 5",
+        5, (_unit_session(40, 128, 920, 8, 944, 64, 63, 63, (1.0 / 16,) * 16),))
     w["v02_batch8"] = Workload(
         "v02_batch8",
         "8 independent 640x368-class sessions, full rings of 8..128 units of 944 "
@@ -220,7 +234,7 @@ def get(name: str) -> Workload:
 
 def ring_logical(seed, session, s: SessionShape, which: str, poison_invalid=False):
     """Ring content in logical layout [H][cap][hd] (bf16 bits)."""
-    assert which in ("ring_k", "ring_v")
+    assert which in ("ring_k", "ring_v", "uncond_ring_k", "uncond_ring_v")
 
     def one(h):
         return round_to_bf16_bits(
@@ -321,6 +335,28 @@ def make_inputs(wl: Workload, poison_invalid=False, reuse_step_inputs=False,
         si_in.eps = latent(seed, si, s, "eps")
         out.append(si_in)
     return UnitInputs(wl, out, projection_weight(seed, wl.d, wl.head_dim))
+
+
+@dataclass
+class BranchInputs:
+    """The unconditional branch of a guided unit: ring before the append and
+    the slice appended to it (same shapes as the conditional branch)."""
+    ring_k: np.ndarray
+    ring_v: np.ndarray
+    slice_k: np.ndarray | None
+    slice_v: np.ndarray | None
+
+
+def uncond_inputs(wl: Workload, session: int, poison_invalid=False) -> BranchInputs:
+    s = wl.sessions[session]
+    rk = ring_logical(wl.seed, session, s, "uncond_ring_k", poison_invalid)
+    rv = ring_logical(wl.seed, session, s, "uncond_ring_v", poison_invalid)
+    if s.slice_tokens:
+        sk = token_major(wl.seed, session, s, "uncond_slice_k", s.slice_tokens)
+        sv = token_major(wl.seed, session, s, "uncond_slice_v", s.slice_tokens)
+    else:
+        sk = sv = None
+    return BranchInputs(rk, rv, sk, sv)
 
 
 def custom_session(n_heads, head_dim, n_video, n_audio, slice_tokens, cap_tokens,
