@@ -48,6 +48,8 @@ def _args():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="v02_unit")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-probes", action="store_true",
+                    help="skip the z-dependent, guided and batched-append probes")
     ap.add_argument("--quiet", action="store_true")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="only run a plain device-to-device copy of BYTES bytes (three "
@@ -79,12 +81,15 @@ def _log(args, *a):
         print(*a, file=sys.stderr, flush=True)
 
 
-def _attn_traffic():
+def _attn_traffic(workload_name):
     """HBM bytes per attention launch from committed rocprofv3 counter runs,
-    valid only while attention.hip is unchanged since they were taken."""
+    valid only for the workload they were taken on and while attention.hip is
+    unchanged since then."""
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
+        if t.get("workload", "").split(" ")[0] != workload_name:
+            return None
         with open(ATTN_SRC, "rb") as f:
             h = hashlib.sha256(f.read()).hexdigest()
         if t.get("attention_hip_sha256") != h:
@@ -338,12 +343,19 @@ def main():
     torch.cuda.synchronize()
 
     fmd.profile_enable(True)
+    # One pair of events per unit on the launch stream: the per-unit median
+    # and p90 beside the wall-clock mean.
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(args.steps):
+    for a, b in evs:
+        a.record()
         one_unit()
+        b.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    unit_ms = sorted(a.elapsed_time(b) for a, b in evs)
     kt = {k: fmd.profile_read(k) for k in fmd.KERNEL_CLASSES}
     fmd.profile_enable(False)
 
@@ -354,7 +366,7 @@ def main():
     attn_avg_s = attn_ms / attn_n / 1e3
     attn_flops_launch = wl.attention_flops_per_step()    # one launch covers all sessions of a step
     attn_tflops = attn_flops_launch / attn_avg_s / 1e12
-    traffic = _attn_traffic()
+    traffic = _attn_traffic(wl.name)
     per_kernel_us = {k: (v[0] / v[1] * 1e3 if v[1] else None) for k, v in kt.items()}
     app_ms, app_n = kt["append"]
     append_gbs = wl.append_bytes() / (app_ms / app_n / 1e3) / 1e9 if app_n else None
@@ -400,13 +412,16 @@ def main():
         "append_frac_hbm": round(append_gbs / HBM_PEAK_GBS, 4) if append_gbs else None,
         "proj_TFLOPs": round(proj_tflops, 1) if proj_tflops else None,
         "unit_layers_per_160ms": round(UNIT_BUDGET_S / (ms_per_step / 1e3 / n_sess), 2),
+        "step_ms_median": round(unit_ms[len(unit_ms) // 2], 4),
+        "step_ms_p90": round(unit_ms[min(len(unit_ms) - 1, (9 * len(unit_ms)) // 10)], 4),
     }
-    out["qkv_unit"] = qkv_unit_probe(wl, ui, caches, states, w_o)
-    del caches, ios
-    torch.cuda.empty_cache()
-    out["cfg_unit"] = cfg_unit_probe()
-    torch.cuda.empty_cache()
-    out["append_batch8"] = append_batch_probe()
+    if not args.no_probes:
+        out["qkv_unit"] = qkv_unit_probe(wl, ui, caches, states, w_o)
+        del caches, ios
+        torch.cuda.empty_cache()
+        out["cfg_unit"] = cfg_unit_probe()
+        torch.cuda.empty_cache()
+        out["append_batch8"] = append_batch_probe()
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, ui, args)
     print(json.dumps(out), flush=True)

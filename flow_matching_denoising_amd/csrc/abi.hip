@@ -12,6 +12,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <functional>
 #include <mutex>
 #include <string>
 #include <vector>
@@ -206,12 +207,13 @@ int env_int(const char* name, int dflt) {
   return atoi(v);
 }
 
-// Key splits.  Work items of one launch are dispatched to the CUs in rounds;
-// with items of about equal length, a launch whose item count is a multiple
-// of the CU count leaves no CU idle in its last round.  The item size is
-// chosen among candidates of 1..16 rounds (at least kMinWindows windows per
-// item) by that round efficiency, with a small penalty per split for the
-// combine pass, which reads every split's partial output once.  Depends only
+// Key splits.  The item size (64-key windows per work item) trades the
+// dispatch tail against the combine pass, which reads every split's partial
+// output once.  Candidates of 1..40 dispatch rounds are scored with a model of
+// the launch: every XCD takes an equal contiguous range of the head-major item
+// order (xcd_remap), and its 32 CUs take the range's items in order, each the
+// next free CU (greedy list scheduling); the score is that range's finish time
+// plus the combine work, both in units of one window of one item.  Depends only
 // on the shapes.  FMD_ATTN_SPLIT forces a split count per session,
 // FMD_ATTN_TARGET_ITEMS a target item count (both for experiments).
 int plan_split_count(const SessPlan& p, double per_item) {
@@ -219,6 +221,52 @@ int plan_split_count(const SessPlan& p, double per_item) {
   int ns = (int)ceil(p.nwin_total / (per_item > 1 ? per_item : 1.0));
   ns = std::min(ns, std::max(1, p.nwin_total / kMinWindows));
   return std::max(1, std::min(ns, p.nwin_total));
+}
+
+// Windows of split `split` of a session (as the kernel divides them).
+int split_windows(const SessPlan& p, int split) {
+  const int sg = split >= p.split0[2] ? 2 : (split >= p.split0[1] ? 1 : 0);
+  const int ns = p.split0[sg + 1] - p.split0[sg], ls = split - p.split0[sg];
+  return (ls + 1) * p.nwin[sg] / ns - ls * p.nwin[sg] / ns;
+}
+
+// Order of a launch's sessions inside each head's items: longest ring item
+// first, so each XCD ends its range on short items.
+void session_order(const SessPlan* plans, int n, int* order) {
+  std::vector<double> len(n);
+  for (int k = 0; k < n; ++k) {
+    const SessPlan& p = plans[k];
+    order[k] = k;
+    len[k] = p.split0[2] > 0 ? (double)(p.nwin[0] + p.nwin[1]) / p.split0[2] : p.nwin[2];
+  }
+  std::stable_sort(order, order + n, [&](int x, int y) { return len[x] > len[y]; });
+}
+
+double score_plan(const std::vector<SessPlan>& plans, int H) {
+  constexpr double kItemOverhead = 2.0;   // Q load, pipeline fill, O/LSE store
+  constexpr double kCombinePerSplit = 1.3;   // per split of a 928-query session
+  std::vector<int> seq;   // windows of one head's items, launch order
+  double combine = 0;
+  for (size_t c0 = 0; c0 < plans.size(); c0 += kMaxSessPerLaunch) {
+    const int cn = (int)std::min<size_t>(kMaxSessPerLaunch, plans.size() - c0);
+    int order[kMaxSessPerLaunch];
+    session_order(plans.data() + c0, cn, order);
+    for (int j = 0; j < cn; ++j) {
+      const SessPlan& p = plans[c0 + order[j]];
+      for (int sp = 0; sp < p.nsplit; ++sp) seq.insert(seq.end(), p.n_qblk, split_windows(p, sp));
+      if (p.nsplit > 1) combine += kCombinePerSplit * p.nsplit * p.n_q / 928.0;
+    }
+  }
+  const int cus = kTargetCUs / kNumXcd;
+  const int64_t n = (int64_t)H * seq.size();
+  const int64_t range = (n + kNumXcd - 1) / kNumXcd;   // XCD 0's range
+  std::vector<double> cu(cus, 0.0);                      // min-heap of finish times
+  for (int64_t i = 0; i < range; ++i) {
+    std::pop_heap(cu.begin(), cu.end(), std::greater<double>());
+    cu.back() += seq[i % seq.size()] + kItemOverhead;
+    std::push_heap(cu.begin(), cu.end(), std::greater<double>());
+  }
+  return *std::max_element(cu.begin(), cu.end()) + combine;
 }
 
 void choose_splits(std::vector<SessPlan>& plans, int H) {
@@ -230,22 +278,12 @@ void choose_splits(std::vector<SessPlan>& plans, int H) {
   double work = 0;
   for (auto& p : plans) work += (double)H * p.n_qblk * p.nwin_total;
   const int target_env = env_int("FMD_ATTN_TARGET_ITEMS", 0);
-  double best_cost = 1e30, best_per_item = work;
-  for (int rounds = 1; rounds <= 16; ++rounds) {
+  double best_cost = 1e300, best_per_item = work;
+  for (int rounds = 1; rounds <= 40; ++rounds) {
     const int target = target_env > 0 ? target_env : rounds * kTargetCUs;
     const double per_item = work / target;
-    // Ring-segment items are the long ones (the unit's own keys are a
-    // short segment of their own); count their rounds.
-    double long_items = 0, split_sum = 0;
-    for (auto& p : plans) {
-      SessPlan q = p;
-      set_splits(q, plan_split_count(p, per_item));
-      long_items += (double)H * p.n_qblk * q.split0[2];
-      split_sum += q.nsplit;
-    }
-    const double r = long_items / kTargetCUs;
-    const double eff = r > 0 ? r / ceil(r) : 1.0;
-    const double cost = 1.0 / eff + 0.004 * split_sum / plans.size();
+    for (auto& p : plans) set_splits(p, plan_split_count(p, per_item));
+    const double cost = score_plan(plans, H);
     if (cost < best_cost - 1e-9) {
       best_cost = cost;
       best_per_item = per_item;
@@ -344,6 +382,7 @@ int enqueue_steps(const fmd_unit_step* units, int n, const std::vector<SessPlan>
     pa.w = static_cast<const bf16*>(w_o);
     bool any_split = false;
     bf16* o_prev = nullptr;
+    AttnSess asess[kMaxSessPerLaunch];
     for (int k = 0; k < cn; ++k) {
       const fmd_unit_step& u = units[c0 + k];
       const SessPlan& p = plans[c0 + k];
@@ -363,7 +402,7 @@ int enqueue_steps(const fmd_unit_step* units, int n, const std::vector<SessPlan>
                        p.n_q, p.npad / 16, va.items, 0};
       if (!second) va.items += H * (p.npad / 16);
 
-      AttnSess& as = aa.s[k];
+      AttnSess& as = asess[k];
       as.q = static_cast<const bf16*>(u.q);
       as.kt_u = kt;
       as.vt_u = vt;
@@ -383,8 +422,6 @@ int enqueue_steps(const fmd_unit_step* units, int n, const std::vector<SessPlan>
       for (int t = 0; t < 4; ++t) as.split0[t] = p.split0[t];
       as.n_qblk = p.n_qblk;
       as.nsplit = p.nsplit;
-      as.item0 = aa.items;
-      aa.items += H * p.nsplit * p.n_qblk;
 
       ca.s[k] = CombineSess{as.opart, as.lse, o, p.n_q, p.nsplit, ca.items, 0};
       if (p.nsplit > 1) {
@@ -405,6 +442,19 @@ int enqueue_steps(const fmd_unit_step* units, int n, const std::vector<SessPlan>
       pa.s[j] = ProjSess{o, u.z, zb_out ? zb_out[unit] : nullptr, {nullptr, nullptr, nullptr},
                          p.n_q, mtiles, pa.items, u.h};
       pa.items += mtiles * ntiles;
+    }
+    // Attention items, head-major over the sessions.  Inside a head the
+    // sessions go longest ring item first, so each XCD ends its range on short
+    // items.
+    {
+      int order[kMaxSessPerLaunch];
+      session_order(plans.data() + c0, cn, order);
+      for (int j = 0; j < cn; ++j) {
+        aa.s[j] = asess[order[j]];
+        aa.s[j].hoff = aa.per_head;
+        aa.per_head += aa.s[j].nsplit * aa.s[j].n_qblk;
+      }
+      aa.items = H * aa.per_head;
     }
     // Sessions without splits take no combine items; the combine kernel finds
     // its session by item0, so give them an empty range at the current end.

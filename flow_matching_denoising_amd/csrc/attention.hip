@@ -261,22 +261,22 @@ void attn_kernel(AttnArgs a) {
   auto kbuf = [&](int i) { return lds + i * T::K_BYTES; };
   auto vbuf = [&](int i) { return lds + T::STAGES * T::K_BYTES + i * T::V_BYTES; };
 
+  // Item order: head, then session, then (split, query block), query block
+  // fastest, so the query blocks sharing one key range are adjacent (same XCD).
   const int item = xcd_remap(blockIdx.x, a.items);
+  const int h = item / a.per_head;
+  const int r = item - h * a.per_head;
   int si = 0;
 #pragma unroll
   for (int i = 1; i < kMaxSessPerLaunch; ++i)
-    if (i < a.n_sess && item >= a.s[i].item0) si = i;
+    if (i < a.n_sess && r >= a.s[i].hoff) si = i;
   const AttnSess& s = a.s[si];
   const int H = a.H;
   const float scale_log2 = a.scale_log2;
 
-  // Item order inside a session: (head, split, query block), query block fastest,
-  // so the query blocks sharing one key range are adjacent (same XCD).
-  int local = item - s.item0;
+  const int local = r - s.hoff;
   const int qblk = local % s.n_qblk;
-  local /= s.n_qblk;
-  const int split = local % s.nsplit;
-  const int h = local / s.nsplit;
+  const int split = local / s.n_qblk;
 
   // The split's segment and window range.
   const int sg = split >= s.split0[2] ? 2 : (split >= s.split0[1] ? 1 : 0);

@@ -104,13 +104,18 @@ struct AttnSess {
   int32_t split0[4];  // key splits of segment t: [split0[t], split0[t+1]); split0[3] = nsplit
   int32_t n_qblk;
   int32_t nsplit;
-  int32_t item0;
+  int32_t hoff;       // first item of this session among one head's items
 };
+// Items are numbered head-major over all sessions of the launch: head h's
+// items are [h * per_head, (h + 1) * per_head), and inside them session i
+// takes [hoff, hoff + nsplit * n_qblk) (hoff increasing with i).  Every XCD's
+// contiguous range of items then holds the same mix of sessions.
 struct AttnArgs {
   AttnSess s[kMaxSessPerLaunch];
   int32_t n_sess;
   int32_t H;
-  int32_t items;
+  int32_t per_head;   // items per head, all sessions
+  int32_t items;      // H * per_head
   float scale_log2;   // log2(e) / sqrt(head_dim)
 };
 
