@@ -44,8 +44,11 @@ ATTN_SRC = os.path.join(ROOT, "flow_matching_denoising_amd", "csrc", "attention.
 def _args():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=40)
+    # Under sustained MFMA load the GPU's clock settles only after a few hundred
+    # ms (the first launches run up to 30 % slower); 60 units of the
+    # 640x368-class workload are about 0.3 s.
+    ap.add_argument("--warmup", type=int, default=60)
     ap.add_argument("--workload", default="v02_unit")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-probes", action="store_true",
@@ -99,7 +102,7 @@ def _attn_traffic(workload_name):
         return None
 
 
-def qkv_unit_probe(wl, ui, caches, states, w_o, units=10, warmup=2):
+def qkv_unit_probe(wl, ui, caches, states, w_o, units=20, warmup=5):
     """The z-dependent solver on the same workload: every step first projects
     the unit's Q, K_u, V_u from the current latent (bf16 [3d][d] weights, one
     GEMM of n_q x 3d x d), then runs the step.  Same rings, same append."""
@@ -145,7 +148,7 @@ def qkv_unit_probe(wl, ui, caches, states, w_o, units=10, warmup=2):
             "qkv_gemm_TFLOPs": round(qkv_flops / (ms / n / 1e3) / 1e12, 1)}
 
 
-def cfg_unit_probe(units=3, warmup=1):
+def cfg_unit_probe(units=4, warmup=2):
     """The guided (teacher) sampler on its 640x368-class workload: conditional
     and unconditional 60,416-key rings, both appended, 16 steps; per step one
     Q/K/V projection, attention over both branches (one launch), the guided
