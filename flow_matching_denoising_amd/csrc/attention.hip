@@ -150,17 +150,20 @@ __device__ __forceinline__ void dma16(const i32x4& rs, int voff, int soff, char*
 // (first and last windows of a segment, which may reach past its storage);
 // the others pass it as the scalar offset.  Scores of keys outside [lo, hi)
 // are masked and their values zeroed in LDS before use.
+// Offsets are 32-bit unsigned byte counts: a window that starts below the
+// segment's end (start * HD * 2 < 2^31) can reach up to 16 KiB past it, which
+// the range check turns into zeros.
 template <int HD, bool CHECKED, int N>
 __device__ __forceinline__ void load_tile(const i32x4& rs, int start, char* dst,
                                           const int (&off)[N], int wave) {
-  const int woff = start * HD * 2;
+  const uint32_t woff = (uint32_t)start * (HD * 2);
 #pragma unroll
   for (int i = 0; i < N; ++i) {
     char* d = dst + (wave + kAttnWaves * i) * 1024;
     if (CHECKED)
-      dma16(rs, off[i] + woff, 0, d);
+      dma16(rs, (int)((uint32_t)off[i] + woff), 0, d);
     else
-      dma16(rs, off[i], woff, d);
+      dma16(rs, off[i], (int)woff, d);
   }
 }
 
