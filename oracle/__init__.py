@@ -28,6 +28,10 @@ sections):
 6. ``cfg.denoise_unit_cfg`` -- the classifier-free-guided sampler of the
    teacher: conditional and unconditional branches, guided velocity
    v_u + g (v_c - v_u) [same page, training stages, Stage 3].
+7. ``ulysses.ulysses_attention`` -- the attention computed over P performer
+   ranks: head-sharded cache, sequence-sharded video rows, all-to-all between
+   sequence and head dimensions, gather [Wan-Streamer v0.2: Higher
+   Resolution, Same Latency (nanless digest), 方法概述和架构].
 
 Everything is float64 unless a function says otherwise.  bf16 inputs arrive as
 uint16 bit patterns and are widened exactly by ``ring.bf16_bits_to_f64``.
@@ -43,3 +47,4 @@ from .attention import attention, attention_naive  # noqa: F401
 from .flow import velocity, euler_step, denoise_step, denoise_unit  # noqa: F401
 from .qkv import round_to_bf16, f64_to_bf16_bits, qkv_projection, denoise_unit_qkv  # noqa: F401
 from .cfg import guided_velocity, denoise_unit_cfg  # noqa: F401
+from .ulysses import ulysses_attention  # noqa: F401
