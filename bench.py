@@ -18,6 +18,8 @@ Prints ONE JSON line (rank 0, N=1).  Besides throughput it reports:
   from the latent at every step);
 * cfg_unit: the guided teacher's sampler (conditional + unconditional rings,
   16 steps, guidance 5) on the 640x368-class unit;
+* ulysses_rank_p8: one rank's attention under 8-way Ulysses context parallel
+  (5 heads, all 928 tokens, the head shard of the ring);
 * append_batch8: the batched ring append at the 8-session shape.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
@@ -212,6 +214,42 @@ def cfg_unit_probe(units=4, warmup=2):
             "attn_TFLOPs": round(attn_flops / (attn_ms / attn_n / 1e3) / 1e12, 1),
             "per_kernel_us": {k: (round(v[0] / v[1] * 1e3, 2) if v[1] else None)
                               for k, v in kt.items()}}
+
+
+def ulysses_rank_probe(P=8, launches=20, warmup=10):
+    """One Ulysses rank's attention at the 640x368-class shape: after the
+    sequence -> head exchange a rank of P holds all 928 tokens for H/P heads
+    and the head shard of the 60,416-key ring.  Contents do not change the
+    work, so the tensors are drawn on the device."""
+    import torch
+
+    import flow_matching_denoising_amd as fmd
+
+    H, hd, cap, n_q, n_audio = 40 // P, 128, 64 * 944, 928, 8
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device=dev).manual_seed(9)
+    rnd = lambda *shape: torch.randn(shape, generator=g, device=dev).to(torch.bfloat16)  # noqa: E731
+    cache = fmd.KVCache(H, hd, cap, device=dev, k=rnd(H, cap, hd),
+                        v=fmd.KVCache.logical_to_device_v(rnd(H, cap, hd)), len_tokens=cap,
+                        head_tokens=63 * 944)
+    unit = fmd.UnitStep(cache, rnd(n_q, H, hd), rnd(n_q, H, hd), rnd(n_q, H, hd), n_audio=n_audio)
+    o = torch.empty((n_q, H, hd), dtype=torch.bfloat16, device=dev)
+    ws = fmd.alloc_workspace(fmd.workspace_bytes([unit]), dev)
+    for _ in range(warmup):
+        fmd.attention([unit], o, ws)
+    torch.cuda.synchronize()
+    fmd.profile_enable(True)
+    for _ in range(launches):
+        fmd.attention([unit], o, ws)
+    torch.cuda.synchronize()
+    ms, n = fmd.profile_read("attn")
+    c_ms, c_n = fmd.profile_read("combine")
+    fmd.profile_enable(False)
+    flops = 4.0 * n_q * (cap + n_q) * H * hd
+    return {"ranks": P, "heads_per_rank": H, "queries": n_q, "keys_per_query": cap + n_q,
+            "attn_us": round(ms / n * 1e3, 2),
+            "attn_TFLOPs": round(flops / (ms / n / 1e3) / 1e12, 1),
+            "combine_us": round(c_ms / c_n * 1e3, 2) if c_n else None}
 
 
 def append_batch_probe(launches=20):
@@ -423,6 +461,8 @@ def main():
         del caches, ios
         torch.cuda.empty_cache()
         out["cfg_unit"] = cfg_unit_probe()
+        torch.cuda.empty_cache()
+        out["ulysses_rank_p8"] = ulysses_rank_probe(8)
         torch.cuda.empty_cache()
         out["append_batch8"] = append_batch_probe()
     if not args.no_cpu_baseline:
