@@ -32,6 +32,9 @@ sections):
    ranks: head-sharded cache, sequence-sharded video rows, all-to-all between
    sequence and head dimensions, gather [Wan-Streamer v0.2: Higher
    Resolution, Same Latency (nanless digest), 方法概述和架构].
+8. ``layers.denoise_unit_layers`` -- the z-dependent solver over a stack of
+   L attention layers with per-layer rings and a residual stream
+   [Wan-Streamer (gongshangzheng blog), 3.3 and 3.4].
 
 Everything is float64 unless a function says otherwise.  bf16 inputs arrive as
 uint16 bit patterns and are widened exactly by ``ring.bf16_bits_to_f64``.
@@ -48,3 +51,4 @@ from .flow import velocity, euler_step, denoise_step, denoise_unit  # noqa: F401
 from .qkv import round_to_bf16, f64_to_bf16_bits, qkv_projection, denoise_unit_qkv  # noqa: F401
 from .cfg import guided_velocity, denoise_unit_cfg  # noqa: F401
 from .ulysses import ulysses_attention  # noqa: F401
+from .layers import layer_stack_velocity, denoise_unit_layers  # noqa: F401

@@ -264,3 +264,61 @@ def check_cfg_mean_decay(unit_cfg_fn, g=4.0, hs=(0.5, 0.5), seed=6, H=2, hd=8, n
     expect = (eps - mean0) + np.prod([1.0 - h for h in hs]) * mean0
     got = unit_cfg_fn(empty, dict(empty), eps, list(hs), g, w, w_o, H)["z"]
     return float(np.max(np.abs(got - expect)))
+
+
+# ---------------------------------------------------------------------------
+# Stack of L attention layers with a residual stream.
+# ---------------------------------------------------------------------------
+def check_layers_uniform_closed_form(unit_layers_fn, hs=(0.5, 0.25), seed=9, H=2, hd=8,
+                                     cap=64, n_q=5):
+    """Every layer has W_q = 0 and W_v = 0: layer l's attention is the plain
+    mean of its own valid ring values and slice over (len_l + T_l + n_q),
+    whatever its input, so v = sum_l mean_l W_o,l^T and z_final = eps -
+    (sum h) v.  The three layers have different rings, states, slices and
+    W_o; nothing is evicted (len + T <= cap).  Returns max |error|."""
+    rng = np.random.default_rng(seed)
+    d = H * hd
+    eps = rng.standard_normal((n_q, d))
+    layers, w_qkv, w_o, v = [], [], [], np.zeros((n_q, d))
+    for length, head, T in ((30, 40, 6), (12, 3, 0), (47, 20, 9)):
+        ring_k = random_bits(rng, (H, cap, hd))
+        ring_v = random_bits(rng, (H, cap, hd))
+        sk = random_bits(rng, (T, H, hd)) if T else None
+        sv = random_bits(rng, (T, H, hd)) if T else None
+        slots = [(head - length + i) % cap for i in range(length)]
+        total = widen(ring_v)[:, slots, :].sum(axis=1)
+        if T:
+            total = total + widen(sv).sum(axis=0)
+        mean = total / (length + T + n_q)
+        w = np.zeros((3 * d, d), dtype=np.uint16)
+        w[d:2 * d] = random_bits(rng, (d, d))
+        wo = random_bits(rng, (d, d), scale=d ** -0.5)
+        v = v + np.tile(mean.reshape(1, d), (n_q, 1)) @ widen(wo).T
+        layers.append(dict(ring_k=ring_k, ring_v=ring_v, length=length, head=head,
+                           slice_k=sk, slice_v=sv))
+        w_qkv.append(w)
+        w_o.append(wo)
+    expect = eps - sum(hs) * v
+    got = unit_layers_fn(layers, eps, list(hs), w_qkv, w_o, H)["z"]
+    return float(np.max(np.abs(got - expect)))
+
+
+def check_layers_residual_chain(unit_layers_fn, hs=(0.25, 0.25), seed=10, H=2, hd=8, n_q=16):
+    """Two layers, empty rings, W_q = W_k = 0, W_v = I, W_o = I: layer 0 sees
+    z and adds mean(z) to every row; layer 1 sees z + mean(z), whose mean is
+    2 mean(z), and adds it; so v = 3 mean(z) (up to bf16 rounding of the layer
+    inputs), deviations from the mean are invariant and the mean decays by
+    (1 - 3h) per step.  Layer 1 fed with z instead of z + r would give (1 - 2h).
+    Returns max |error|."""
+    rng = np.random.default_rng(seed)
+    d = H * hd
+    eps = rng.standard_normal((n_q, d)) + 0.5
+    w = np.zeros((3 * d, d), dtype=np.uint16)
+    w[2 * d:] = bits(np.eye(d))
+    eye = bits(np.eye(d))
+    empty = dict(ring_k=np.zeros((H, 16, hd), dtype=np.uint16),
+                 ring_v=np.zeros((H, 16, hd), dtype=np.uint16), length=0, head=0)
+    mean0 = eps.mean(axis=0, keepdims=True)
+    expect = (eps - mean0) + np.prod([1.0 - 3.0 * h for h in hs]) * mean0
+    got = unit_layers_fn([empty, dict(empty)], eps, list(hs), [w, w], [eye, eye], H)["z"]
+    return float(np.max(np.abs(got - expect)))
