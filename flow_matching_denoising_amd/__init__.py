@@ -80,6 +80,15 @@ class _UnitCfgIO(ctypes.Structure):
                 ("h", ctypes.POINTER(ctypes.c_float)), ("guidance", ctypes.c_float)]
 
 
+class _UnitLayersIO(ctypes.Structure):
+    _fields_ = [("caches", ctypes.POINTER(ctypes.POINTER(_Cache))),
+                ("k_slices", ctypes.POINTER(ctypes.c_void_p)),
+                ("v_slices", ctypes.POINTER(ctypes.c_void_p)),
+                ("slice_tokens", ctypes.c_int64), ("z", ctypes.c_void_p),
+                ("n_video", ctypes.c_int32), ("n_audio", ctypes.c_int32),
+                ("h", ctypes.POINTER(ctypes.c_float))]
+
+
 def _sig(name, restype, *argtypes):
     f = getattr(_lib, name)
     f.restype = restype
@@ -110,6 +119,12 @@ _unit_cfg_workspace_bytes = _sig("fmd_unit_cfg_workspace_bytes", ctypes.c_int,
                                  ctypes.POINTER(_UnitCfgIO), _i32, ctypes.POINTER(_sz))
 _denoise_unit_cfg = _sig("fmd_denoise_unit_cfg", ctypes.c_int, ctypes.POINTER(_UnitCfgIO), _i32,
                          _i32, _vp, _vp, _vp, _sz, _vp)
+_unit_layers_workspace_bytes = _sig("fmd_unit_layers_workspace_bytes", ctypes.c_int,
+                                    ctypes.POINTER(_UnitLayersIO), _i32, _i32,
+                                    ctypes.POINTER(_sz))
+_denoise_unit_layers = _sig("fmd_denoise_unit_layers", ctypes.c_int, ctypes.POINTER(_UnitLayersIO),
+                            _i32, _i32, _i32, ctypes.POINTER(_vp), ctypes.POINTER(_vp), _vp, _sz,
+                            _vp)
 _strerror = _sig("fmd_strerror", ctypes.c_char_p, ctypes.c_int)
 _last_error = _sig("fmd_last_error", ctypes.c_char_p)
 _profile_enable = _sig("fmd_profile_enable", ctypes.c_int, ctypes.c_int)
@@ -120,7 +135,8 @@ _version = _sig("fmd_version", ctypes.c_char_p)
 EXPORTED = ["fmd_kv_append", "fmd_kv_append_batched", "fmd_workspace_bytes", "fmd_denoise_step",
             "fmd_attention", "fmd_unit_workspace_bytes", "fmd_denoise_unit",
             "fmd_unit_qkv_workspace_bytes", "fmd_denoise_unit_qkv",
-            "fmd_unit_cfg_workspace_bytes", "fmd_denoise_unit_cfg", "fmd_strerror",
+            "fmd_unit_cfg_workspace_bytes", "fmd_denoise_unit_cfg",
+            "fmd_unit_layers_workspace_bytes", "fmd_denoise_unit_layers", "fmd_strerror",
             "fmd_last_error", "fmd_profile_enable", "fmd_profile_read", "fmd_version"]
 
 
@@ -436,6 +452,73 @@ def denoise_unit_cfg(sessions, w_qkv, w_o, workspace=None, stream=None):
     _check(_denoise_unit_cfg(arr, n, n_steps, _ptr(w_qkv, torch.bfloat16, "w_qkv"),
                              _ptr(w_o, torch.bfloat16, "w_o"), workspace.data_ptr(),
                              workspace.numel(), _stream_ptr(stream)))
+
+
+class UnitLayersIO:
+    """One session's inputs for a unit of the layer-stack solver (see
+    ``fmd_unit_layers_io``): one ring per layer, one K/V slice per layer (or
+    none), the latent z (float32 [n_q][d], eps in, final latent out) and the
+    step sizes h."""
+
+    def __init__(self, caches, z, h, k_slices=None, v_slices=None, n_audio=0):
+        self.caches, self.z = list(caches), z
+        self.k_slices = list(k_slices) if k_slices is not None else None
+        self.v_slices = list(v_slices) if v_slices is not None else None
+        self.h = (ctypes.c_float * len(h))(*[float(x) for x in h])
+        self.n_steps = len(h)
+        self.n_q = z.shape[0]
+        self.n_audio = n_audio
+
+    def _struct(self):
+        L = len(self.caches)
+        self._c_arr = (ctypes.POINTER(_Cache) * L)(*[ctypes.pointer(c._c) for c in self.caches])
+        T = 0
+        if self.k_slices is not None:
+            if len(self.k_slices) != L or len(self.v_slices) != L:
+                raise ValueError("one K and one V slice per layer")
+            T = self.k_slices[0].shape[0]
+            if any(k.shape[0] != T for k in self.k_slices + self.v_slices):
+                raise ValueError("every layer appends the same number of tokens")
+            self._k_arr = (_vp * L)(*[_ptr(k, torch.bfloat16, "k_slice") for k in self.k_slices])
+            self._v_arr = (_vp * L)(*[_ptr(v, torch.bfloat16, "v_slice") for v in self.v_slices])
+            kp, vp = self._k_arr, self._v_arr
+        else:
+            kp = vp = None
+        return _UnitLayersIO(self._c_arr, kp, vp, T, _ptr(self.z, torch.float32, "z"),
+                             self.n_q - self.n_audio, self.n_audio,
+                             ctypes.cast(self.h, ctypes.POINTER(ctypes.c_float)))
+
+
+def _layers_array(sessions):
+    n = len(sessions)
+    L = len(sessions[0].caches)
+    if any(len(s.caches) != L for s in sessions):
+        raise ValueError("every session has the same number of layers")
+    return (_UnitLayersIO * n)(*[s._struct() for s in sessions]), n, L
+
+
+def unit_layers_workspace_bytes(sessions) -> int:
+    arr, n, L = _layers_array(sessions)
+    out = _sz(0)
+    _check(_unit_layers_workspace_bytes(arr, n, L, ctypes.byref(out)))
+    return out.value
+
+
+def denoise_unit_layers(sessions, w_qkv, w_o, workspace=None, stream=None):
+    """Append every layer's slice, then run the S solver steps through the
+    layer stack (w_qkv, w_o: one bf16 weight tensor per layer)."""
+    n_steps = sessions[0].n_steps
+    if any(s.n_steps != n_steps for s in sessions):
+        raise ValueError("all sessions must have the same number of steps")
+    if workspace is None:
+        workspace = alloc_workspace(unit_layers_workspace_bytes(sessions), sessions[0].z.device)
+    arr, n, L = _layers_array(sessions)
+    if len(w_qkv) != L or len(w_o) != L:
+        raise ValueError("one W_qkv and one W_o per layer")
+    wq = (_vp * L)(*[_ptr(w, torch.bfloat16, "w_qkv") for w in w_qkv])
+    wo = (_vp * L)(*[_ptr(w, torch.bfloat16, "w_o") for w in w_o])
+    _check(_denoise_unit_layers(arr, n, L, n_steps, wq, wo, workspace.data_ptr(),
+                                workspace.numel(), _stream_ptr(stream)))
 
 
 def profile_enable(on: bool = True):

@@ -357,9 +357,12 @@ int check_workspace(void* ws, size_t have, size_t need) {
 // guidance[i].  The pair's unit keys and values are transposed once, both
 // branches attend, their outputs are mixed (in place into the conditional
 // one) and one projection updates z.
+// proj_mode: kProjEuler, or kProjLayer / kProjLayerLast for a layer of a
+// stack, with r_out (one fp32 residual per projected unit).
 int enqueue_steps(const fmd_unit_step* units, int n, const std::vector<SessPlan>& plans,
                   const void* w_o, char* ws, bf16* o_out, hipStream_t st,
-                  bf16* const* zb_out = nullptr, const float* guidance = nullptr) {
+                  bf16* const* zb_out = nullptr, const float* guidance = nullptr,
+                  int proj_mode = kProjEuler, float* const* r_out = nullptr) {
   const int H = units[0].cache->n_heads, hd = units[0].cache->head_dim;
   const int d = H * hd;
   const float scale_log2 = (float)(1.4426950408889634 / sqrt((double)hd));
@@ -439,8 +442,8 @@ int enqueue_steps(const fmd_unit_step* units, int n, const std::vector<SessPlan>
       const int j = k / per_proj, unit = (c0 + k) / per_proj;
       const int mtiles = (p.n_q + kProjTile - 1) / kProjTile;
       const int ntiles = (d + kProjTileN - 1) / kProjTileN;
-      pa.s[j] = ProjSess{o, u.z, zb_out ? zb_out[unit] : nullptr, {nullptr, nullptr, nullptr},
-                         p.n_q, mtiles, pa.items, u.h};
+      pa.s[j] = ProjSess{o, u.z, zb_out ? zb_out[unit] : nullptr, r_out ? r_out[unit] : nullptr,
+                         {nullptr, nullptr, nullptr}, p.n_q, mtiles, pa.items, u.h};
       pa.items += mtiles * ntiles;
     }
     // Attention items, head-major over the sessions.  Inside a head the
@@ -469,7 +472,7 @@ int enqueue_steps(const fmd_unit_step* units, int n, const std::vector<SessPlan>
         (rc = timed_launch(FMD_KERNEL_MIX, st, [&] { return launch_mix(ma, st); })))
       return rc;
     if (!o_out &&
-        (rc = timed_launch(FMD_KERNEL_PROJ, st, [&] { return launch_proj(pa, kProjEuler, st); })))
+        (rc = timed_launch(FMD_KERNEL_PROJ, st, [&] { return launch_proj(pa, proj_mode, st); })))
       return rc;
   }
   return FMD_OK;
@@ -716,74 +719,94 @@ int fmd_denoise_unit(fmd_unit_io* sessions, int32_t n_sessions, int32_t n_steps,
   return FMD_OK;
 }
 
-// The z-dependent solver's driver, shared by the plain and the guided form.
-// One solver unit has one latent z and nb caches (nb = 1: plain; nb = 2:
-// branch 0 conditional, branch 1 unconditional); its attention sessions are
-// numbered unit * nb + branch.
+// The z-dependent solver's driver, shared by the plain, the guided and the
+// layer-stack form.  One solver unit has one latent z and its caches:
+//   plain:   nb = 1, L = 1: cache[0];
+//   guided:  nb = 2, L = 1: cache[0] conditional, cache[1] unconditional; its
+//            attention sessions are numbered unit * 2 + branch;
+//   layers:  nb = 1, L >= 1: cache[l] is layer l's ring.
 struct SolverUnit {
-  fmd_kv_cache* cache[2];
-  int64_t slice_tokens[2];   // appended before the steps (for planning)
+  std::vector<fmd_kv_cache*> cache;
+  std::vector<int64_t> slice_tokens;   // appended before the steps (for planning)
   float* z;
   int32_t n_video, n_audio;
   const float* h;
   float g;
 };
 
-// Workspace: per unit bf16(z), Q, K_u, V_u ([n_q][d] each), then the step
-// workspace of fmd_denoise_step for all attention sessions' post-append rings.
+// Workspace: per unit bf16 z (the Q/K/V projection's input), Q, K_u, V_u
+// ([n_q][d] bf16 each) and, for a layer stack, the fp32 residual; then the
+// step workspace of fmd_denoise_step, sized for the largest layer (the layers
+// of a step run one after another and reuse it).
 struct SolverLayout {
-  std::vector<fmd_kv_cache> after;   // per attention session
-  std::vector<fmd_unit_step> steps;  // per attention session
-  std::vector<SessPlan> plans;
-  std::vector<size_t> off;           // per unit: zb, then q, k, v at +1..3 * slab
+  std::vector<std::vector<fmd_kv_cache>> after;   // per layer: per attention session
+  std::vector<std::vector<fmd_unit_step>> steps;  // per layer
+  std::vector<std::vector<SessPlan>> plans;       // per layer
+  std::vector<size_t> off;                        // per unit: zb, q, k, v, [r]
   size_t slab_total = 0, bytes = 0;
 };
 
-static void layout_solver(const std::vector<SolverUnit>& us, int nb, SolverLayout& L) {
+static size_t unit_slab(int n_q, int d) { return align256((size_t)n_q * d * 2); }
+
+static void layout_solver(const std::vector<SolverUnit>& us, int nb, int n_layers,
+                          SolverLayout& L) {
   const int n = (int)us.size();
   const int d = us[0].cache[0]->n_heads * us[0].cache[0]->head_dim;
-  L.after.resize((size_t)n * nb);
-  L.steps.resize((size_t)n * nb);
+  L.after.assign(n_layers, std::vector<fmd_kv_cache>((size_t)n * nb));
+  L.steps.assign(n_layers, std::vector<fmd_unit_step>((size_t)n * nb));
+  L.plans.assign(n_layers, {});
   L.off.resize(n);
   size_t off = 0;
   for (int i = 0; i < n; ++i) {
-    const SolverUnit& u = us[i];
-    const int n_q = u.n_video + u.n_audio;
+    const int n_q = us[i].n_video + us[i].n_audio;
     L.off[i] = off;
-    off += 4 * align256((size_t)n_q * d * 2);
-    for (int b = 0; b < nb; ++b) {
-      fmd_kv_cache& a = L.after[(size_t)i * nb + b];
-      a = *u.cache[b];
-      if (u.slice_tokens[b] > 0) {
-        a.head_tokens = (a.head_tokens + u.slice_tokens[b]) % a.cap_tokens;
-        a.len_tokens = std::min(a.len_tokens + u.slice_tokens[b], a.cap_tokens);
-      }
-      // q/k_u/v_u are placeholders here (set per step); planning needs shapes only.
-      L.steps[(size_t)i * nb + b] =
-          fmd_unit_step{&a, u.z, u.z, u.z, u.z, u.n_video, u.n_audio, u.h[0]};
-    }
+    off += 4 * unit_slab(n_q, d);
+    if (n_layers > 1) off += 2 * unit_slab(n_q, d);   // fp32 residual
   }
   L.slab_total = off;
   size_t step_bytes = 0;
-  plan_steps(L.steps.data(), n * nb, false, L.plans, &step_bytes);
+  for (int l = 0; l < n_layers; ++l) {
+    for (int i = 0; i < n; ++i) {
+      const SolverUnit& u = us[i];
+      for (int b = 0; b < nb; ++b) {
+        const int c = n_layers > 1 ? l : b;
+        fmd_kv_cache& a = L.after[l][(size_t)i * nb + b];
+        a = *u.cache[c];
+        if (u.slice_tokens[c] > 0) {
+          a.head_tokens = (a.head_tokens + u.slice_tokens[c]) % a.cap_tokens;
+          a.len_tokens = std::min(a.len_tokens + u.slice_tokens[c], a.cap_tokens);
+        }
+        // q/k_u/v_u are placeholders here (set per step); planning needs shapes only.
+        L.steps[l][(size_t)i * nb + b] =
+            fmd_unit_step{&a, u.z, u.z, u.z, u.z, u.n_video, u.n_audio, u.h[0]};
+      }
+    }
+    size_t bytes = 0;
+    plan_steps(L.steps[l].data(), n * nb, false, L.plans[l], &bytes);
+    step_bytes = std::max(step_bytes, bytes);
+  }
   L.bytes = L.slab_total + step_bytes;
 }
 
 // Enqueue the solver (validated, appends already enqueued): a bf16 copy of
-// each starting latent, then per step the Q/K/V projection of every unit and
-// the attention + projection step over all attention sessions.
-static int run_solver(const std::vector<SolverUnit>& us, int nb, int n_steps, const void* w_qkv,
-                      const void* w_o, char* ws, SolverLayout& L, hipStream_t st) {
+// each starting latent (and a cleared residual for a layer stack), then per
+// step and layer the Q/K/V projection of every unit and the attention +
+// projection step over all attention sessions.  w_qkv / w_o: one per layer.
+static int run_solver(const std::vector<SolverUnit>& us, int nb, int n_layers, int n_steps,
+                      const void* const* w_qkv, const void* const* w_o, char* ws,
+                      SolverLayout& L, hipStream_t st) {
   const int n = (int)us.size();
   const int H = us[0].cache[0]->n_heads, hd = us[0].cache[0]->head_dim;
   const int d = H * hd;
   std::vector<bf16*> zb(n), q(n), k(n), v(n);
+  std::vector<float*> r(n, nullptr);
   for (int i = 0; i < n; ++i) {
-    const size_t slab = align256((size_t)(us[i].n_video + us[i].n_audio) * d * 2);
+    const size_t slab = unit_slab(us[i].n_video + us[i].n_audio, d);
     zb[i] = reinterpret_cast<bf16*>(ws + L.off[i]);
     q[i] = reinterpret_cast<bf16*>(ws + L.off[i] + slab);
     k[i] = reinterpret_cast<bf16*>(ws + L.off[i] + 2 * slab);
     v[i] = reinterpret_cast<bf16*>(ws + L.off[i] + 3 * slab);
+    if (n_layers > 1) r[i] = reinterpret_cast<float*>(ws + L.off[i] + 4 * slab);
   }
   int rc;
   for (int c0 = 0; c0 < n; c0 += kMaxSessPerLaunch) {
@@ -793,7 +816,7 @@ static int run_solver(const std::vector<SolverUnit>& us, int nb, int n_steps, co
     for (int j = 0; j < cn; ++j) {
       const int i = c0 + j;
       const int64_t ne = (int64_t)(us[i].n_video + us[i].n_audio) * d;
-      ca.s[j] = CvtSess{us[i].z, zb[i], ne, ca.items};
+      ca.s[j] = CvtSess{us[i].z, zb[i], r[i], ne, ca.items};
       ca.items += ne / 8;
     }
     if ((rc = timed_launch(FMD_KERNEL_CVT, st, [&] { return launch_cvt(ca, st); }))) return rc;
@@ -803,41 +826,47 @@ static int run_solver(const std::vector<SolverUnit>& us, int nb, int n_steps, co
   for (int i = 0; i < n; ++i) g[i] = us[i].g;
   char* step_ws = ws + L.slab_total;
   for (int s = 0; s < n_steps; ++s) {
-    for (int c0 = 0; c0 < n; c0 += kMaxSessPerLaunch) {
-      const int cn = std::min(kMaxSessPerLaunch, n - c0);
-      ProjArgs pa = {};
-      pa.n_sess = cn;
-      pa.d = d;
-      pa.n_out = 3 * d;
-      pa.w = static_cast<const bf16*>(w_qkv);
-      const int ntiles = (3 * d + kProjTileN - 1) / kProjTileN;
-      for (int j = 0; j < cn; ++j) {
-        const int i = c0 + j;
-        const int n_q = us[i].n_video + us[i].n_audio;
-        const int mtiles = (n_q + kProjTile - 1) / kProjTile;
-        pa.s[j] = ProjSess{zb[i], nullptr, nullptr, {q[i], k[i], v[i]}, n_q, mtiles, pa.items,
-                           0.f};
-        pa.items += mtiles * ntiles;
+    for (int l = 0; l < n_layers; ++l) {
+      for (int c0 = 0; c0 < n; c0 += kMaxSessPerLaunch) {
+        const int cn = std::min(kMaxSessPerLaunch, n - c0);
+        ProjArgs pa = {};
+        pa.n_sess = cn;
+        pa.d = d;
+        pa.n_out = 3 * d;
+        pa.w = static_cast<const bf16*>(w_qkv[l]);
+        const int ntiles = (3 * d + kProjTileN - 1) / kProjTileN;
+        for (int j = 0; j < cn; ++j) {
+          const int i = c0 + j;
+          const int n_q = us[i].n_video + us[i].n_audio;
+          const int mtiles = (n_q + kProjTile - 1) / kProjTile;
+          pa.s[j] = ProjSess{zb[i], nullptr, nullptr, nullptr, {q[i], k[i], v[i]}, n_q, mtiles,
+                             pa.items, 0.f};
+          pa.items += mtiles * ntiles;
+        }
+        if ((rc = timed_launch(FMD_KERNEL_QKV, st, [&] { return launch_proj(pa, kProjQkv, st); })))
+          return rc;
       }
-      if ((rc = timed_launch(FMD_KERNEL_QKV, st, [&] { return launch_proj(pa, kProjQkv, st); })))
+      std::vector<fmd_unit_step>& steps = L.steps[l];
+      for (int i = 0; i < n; ++i) {
+        for (int b = 0; b < nb; ++b) {
+          fmd_unit_step& u = steps[(size_t)i * nb + b];
+          u.cache = us[i].cache[n_layers > 1 ? l : b];   // now in its post-append state
+          u.q = q[i];
+          u.k_u = k[i];
+          u.v_u = v[i];
+          u.z = us[i].z;
+          u.h = us[i].h[s];
+        }
+      }
+      const bool last_layer = l + 1 == n_layers;
+      const int mode = n_layers == 1 ? kProjEuler : (last_layer ? kProjLayerLast : kProjLayer);
+      // The last layer of the last step needs no bf16 copy of its result.
+      const bool need_zb = !(last_layer && s + 1 == n_steps);
+      if ((rc = enqueue_steps(steps.data(), n * nb, L.plans[l], w_o[l], step_ws, nullptr, st,
+                              need_zb ? zb.data() : nullptr, nb == 2 ? g.data() : nullptr, mode,
+                              n_layers > 1 ? r.data() : nullptr)))
         return rc;
     }
-    for (int i = 0; i < n; ++i) {
-      for (int b = 0; b < nb; ++b) {
-        fmd_unit_step& u = L.steps[(size_t)i * nb + b];
-        u.cache = us[i].cache[b];   // now in its post-append state
-        u.q = q[i];
-        u.k_u = k[i];
-        u.v_u = v[i];
-        u.z = us[i].z;
-        u.h = us[i].h[s];
-      }
-    }
-    // The last step needs no bf16 copy of its result.
-    if ((rc = enqueue_steps(L.steps.data(), n * nb, L.plans, w_o, step_ws, nullptr, st,
-                            s + 1 < n_steps ? zb.data() : nullptr,
-                            nb == 2 ? g.data() : nullptr)))
-      return rc;
   }
   return FMD_OK;
 }
@@ -907,7 +936,7 @@ static int validate_unit_qkv(const fmd_unit_qkv_io* ss, int n, int n_steps) {
 static std::vector<SolverUnit> qkv_units(const fmd_unit_qkv_io* ss, int n) {
   std::vector<SolverUnit> us(n);
   for (int i = 0; i < n; ++i)
-    us[i] = SolverUnit{{ss[i].cache, nullptr}, {ss[i].slice_tokens, 0}, ss[i].z, ss[i].n_video,
+    us[i] = SolverUnit{{ss[i].cache}, {ss[i].slice_tokens}, ss[i].z, ss[i].n_video,
                        ss[i].n_audio, ss[i].h, 1.f};
   return us;
 }
@@ -919,7 +948,7 @@ int fmd_unit_qkv_workspace_bytes(const fmd_unit_qkv_io* sessions, int32_t n_sess
   int rc = validate_unit_qkv(sessions, n_sessions, 1);
   if (rc) return rc;
   SolverLayout L;
-  layout_solver(qkv_units(sessions, n_sessions), 1, L);
+  layout_solver(qkv_units(sessions, n_sessions), 1, 1, L);
   *out_bytes = L.bytes;
   return FMD_OK;
 }
@@ -934,7 +963,7 @@ int fmd_denoise_unit_qkv(fmd_unit_qkv_io* sessions, int32_t n_sessions, int32_t 
   if ((rc = check_tensor(w_o, 0, "w_o"))) return rc;
   const std::vector<SolverUnit> us = qkv_units(sessions, n_sessions);
   SolverLayout L;
-  layout_solver(us, 1, L);
+  layout_solver(us, 1, 1, L);
   if ((rc = check_workspace(workspace, workspace_bytes, L.bytes))) return rc;
 
   hipStream_t st = static_cast<hipStream_t>(stream);
@@ -948,7 +977,7 @@ int fmd_denoise_unit_qkv(fmd_unit_qkv_io* sessions, int32_t n_sessions, int32_t 
     ts.push_back(sessions[i].slice_tokens);
   }
   if ((rc = enqueue_unit_appends(caches, ks, vs, ts, st))) return rc;
-  return run_solver(us, 1, n_steps, w_qkv, w_o, static_cast<char*>(workspace), L, st);
+  return run_solver(us, 1, 1, n_steps, &w_qkv, &w_o, static_cast<char*>(workspace), L, st);
 }
 
 // ---------------------------------------------------------------------------
@@ -999,7 +1028,7 @@ int fmd_unit_cfg_workspace_bytes(const fmd_unit_cfg_io* sessions, int32_t n_sess
   int rc = validate_unit_cfg(sessions, n_sessions, 1);
   if (rc) return rc;
   SolverLayout L;
-  layout_solver(cfg_units(sessions, n_sessions), 2, L);
+  layout_solver(cfg_units(sessions, n_sessions), 2, 1, L);
   *out_bytes = L.bytes;
   return FMD_OK;
 }
@@ -1014,7 +1043,7 @@ int fmd_denoise_unit_cfg(fmd_unit_cfg_io* sessions, int32_t n_sessions, int32_t 
   if ((rc = check_tensor(w_o, 0, "w_o"))) return rc;
   const std::vector<SolverUnit> us = cfg_units(sessions, n_sessions);
   SolverLayout L;
-  layout_solver(us, 2, L);
+  layout_solver(us, 2, 1, L);
   if ((rc = check_workspace(workspace, workspace_bytes, L.bytes))) return rc;
 
   hipStream_t st = static_cast<hipStream_t>(stream);
@@ -1029,7 +1058,97 @@ int fmd_denoise_unit_cfg(fmd_unit_cfg_io* sessions, int32_t n_sessions, int32_t 
     ts.insert(ts.end(), {s.cond_slice_tokens, s.uncond_slice_tokens});
   }
   if ((rc = enqueue_unit_appends(caches, ks, vs, ts, st))) return rc;
-  return run_solver(us, 2, n_steps, w_qkv, w_o, static_cast<char*>(workspace), L, st);
+  return run_solver(us, 2, 1, n_steps, &w_qkv, &w_o, static_cast<char*>(workspace), L, st);
+}
+
+// ---------------------------------------------------------------------------
+// The layer-stack solver: one ring and one pair of weights per layer.
+// ---------------------------------------------------------------------------
+static int validate_unit_layers(const fmd_unit_layers_io* ss, int n, int n_layers,
+                                int n_steps) {
+  if (!ss) return fail(FMD_E_INVAL, "sessions is NULL");
+  if (n < 1 || n > FMD_MAX_SESSIONS)
+    return fail(FMD_E_INVAL, "n_sessions=%d (must be 1..%d)", n, FMD_MAX_SESSIONS);
+  if (n_layers < 1 || n_layers > FMD_MAX_LAYERS)
+    return fail(FMD_E_INVAL, "n_layers=%d (must be 1..%d)", n_layers, FMD_MAX_LAYERS);
+  if (n_steps < 1) return fail(FMD_E_INVAL, "n_steps=%d (must be >= 1)", n_steps);
+  int rc;
+  std::vector<const fmd_kv_cache*> seen;
+  for (int i = 0; i < n; ++i) {
+    const fmd_unit_layers_io& s = ss[i];
+    if (!s.caches) return fail(FMD_E_INVAL, "session %d: caches is NULL", i);
+    if (s.slice_tokens < 0)
+      return fail(FMD_E_INVAL, "session %d: slice_tokens %lld", i, (long long)s.slice_tokens);
+    if (s.slice_tokens > 0 && (!s.k_slices || !s.v_slices))
+      return fail(FMD_E_INVAL, "session %d: slice arrays are NULL", i);
+    for (int l = 0; l < n_layers; ++l) {
+      if ((rc = check_cache(s.caches[l], i))) return rc;
+      if ((rc = check_same_shape(ss[0].caches[0], s.caches[l], i))) return rc;
+      if (s.slice_tokens > 0 &&
+          (rc = check_append(s.caches[l], s.k_slices[l], s.v_slices[l], s.slice_tokens, i)))
+        return rc;
+      seen.push_back(s.caches[l]);
+    }
+    if ((rc = check_unit_latent(s.z, s.n_video, s.n_audio, s.h, n_steps, i))) return rc;
+  }
+  std::sort(seen.begin(), seen.end());
+  if (std::adjacent_find(seen.begin(), seen.end()) != seen.end())
+    return fail(FMD_E_INVAL, "a cache appears twice among the sessions' layers");
+  return FMD_OK;
+}
+
+static std::vector<SolverUnit> layer_units(const fmd_unit_layers_io* ss, int n, int n_layers) {
+  std::vector<SolverUnit> us(n);
+  for (int i = 0; i < n; ++i)
+    us[i] = SolverUnit{std::vector<fmd_kv_cache*>(ss[i].caches, ss[i].caches + n_layers),
+                       std::vector<int64_t>(n_layers, ss[i].slice_tokens), ss[i].z,
+                       ss[i].n_video, ss[i].n_audio, ss[i].h, 1.f};
+  return us;
+}
+
+int fmd_unit_layers_workspace_bytes(const fmd_unit_layers_io* sessions, int32_t n_sessions,
+                                    int32_t n_layers, size_t* out_bytes) {
+  g_last_error.clear();
+  if (!out_bytes) return fail(FMD_E_INVAL, "out_bytes is NULL");
+  int rc = validate_unit_layers(sessions, n_sessions, n_layers, 1);
+  if (rc) return rc;
+  SolverLayout L;
+  layout_solver(layer_units(sessions, n_sessions, n_layers), 1, n_layers, L);
+  *out_bytes = L.bytes;
+  return FMD_OK;
+}
+
+int fmd_denoise_unit_layers(fmd_unit_layers_io* sessions, int32_t n_sessions, int32_t n_layers,
+                            int32_t n_steps, const void* const* w_qkv, const void* const* w_o,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+  g_last_error.clear();
+  int rc = validate_unit_layers(sessions, n_sessions, n_layers, n_steps);
+  if (rc) return rc;
+  if (!w_qkv || !w_o) return fail(FMD_E_INVAL, "weight arrays are NULL");
+  for (int l = 0; l < n_layers; ++l) {
+    if ((rc = check_tensor(w_qkv[l], l, "w_qkv"))) return rc;
+    if ((rc = check_tensor(w_o[l], l, "w_o"))) return rc;
+  }
+  const std::vector<SolverUnit> us = layer_units(sessions, n_sessions, n_layers);
+  SolverLayout L;
+  layout_solver(us, 1, n_layers, L);
+  if ((rc = check_workspace(workspace, workspace_bytes, L.bytes))) return rc;
+
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  std::vector<fmd_kv_cache*> caches;
+  std::vector<const void*> ks, vs;
+  std::vector<int64_t> ts;
+  for (int i = 0; i < n_sessions; ++i) {
+    const fmd_unit_layers_io& s = sessions[i];
+    for (int l = 0; l < n_layers; ++l) {
+      caches.push_back(s.caches[l]);
+      ks.push_back(s.slice_tokens > 0 ? s.k_slices[l] : nullptr);
+      vs.push_back(s.slice_tokens > 0 ? s.v_slices[l] : nullptr);
+      ts.push_back(s.slice_tokens);
+    }
+  }
+  if ((rc = enqueue_unit_appends(caches, ks, vs, ts, st))) return rc;
+  return run_solver(us, 1, n_layers, n_steps, w_qkv, w_o, static_cast<char*>(workspace), L, st);
 }
 
 int fmd_profile_enable(int enable) {

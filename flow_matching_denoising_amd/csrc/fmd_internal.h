@@ -140,14 +140,22 @@ struct CombineArgs {
 //   kProjEuler: n_out = d; z <- z - h * Y (fp32, in place), and, if zb is set,
 //               zb <- bf16(z) (the next step's projection input);
 //   kProjQkv:   n_out = 3d; column c of Y goes to out[c / d], column c % d,
-//               rounded to bf16 (the unit's Q, K_u, V_u).
+//               rounded to bf16 (the unit's Q, K_u, V_u);
+//   kProjLayer: n_out = d; a layer of a stack adds its update to the fp32
+//               residual r <- r + Y and writes zb <- bf16(z + r), the next
+//               layer's input;
+//   kProjLayerLast: the stack's last layer: z <- z - h * (r + Y), r <- 0,
+//               and, if zb is set, zb <- bf16(z).
 constexpr int kProjEuler = 0;
 constexpr int kProjQkv = 1;
+constexpr int kProjLayer = 2;
+constexpr int kProjLayerLast = 3;
 
 struct ProjSess {
   const bf16* a;      // [n_q][d]
-  float* z;           // kProjEuler: [n_q][d]
-  bf16* zb;           // kProjEuler: [n_q][d] or nullptr
+  float* z;           // kProjEuler, kProjLayer*: [n_q][d]
+  bf16* zb;           // kProjEuler, kProjLayer*: [n_q][d] or nullptr
+  float* r;           // kProjLayer*: [n_q][d] residual
   bf16* out[3];       // kProjQkv: Q, K_u, V_u, each [n_q][d]
   int32_t n_q;
   int32_t n_mtiles;
@@ -167,6 +175,7 @@ struct ProjArgs {
 struct CvtSess {
   const float* z;
   bf16* zb;
+  float* r;           // if set, cleared to 0 (a layer stack's residual)
   int64_t n;          // elements (n_q * d), a multiple of 8
   int64_t item0;      // first 8-element group of this session
 };

@@ -239,6 +239,38 @@ __global__ __launch_bounds__(WAVES * 64) void proj_kernel(ProjArgs a) {
         }
       }
     }
+  } else if constexpr (MODE == kProjLayer || MODE == kProjLayerLast) {
+    // Residual stream of a layer stack (see kProjLayer / kProjLayerLast).
+    float* const zc = z + n;
+    float* const rc = s.r + n;
+    bf16* const zbc = s.zb ? s.zb + n : nullptr;
+#pragma unroll
+    for (int i = 0; i < MT; ++i) {
+      float zv[16], rv[16];
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        const int m = m0 + i * 32 + (q >> 2) * 8 + g * 4 + (q & 3);
+        const bool in = full || m < n_q;
+        zv[q] = in ? zc[(int64_t)m * d] : 0.f;
+        rv[q] = in ? rc[(int64_t)m * d] : 0.f;
+      }
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        const int m = m0 + i * 32 + (q >> 2) * 8 + g * 4 + (q & 3);
+        if (full || m < n_q) {
+          const float rn = rv[q] + acc[i][q];
+          if constexpr (MODE == kProjLayer) {
+            rc[(int64_t)m * d] = rn;
+            if (zbc) zbc[(int64_t)m * d] = (bf16)(zv[q] + rn);
+          } else {
+            const float zn = zv[q] - hstep * rn;
+            zc[(int64_t)m * d] = zn;
+            rc[(int64_t)m * d] = 0.f;
+            if (zbc) zbc[(int64_t)m * d] = (bf16)zn;
+          }
+        }
+      }
+    }
   } else {
     // Column n of Y is column n % d of Q, K_u or V_u, rounded to bf16.
     const int t = n >= 2 * d ? 2 : (n >= d ? 1 : 0);
@@ -272,6 +304,10 @@ __global__ __launch_bounds__(256) void cvt_kernel(CvtArgs a) {
     y[4 + t] = (bf16)x1[t];
   }
   *reinterpret_cast<bf16x8*>(s.zb + e) = y;
+  if (s.r) {
+    *reinterpret_cast<f32x4*>(s.r + e) = f32x4{0.f, 0.f, 0.f, 0.f};
+    *reinterpret_cast<f32x4*>(s.r + e + 4) = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
 }
 
 // The guided velocity v_u + g (v_c - v_u) of two branches that share W_o is
@@ -298,18 +334,27 @@ __global__ __launch_bounds__(256) void mix_kernel(MixArgs a) {
 hipError_t launch_proj(const ProjArgs& a, int mode, hipStream_t st) {
   if (a.items <= 0) return hipSuccess;
   static const hipError_t attr_err = [] {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&proj_kernel<kProjEuler>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES);
-    if (e == hipSuccess)
-      e = hipFuncSetAttribute(reinterpret_cast<const void*>(&proj_kernel<kProjQkv>),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES);
+    const void* fns[] = {reinterpret_cast<const void*>(&proj_kernel<kProjEuler>),
+                         reinterpret_cast<const void*>(&proj_kernel<kProjQkv>),
+                         reinterpret_cast<const void*>(&proj_kernel<kProjLayer>),
+                         reinterpret_cast<const void*>(&proj_kernel<kProjLayerLast>)};
+    hipError_t e = hipSuccess;
+    for (const void* f : fns)
+      if (e == hipSuccess)
+        e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES);
     return e;
   }();
   if (attr_err != hipSuccess) return attr_err;
-  if (mode == kProjEuler)
-    hipLaunchKernelGGL(proj_kernel<kProjEuler>, dim3(a.items), dim3(WAVES * 64), LDS_BYTES, st, a);
-  else
-    hipLaunchKernelGGL(proj_kernel<kProjQkv>, dim3(a.items), dim3(WAVES * 64), LDS_BYTES, st, a);
+  const dim3 grid(a.items), block(WAVES * 64);
+  switch (mode) {
+    case kProjEuler: hipLaunchKernelGGL(proj_kernel<kProjEuler>, grid, block, LDS_BYTES, st, a); break;
+    case kProjQkv: hipLaunchKernelGGL(proj_kernel<kProjQkv>, grid, block, LDS_BYTES, st, a); break;
+    case kProjLayer: hipLaunchKernelGGL(proj_kernel<kProjLayer>, grid, block, LDS_BYTES, st, a); break;
+    case kProjLayerLast:
+      hipLaunchKernelGGL(proj_kernel<kProjLayerLast>, grid, block, LDS_BYTES, st, a);
+      break;
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 

@@ -276,6 +276,54 @@ int fmd_denoise_unit_cfg(fmd_unit_cfg_io* sessions, int32_t n_sessions, int32_t 
                          const void* w_qkv, const void* w_o, void* workspace,
                          size_t workspace_bytes, void* stream);
 
+/*
+ * The z-dependent solver over a stack of n_layers attention layers, each with
+ * its own ring: the velocity network is a block-causal transformer evaluated
+ * on the unit's noisy latents with the clean context at every solver step
+ * [Wan-Streamer (gongshangzheng blog), 3.3 Block-Causal Transformer, 3.4
+ * 条件流匹配]; the pages give no layer structure, so a layer here is the
+ * attention block of fmd_denoise_unit_qkv on a residual stream.  Per step s:
+ *   r = 0;  for l = 0 .. n_layers-1:
+ *     [Q | K_u | V_u] = bf16( bf16(z + r) * W_qkv[l]^T )
+ *     O = attention of Q over [layer l's valid ring ; K_u, V_u]
+ *     r = r + O * W_o[l]^T                       (fp32)
+ *   z <- z - h[s] * r
+ * With n_layers = 1 this is fmd_denoise_unit_qkv.
+ * One session's inputs:
+ *   caches         : [n_layers] the session's ring of each layer (state before
+ *                    the appends; updated); distinct caches of one shape
+ *   k/v_slices     : [n_layers] bf16 [slice_tokens][n_heads][head_dim], one
+ *                    per layer; not read when slice_tokens is 0
+ *   slice_tokens   : tokens appended to every layer's ring (0 = none)
+ *   z              : fp32 [n_q][d], eps on entry, the final latent on exit
+ *   h              : HOST array [n_steps] of positive step sizes
+ */
+#define FMD_MAX_LAYERS 256
+typedef struct fmd_unit_layers_io {
+  fmd_kv_cache* const* caches;
+  const void* const* k_slices;
+  const void* const* v_slices;
+  int64_t slice_tokens;
+  float* z;
+  int32_t n_video;
+  int32_t n_audio;
+  const float* h;
+} fmd_unit_layers_io;
+
+/* Workspace bytes fmd_denoise_unit_layers needs (pure host arithmetic). */
+int fmd_unit_layers_workspace_bytes(const fmd_unit_layers_io* sessions, int32_t n_sessions,
+                                    int32_t n_layers, size_t* out_bytes);
+
+/* One denoised unit of the layer-stack solver for n_sessions sessions: one
+ * batched append of every layer's slice, then n_steps steps as above.  w_qkv,
+ * w_o: HOST arrays [n_layers] of device pointers to bf16 [3d][d] and [d][d]
+ * weights.  Errors: as fmd_denoise_unit_qkv; n_layers outside
+ * 1..FMD_MAX_LAYERS or a cache used twice -> FMD_E_INVAL.  Nothing is
+ * enqueued when an error is returned. */
+int fmd_denoise_unit_layers(fmd_unit_layers_io* sessions, int32_t n_sessions, int32_t n_layers,
+                            int32_t n_steps, const void* const* w_qkv, const void* const* w_o,
+                            void* workspace, size_t workspace_bytes, void* stream);
+
 /* Static description of a status code (never NULL). */
 const char* fmd_strerror(int status);
 

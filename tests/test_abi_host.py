@@ -269,3 +269,59 @@ def test_unit_cfg_workspace_holds_both_branches():
     # A second attention output (928 x 5120 bf16) and staging on top of the
     # single-branch workspace.
     assert out.value >= q.value + 928 * 5120 * 2
+
+
+def _layers_io(caches, h, T=0, z=FAKE, with_slices=True):
+    from flow_matching_denoising_amd import _UnitLayersIO
+    L = len(caches)
+    arr = (ctypes.POINTER(_Cache) * L)(*[ctypes.pointer(c) for c in caches])
+    sl = (ctypes.c_void_p * L)(*([FAKE] * L)) if with_slices else None
+    io = _UnitLayersIO(arr, sl, sl, T, z, 12, 4, ctypes.cast(h, ctypes.POINTER(ctypes.c_float)))
+    io._keep = (arr, sl)
+    return io
+
+
+def test_denoise_unit_layers_validation_leaves_state():
+    from flow_matching_denoising_amd import _UnitLayersIO
+    h = (ctypes.c_float * 2)(0.5, 0.5)
+    a, b, c = _cache(), _cache(), _cache()
+    w = (ctypes.c_void_p * 3)(FAKE, FAKE, FAKE)
+    run = fmd._denoise_unit_layers
+
+    def call(ios, L, n_steps=2, ws=1 << 30, wq=w):
+        arr = (_UnitLayersIO * len(ios))(*ios)
+        return run(arr, len(ios), L, n_steps, wq, w, FAKE, ws, None)
+    assert call([_layers_io([a, a], h)], 2) == -1                    # one ring in two layers
+    assert call([_layers_io([a, b], h), _layers_io([c, a], h)], 2) == -1   # shared across sessions
+    assert call([_layers_io([a, _cache(H=3)], h)], 2) == -2          # layer shapes differ
+    assert call([_layers_io([a, b], h, T=8, with_slices=False)], 2) == -1   # no slice arrays
+    assert call([_layers_io([a, b], h, T=200)], 2) == -3             # slice > cap
+    assert call([_layers_io([a, b], h)], 0) == -1                    # no layers
+    assert call([_layers_io([a, b], h)], 2, n_steps=0) == -1
+    assert call([_layers_io([a, b], h, z=0)], 2) == -1               # no z
+    assert call([_layers_io([a, b], h)], 2, ws=16) == -5             # workspace too small
+    assert call([_layers_io([a, b], h)], 2, wq=None) == -1           # no weight array
+    h[1] = -1.0
+    assert call([_layers_io([a, b], h)], 2) == -1                    # h[1] < 0
+    for x in (a, b, c):
+        assert (x.len_tokens, x.head_tokens) == (96, 96)
+
+
+def test_unit_layers_workspace():
+    from flow_matching_denoising_amd import _UnitLayersIO, _UnitQkvIO
+    h = (ctypes.c_float * 1)(1.0)
+    rings = [_cache(H=40, hd=128, cap=60416, ln=60416, head=0) for _ in range(3)]
+
+    def ws(L):
+        io = _layers_io(rings[:L], h)
+        io.n_video, io.n_audio = 920, 8
+        out = ctypes.c_size_t(0)
+        assert fmd._unit_layers_workspace_bytes((_UnitLayersIO * 1)(io), 1, L,
+                                                ctypes.byref(out)) == 0
+        return out.value
+    qio = _UnitQkvIO(ctypes.pointer(rings[0]), 0, 0, 0, FAKE, 920, 8,
+                     ctypes.cast(h, ctypes.POINTER(ctypes.c_float)))
+    q = ctypes.c_size_t(0)
+    assert fmd._unit_qkv_workspace_bytes((_UnitQkvIO * 1)(qio), 1, ctypes.byref(q)) == 0
+    assert ws(1) == q.value                              # one layer: the z-dependent solver
+    assert ws(3) == ws(2) >= q.value + 928 * 5120 * 4    # plus the fp32 residual, rings alike
