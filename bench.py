@@ -20,6 +20,8 @@ Prints ONE JSON line (rank 0, N=1).  Besides throughput it reports:
   16 steps, guidance 5) on the 640x368-class unit;
 * ulysses_rank_p8: one rank's attention under 8-way Ulysses context parallel
   (5 heads, all 928 tokens, the head shard of the ring);
+* layers_unit: the layer-stack solver with 4 layers (one ring and one pair of
+  weights per layer) on the 640x368-class unit;
 * append_batch8: the batched ring append at the 8-session shape.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
@@ -212,6 +214,61 @@ def cfg_unit_probe(units=4, warmup=2):
             "ms_per_unit": round(wall / units * 1e3, 3),
             "attn_us": round(attn_ms / attn_n * 1e3, 2),
             "attn_TFLOPs": round(attn_flops / (attn_ms / attn_n / 1e3) / 1e12, 1),
+            "per_kernel_us": {k: (round(v[0] / v[1] * 1e3, 2) if v[1] else None)
+                              for k, v in kt.items()}}
+
+
+def layers_unit_probe(n_layers=4, units=4, warmup=2):
+    """The layer-stack solver on the 640x368-class unit: n_layers attention
+    layers, each with its own 60,416-key ring (filled by this unit's append of
+    a 944-token slice per layer) and its own W_qkv / W_o, 4 solver steps.
+    Contents do not change the work, so tensors are drawn on the device
+    (weights scaled by d^-1/2)."""
+    import torch
+
+    import flow_matching_denoising_amd as fmd
+
+    H, hd, cap, T, n_q, n_audio = 40, 128, 64 * 944, 944, 928, 8
+    d = H * hd
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device=dev).manual_seed(11)
+    rnd = lambda *shape, scale=1.0: (torch.randn(shape, generator=g, device=dev) * scale).to(  # noqa: E731
+        torch.bfloat16)
+    caches, ks, vs, wq, wo = [], [], [], [], []
+    for _ in range(n_layers):
+        caches.append(fmd.KVCache(H, hd, cap, device=dev, k=rnd(H, cap, hd),
+                                  v=fmd.KVCache.logical_to_device_v(rnd(H, cap, hd)),
+                                  len_tokens=cap - T, head_tokens=cap - T))
+        ks.append(rnd(T, H, hd))
+        vs.append(rnd(T, H, hd))
+        wq.append(rnd(3 * d, d, scale=d ** -0.5))
+        wo.append(rnd(d, d, scale=d ** -0.5))
+    z = torch.randn((n_q, d), generator=g, device=dev)
+    hs = [0.25] * 4
+    io = fmd.UnitLayersIO(caches, z, hs, ks, vs, n_audio=n_audio)
+    ws = fmd.alloc_workspace(fmd.unit_layers_workspace_bytes([io]), dev)
+
+    def one():
+        for c in caches:
+            c.set_state(cap - T, cap - T)
+        fmd.denoise_unit_layers([io], wq, wo, ws)
+
+    for _ in range(warmup):
+        one()
+    torch.cuda.synchronize()
+    fmd.profile_enable(True)
+    t0 = time.perf_counter()
+    for _ in range(units):
+        one()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kt = {k: fmd.profile_read(k) for k in ("attn", "proj", "qkv", "append")}
+    fmd.profile_enable(False)
+    ring_bytes = 2 * H * cap * hd * 2
+    return {"layers": n_layers, "solver_steps": len(hs),
+            "units_per_s": round(units / wall, 3), "ms_per_unit": round(wall / units * 1e3, 3),
+            "layer_steps_per_s": round(units * n_layers * len(hs) / wall, 1),
+            "ring_GB_per_layer": round(ring_bytes / 1e9, 3),
             "per_kernel_us": {k: (round(v[0] / v[1] * 1e3, 2) if v[1] else None)
                               for k, v in kt.items()}}
 
@@ -463,6 +520,8 @@ def main():
         out["cfg_unit"] = cfg_unit_probe()
         torch.cuda.empty_cache()
         out["ulysses_rank_p8"] = ulysses_rank_probe(8)
+        torch.cuda.empty_cache()
+        out["layers_unit"] = layers_unit_probe(4)
         torch.cuda.empty_cache()
         out["append_batch8"] = append_batch_probe()
     if not args.no_cpu_baseline:
