@@ -71,6 +71,10 @@ int timed_launch(int cls, hipStream_t st, F&& launch) {
       a = take_event();
       b = take_event();
       rec = a && b;
+      if (!rec) {   // keep whichever was created for later
+        if (a) g_event_pool.push_back(a);
+        if (b) g_event_pool.push_back(b);
+      }
     }
   }
   if (rec) (void)hipEventRecord(a, st);
