@@ -838,16 +838,16 @@ static int run_solver(const std::vector<SolverUnit>& us, int nb, int n_layers, i
         pa.d = d;
         pa.n_out = 3 * d;
         pa.w = static_cast<const bf16*>(w_qkv[l]);
-        const int ntiles = (3 * d + kProjTileN - 1) / kProjTileN;
+        const int ntiles = (3 * d + kQkvTile - 1) / kQkvTile;
         for (int j = 0; j < cn; ++j) {
           const int i = c0 + j;
           const int n_q = us[i].n_video + us[i].n_audio;
-          const int mtiles = (n_q + kProjTile - 1) / kProjTile;
+          const int mtiles = (n_q + kQkvTile - 1) / kQkvTile;
           pa.s[j] = ProjSess{zb[i], nullptr, nullptr, nullptr, {q[i], k[i], v[i]}, n_q, mtiles,
                              pa.items, 0.f};
           pa.items += mtiles * ntiles;
         }
-        if ((rc = timed_launch(FMD_KERNEL_QKV, st, [&] { return launch_proj(pa, kProjQkv, st); })))
+        if ((rc = timed_launch(FMD_KERNEL_QKV, st, [&] { return launch_qkv_wide(pa, st); })))
           return rc;
       }
       std::vector<fmd_unit_step>& steps = L.steps[l];

@@ -208,6 +208,9 @@ hipError_t launch_combine(const CombineArgs& a, int head_dim, hipStream_t st);
 hipError_t launch_proj(const ProjArgs& a, int mode, hipStream_t st);
 hipError_t launch_cvt(const CvtArgs& a, hipStream_t st);
 hipError_t launch_mix(const MixArgs& a, hipStream_t st);
+// Q/K/V projection (kProjQkv semantics) with 256 x 256 tiles; ProjSess.n_mtiles
+// counts 256-row tiles.
+hipError_t launch_qkv_wide(const ProjArgs& a, hipStream_t st);
 
 // Attention tiling shared by host planning and the kernel.
 constexpr int kAttnWaves = 8;
@@ -219,5 +222,7 @@ constexpr int kAttnWindow = 64;                              // keys per window
 // Projection tiling: 160 rows x 128 output features per block.
 constexpr int kProjTile = 160;
 constexpr int kProjTileN = 128;
+// Q/K/V projection tiling: 256 rows x 256 output features per block.
+constexpr int kQkvTile = 256;
 
 }  // namespace fmd

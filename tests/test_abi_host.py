@@ -172,7 +172,7 @@ def test_device_code_has_no_packed_fp32_arithmetic():
     from flow_matching_denoising_amd import _build
     hipcc = _build._hipcc()
     with tempfile.TemporaryDirectory() as td:
-        for name in ("attention.hip", "proj_euler.hip", "kv_append.hip"):
+        for name in ("attention.hip", "proj_euler.hip", "kv_append.hip", "gemm_wide.hip"):
             out = os.path.join(td, name + ".s")
             cmd = [hipcc, *_build.COMMON, "--cuda-device-only", "-S",
                    os.path.join(_build.CSRC, name), "-o", out]
