@@ -140,7 +140,7 @@ struct CombineArgs {
 //   kProjEuler: n_out = d; z <- z - h * Y (fp32, in place), and, if zb is set,
 //               zb <- bf16(z) (the next step's projection input);
 //   kProjQkv:   n_out = 3d; column c of Y goes to out[c / d], column c % d,
-//               rounded to bf16 (the unit's Q, K_u, V_u);
+//               rounded to bf16 (the unit's Q, K_u, V_u; launch_qkv_wide);
 //   kProjLayer: n_out = d; a layer of a stack adds its update to the fp32
 //               residual r <- r + Y and writes zb <- bf16(z + r), the next
 //               layer's input;

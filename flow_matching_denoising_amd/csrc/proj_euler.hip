@@ -1,6 +1,6 @@
 // Velocity projection v = O * W^T on bf16 MFMA, with the rectified-flow Euler
-// update z <- z - h * v fused into the epilogue; the same GEMM, with a bf16
-// store epilogue, projects the latent to the unit's Q, K_u and V_u.
+// update z <- z - h * v fused into the epilogue (or, in a layer stack, the
+// residual update of one layer).
 //
 // One network predicts the velocity of both modalities, and along the linear
 // interpolation path that velocity is constant, so an ODE solver integrates
@@ -271,17 +271,6 @@ __global__ __launch_bounds__(WAVES * 64) void proj_kernel(ProjArgs a) {
         }
       }
     }
-  } else {
-    // Column n of Y is column n % d of Q, K_u or V_u, rounded to bf16.
-    const int t = n >= 2 * d ? 2 : (n >= d ? 1 : 0);
-    bf16* const oc = s.out[t] + (n - t * d);
-#pragma unroll
-    for (int i = 0; i < MT; ++i)
-#pragma unroll
-      for (int q = 0; q < 16; ++q) {
-        const int m = m0 + i * 32 + (q >> 2) * 8 + g * 4 + (q & 3);
-        if (full || m < n_q) oc[(int64_t)m * d] = (bf16)acc[i][q];
-      }
   }
 }
 
@@ -335,7 +324,6 @@ hipError_t launch_proj(const ProjArgs& a, int mode, hipStream_t st) {
   if (a.items <= 0) return hipSuccess;
   static const hipError_t attr_err = [] {
     const void* fns[] = {reinterpret_cast<const void*>(&proj_kernel<kProjEuler>),
-                         reinterpret_cast<const void*>(&proj_kernel<kProjQkv>),
                          reinterpret_cast<const void*>(&proj_kernel<kProjLayer>),
                          reinterpret_cast<const void*>(&proj_kernel<kProjLayerLast>)};
     hipError_t e = hipSuccess;
@@ -348,7 +336,6 @@ hipError_t launch_proj(const ProjArgs& a, int mode, hipStream_t st) {
   const dim3 grid(a.items), block(WAVES * 64);
   switch (mode) {
     case kProjEuler: hipLaunchKernelGGL(proj_kernel<kProjEuler>, grid, block, LDS_BYTES, st, a); break;
-    case kProjQkv: hipLaunchKernelGGL(proj_kernel<kProjQkv>, grid, block, LDS_BYTES, st, a); break;
     case kProjLayer: hipLaunchKernelGGL(proj_kernel<kProjLayer>, grid, block, LDS_BYTES, st, a); break;
     case kProjLayerLast:
       hipLaunchKernelGGL(proj_kernel<kProjLayerLast>, grid, block, LDS_BYTES, st, a);
