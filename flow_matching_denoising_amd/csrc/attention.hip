@@ -553,35 +553,37 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
   const float* lse = s.lse + rh;
   const bf16* part = s.opart + rh * HD + e0;
   const int ns = s.nsplit;
-  float mx = kNegInf;
-  for (int k = 0; k < ns; ++k) mx = fmaxf(mx, lse[k * stride]);
-  if (mx == kNegInf) mx = 0.f;             // no key at all: every weight is 0
+  // One pass in batches of 16 splits, every load of a batch issued before
+  // any is used; the running maximum rescales what is accumulated so far.
+  constexpr int B = 16;
+  float m = kNegInf, wsum = 0.f;
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  float wsum = 0.f;
-  // Four splits per round, their loads issued together.
-  int k = 0;
-  for (; k + 4 <= ns; k += 4) {
-    float l[4];
-    bf16x8 x[4];
+  for (int k0 = 0; k0 < ns; k0 += B) {
+    float l[B];
+    bf16x8 x[B];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      l[u] = lse[(k + u) * stride];
-      x[u] = *reinterpret_cast<const bf16x8*>(part + (k + u) * stride * HD);
+    for (int u = 0; u < B; ++u) {
+      const bool in = k0 + u < ns;
+      l[u] = in ? lse[(k0 + u) * stride] : kNegInf;
+      x[u] = in ? *reinterpret_cast<const bf16x8*>(part + (k0 + u) * stride * HD) : bf16x8{};
     }
+    float bm = l[0];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const float w = __builtin_amdgcn_exp2f(l[u] - mx);
+    for (int u = 1; u < B; ++u) bm = fmaxf(bm, l[u]);
+    const float m_new = fmaxf(m, bm);
+    if (m_new == kNegInf) continue;          // no key so far
+    const float c = __builtin_amdgcn_exp2f(m - m_new);   // 0 while m is -inf
+    wsum *= c;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) acc[t] *= c;
+#pragma unroll
+    for (int u = 0; u < B; ++u) {
+      const float w = __builtin_amdgcn_exp2f(l[u] - m_new);
       wsum += w;
 #pragma unroll
       for (int t = 0; t < 8; ++t) acc[t] += w * (float)x[u][t];
     }
-  }
-  for (; k < ns; ++k) {
-    const float w = __builtin_amdgcn_exp2f(lse[k * stride] - mx);
-    wsum += w;
-    const bf16x8 x = *reinterpret_cast<const bf16x8*>(part + k * stride * HD);
-#pragma unroll
-    for (int t = 0; t < 8; ++t) acc[t] += w * (float)x[t];
+    m = m_new;
   }
   const float inv = wsum > 0.f ? 1.0f / wsum : 0.f;
   bf16x8 out;
