@@ -143,6 +143,24 @@ int check_same_shape(const fmd_kv_cache* c0, const fmd_kv_cache* c, int idx) {
   return FMD_OK;
 }
 
+// The sessions' latents are written in place: their fp32 [n_q][d] ranges must
+// not overlap (two sessions updating the same z would race).
+struct ZRange {
+  uintptr_t lo, hi;
+  int idx;
+};
+int check_disjoint_z(std::vector<ZRange> zs) {
+  std::sort(zs.begin(), zs.end(), [](const ZRange& a, const ZRange& b) { return a.lo < b.lo; });
+  for (size_t k = 1; k < zs.size(); ++k)
+    if (zs[k].lo < zs[k - 1].hi)
+      return fail(FMD_E_INVAL, "sessions %d and %d: latents z overlap", zs[k - 1].idx, zs[k].idx);
+  return FMD_OK;
+}
+ZRange z_range(const float* z, int64_t n_q, int d, int idx) {
+  const uintptr_t lo = reinterpret_cast<uintptr_t>(z);
+  return ZRange{lo, lo + (uintptr_t)n_q * d * sizeof(float), idx};
+}
+
 // ---------------------------------------------------------------------------
 // Planning.
 // ---------------------------------------------------------------------------
@@ -334,11 +352,14 @@ int validate_steps(const fmd_unit_step* units, int n, bool need_z) {
   if (n < 1 || n > FMD_MAX_SESSIONS)
     return fail(FMD_E_INVAL, "n_units=%d (must be 1..%d)", n, FMD_MAX_SESSIONS);
   int rc;
+  std::vector<ZRange> zs;
   for (int i = 0; i < n; ++i) {
     if ((rc = check_step(&units[i], i, need_z))) return rc;
     if (i && (rc = check_same_shape(units[0].cache, units[i].cache, i))) return rc;
+    const int d = units[i].cache->n_heads * units[i].cache->head_dim;
+    if (need_z) zs.push_back(z_range(units[i].z, units[i].n_video + units[i].n_audio, d, i));
   }
-  return FMD_OK;
+  return check_disjoint_z(zs);
 }
 
 int check_workspace(void* ws, size_t have, size_t need) {
@@ -647,7 +668,11 @@ static int validate_unit_io(const fmd_unit_io* ss, int n, int n_steps) {
     fmd_unit_step u = {s.cache, s.q, s.k_u, s.v_u, s.z, s.n_video, s.n_audio, s.h[0]};
     if ((rc = check_step(&u, i, true))) return rc;
   }
-  return FMD_OK;
+  std::vector<ZRange> zs;
+  for (int i = 0; i < n; ++i)
+    zs.push_back(z_range(ss[i].z, ss[i].n_video + ss[i].n_audio,
+                         ss[i].cache->n_heads * ss[i].cache->head_dim, i));
+  return check_disjoint_z(zs);
 }
 
 // The post-append ring states of a unit's sessions (for planning).
@@ -934,7 +959,11 @@ static int validate_unit_qkv(const fmd_unit_qkv_io* ss, int n, int n_steps) {
     if ((rc = check_unit_slice(s.cache, s.k_slice, s.v_slice, s.slice_tokens, i))) return rc;
     if ((rc = check_unit_latent(s.z, s.n_video, s.n_audio, s.h, n_steps, i))) return rc;
   }
-  return FMD_OK;
+  std::vector<ZRange> zs;
+  for (int i = 0; i < n; ++i)
+    zs.push_back(z_range(ss[i].z, ss[i].n_video + ss[i].n_audio,
+                         ss[i].cache->n_heads * ss[i].cache->head_dim, i));
+  return check_disjoint_z(zs);
 }
 
 static std::vector<SolverUnit> qkv_units(const fmd_unit_qkv_io* ss, int n) {
@@ -1013,7 +1042,11 @@ static int validate_unit_cfg(const fmd_unit_cfg_io* ss, int n, int n_steps) {
     if (!isfinite(s.guidance))
       return fail(FMD_E_INVAL, "session %d: guidance %g is not finite", i, s.guidance);
   }
-  return FMD_OK;
+  std::vector<ZRange> zs;
+  for (int i = 0; i < n; ++i)
+    zs.push_back(z_range(ss[i].z, ss[i].n_video + ss[i].n_audio,
+                         ss[i].cond->n_heads * ss[i].cond->head_dim, i));
+  return check_disjoint_z(zs);
 }
 
 static std::vector<SolverUnit> cfg_units(const fmd_unit_cfg_io* ss, int n) {
@@ -1098,7 +1131,11 @@ static int validate_unit_layers(const fmd_unit_layers_io* ss, int n, int n_layer
   std::sort(seen.begin(), seen.end());
   if (std::adjacent_find(seen.begin(), seen.end()) != seen.end())
     return fail(FMD_E_INVAL, "a cache appears twice among the sessions' layers");
-  return FMD_OK;
+  std::vector<ZRange> zs;
+  for (int i = 0; i < n; ++i)
+    zs.push_back(z_range(ss[i].z, ss[i].n_video + ss[i].n_audio,
+                         ss[i].caches[0]->n_heads * ss[i].caches[0]->head_dim, i));
+  return check_disjoint_z(zs);
 }
 
 static std::vector<SolverUnit> layer_units(const fmd_unit_layers_io* ss, int n, int n_layers) {

@@ -325,3 +325,32 @@ def test_unit_layers_workspace():
     assert fmd._unit_qkv_workspace_bytes((_UnitQkvIO * 1)(qio), 1, ctypes.byref(q)) == 0
     assert ws(1) == q.value                              # one layer: the z-dependent solver
     assert ws(3) == ws(2) >= q.value + 928 * 5120 * 4    # plus the fp32 residual, rings alike
+
+
+def test_overlapping_latents_are_rejected():
+    # Two sessions whose fp32 latents overlap would race in the in-place
+    # update: every solver entry point rejects them before anything runs.
+    from flow_matching_denoising_amd import _UnitCfgIO, _UnitLayersIO, _UnitQkvIO
+    a, b, c, e = _cache(), _cache(), _cache(), _cache()
+    h = (ctypes.c_float * 1)(0.5)
+    hp = ctypes.cast(h, ctypes.POINTER(ctypes.c_float))
+    d = 2 * 64
+    near = FAKE + 8 * d * 4            # inside the first session's 16 x d floats
+    apart = FAKE + 16 * d * 4          # right after it: allowed
+    arr = (_UnitStep * 2)(_step(a, z=FAKE), _step(b, z=near))
+    assert fmd._denoise_step(arr, 2, FAKE, FAKE, 1 << 30, None) == -1
+    q = (_UnitQkvIO * 2)(_UnitQkvIO(ctypes.pointer(a), FAKE, FAKE, 0, FAKE, 12, 4, hp),
+                         _UnitQkvIO(ctypes.pointer(b), FAKE, FAKE, 0, near, 12, 4, hp))
+    assert fmd._denoise_unit_qkv(q, 2, 1, FAKE, FAKE, FAKE, 1 << 30, None) == -1
+    g = (_UnitCfgIO * 2)(_cfg_io(a, b, h, ct=0, z=FAKE), _cfg_io(c, e, h, ct=0, z=near))
+    assert fmd._denoise_unit_cfg(g, 2, 1, FAKE, FAKE, FAKE, 1 << 30, None) == -1
+    lay = (_UnitLayersIO * 2)(_layers_io([a], h, z=FAKE), _layers_io([b], h, z=near))
+    w = (ctypes.c_void_p * 1)(FAKE)
+    assert fmd._denoise_unit_layers(lay, 2, 1, 1, w, w, FAKE, 1 << 30, None) == -1
+    assert "overlap" in fmd._last_error().decode()
+    out = ctypes.c_size_t(0)
+    ok = (_UnitQkvIO * 2)(_UnitQkvIO(ctypes.pointer(a), FAKE, FAKE, 0, FAKE, 12, 4, hp),
+                          _UnitQkvIO(ctypes.pointer(b), FAKE, FAKE, 0, apart, 12, 4, hp))
+    assert fmd._unit_qkv_workspace_bytes(ok, 2, ctypes.byref(out)) == 0
+    for x in (a, b, c, e):
+        assert (x.len_tokens, x.head_tokens) == (96, 96)
