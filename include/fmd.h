@@ -133,7 +133,8 @@ int fmd_workspace_bytes(const fmd_unit_step* units, int32_t n_units, size_t* out
  *   z <- z - h * v  (fp32).
  *   w_o: bf16 [d][d] stored [d_out][d_in], d = n_heads*head_dim, shared.
  *   workspace: device scratch of at least fmd_workspace_bytes() bytes.
- * Errors: FMD_E_INVAL, FMD_E_SHAPE, FMD_E_ALIGN, FMD_E_WORKSPACE, FMD_E_HIP.
+ * Errors: FMD_E_INVAL (also when two sessions' latents z overlap: each is
+ * updated in place), FMD_E_SHAPE, FMD_E_ALIGN, FMD_E_WORKSPACE, FMD_E_HIP.
  */
 int fmd_denoise_step(const fmd_unit_step* units, int32_t n_units, const void* w_o,
                      void* workspace, size_t workspace_bytes, void* stream);
