@@ -16,6 +16,13 @@
  *  - fmd_denoise_unit: one unit = the append, then the flow-matching solver
  *    [same page, Fig. 2: the performer receives the slice and only runs the
  *    solver].
+ *  - fmd_denoise_unit_qkv: the solver with the unit's Q, K, V projected from
+ *    the current latent at every step [same page, 3.4].
+ *  - fmd_denoise_unit_cfg: the classifier-free-guided sampler of the teacher
+ *    the deployed performer is distilled from [same page, training stages,
+ *    Stage 3].
+ *  - fmd_denoise_unit_layers: the solver over a stack of attention layers,
+ *    one ring per layer [same page, 3.3 and 3.4].
  *
  * Conventions shared by every call
  *  - Tensor pointers are DEVICE pointers owned by the caller.  The library
