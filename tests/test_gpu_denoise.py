@@ -221,3 +221,26 @@ def test_v02_batch8_ragged_sessions_sampled_rows():
     # append offsets, one batched call as the benchmark would time it; the
     # oracle checks the shortest ring, a long one and the longest (wrapped).
     _sampled_unit_check("v02_batch8", [0, 300, 767, 919, 927], sessions=[1, 3, 5])
+
+
+def test_maximum_session_count_four_launch_chunks():
+    # FMD_MAX_SESSIONS sessions in one call: four launches of 16 sessions
+    # each, ragged query counts, ring states (empty, partial, wrapped, full)
+    # and slices, every session checked against the oracle.
+    rng = np.random.default_rng(64)
+    shapes = []
+    for i in range(64):
+        n_v, n_a = int(rng.integers(1, 48)), int(rng.integers(0, 5))
+        cap = int(rng.integers(2, 9)) * 32
+        T = int(rng.integers(0, 2)) * int(rng.integers(1, 33))
+        ln = int(rng.integers(0, cap + 1)) if i % 5 else 0
+        head = int(rng.integers(0, cap))
+        shapes.append(workload.custom_session(2, 64, n_v, n_a, T, cap, ln, head, (0.6, 0.4)))
+    wl = workload.custom_workload("max_sessions", 64, shapes)
+    ui, caches, zs = _run_unit(wl)
+    for i, (si, c, z) in enumerate(zip(ui.sessions, caches, zs)):
+        ref = _oracle_unit(ui, si)
+        assert_close(host_f64(z) - si.eps, ref["z"] - si.eps, f"session {i} dz")
+        gk, gv = cache_logical(fmd, c)
+        assert np.array_equal(gk, ref["ring_k"]) and np.array_equal(gv, ref["ring_v"])
+        assert (c.len_tokens, c.head_tokens) == (ref["length"], ref["head"])
