@@ -231,12 +231,13 @@ int env_int(const char* name, int dflt) {
 
 // Key splits.  The item size (64-key windows per work item) trades the
 // dispatch tail against the combine pass, which reads every split's partial
-// output once.  Candidates of 1..40 dispatch rounds are scored with a model of
-// the launch: every XCD takes an equal contiguous range of the head-major item
-// order (xcd_remap), and its 32 CUs take the range's items in order, each the
-// next free CU (greedy list scheduling); the score is that range's finish time
-// plus the combine work, both in units of one window of one item.  Depends only
-// on the shapes.  FMD_ATTN_SPLIT forces a split count per session,
+// output once.  Candidate item counts (every 32 up to 2048 items, then every
+// 256 up to 40 dispatch rounds of the chip) are scored with a model of the
+// launch: every XCD takes a contiguous range of the head-major item order
+// (xcd_remap), and its 32 CUs take the range's items in order, each the next
+// free CU (greedy list scheduling); the score is the slowest XCD's finish time
+// plus the combine work, both in units of one window of one item.  Depends
+// only on the shapes.  FMD_ATTN_SPLIT forces a split count per session,
 // FMD_ATTN_TARGET_ITEMS a target item count (both for experiments).
 int plan_split_count(const SessPlan& p, double per_item) {
   constexpr int kMinWindows = 16;
@@ -264,8 +265,21 @@ void session_order(const SessPlan* plans, int n, int* order) {
   std::stable_sort(order, order + n, [&](int x, int y) { return len[x] > len[y]; });
 }
 
-double score_plan(const std::vector<SessPlan>& plans, int H) {
+// Finish time of one XCD whose range is `cnt` items of the periodic order
+// `seq`, starting at position `first` of the period.
+double simulate_range(const std::vector<int>& seq, int64_t first, int64_t cnt) {
   constexpr double kItemOverhead = 2.0;   // Q load, pipeline fill, O/LSE store
+  std::vector<double> cu(kTargetCUs / kNumXcd, 0.0);   // min-heap of finish times
+  const int64_t period = (int64_t)seq.size();
+  for (int64_t i = 0; i < cnt; ++i) {
+    std::pop_heap(cu.begin(), cu.end(), std::greater<double>());
+    cu.back() += seq[(first + i) % period] + kItemOverhead;
+    std::push_heap(cu.begin(), cu.end(), std::greater<double>());
+  }
+  return *std::max_element(cu.begin(), cu.end());
+}
+
+double score_plan(const std::vector<SessPlan>& plans, int H) {
   constexpr double kCombinePerSplit = 1.3;   // per split of a 928-query session
   std::vector<int> seq;   // windows of one head's items, launch order
   double combine = 0;
@@ -279,16 +293,26 @@ double score_plan(const std::vector<SessPlan>& plans, int H) {
       if (p.nsplit > 1) combine += kCombinePerSplit * p.nsplit * p.n_q / 928.0;
     }
   }
-  const int cus = kTargetCUs / kNumXcd;
-  const int64_t n = (int64_t)H * seq.size();
-  const int64_t range = (n + kNumXcd - 1) / kNumXcd;   // XCD 0's range
-  std::vector<double> cu(cus, 0.0);                      // min-heap of finish times
-  for (int64_t i = 0; i < range; ++i) {
-    std::pop_heap(cu.begin(), cu.end(), std::greater<double>());
-    cu.back() += seq[i % seq.size()] + kItemOverhead;
-    std::push_heap(cu.begin(), cu.end(), std::greater<double>());
+  // XCD ranges as xcd_remap cuts them.  Ranges that start at the same point of
+  // the per-head period and have the same length finish together: each
+  // distinct one is simulated once (with H a multiple of 8, all are alike).
+  const int64_t period = (int64_t)seq.size();
+  const int64_t n = (int64_t)H * period;
+  const int64_t per = (n + kNumXcd - 1) / kNumXcd;
+  const int tall = n % kNumXcd == 0 ? kNumXcd : (int)(n % kNumXcd);
+  std::vector<std::pair<int64_t, int64_t>> seen;
+  double worst = 0;
+  int64_t start = 0;
+  for (int x = 0; x < kNumXcd; ++x) {
+    const int64_t cnt = x < tall ? per : per - 1;
+    const std::pair<int64_t, int64_t> key(start % period, cnt);
+    if (cnt > 0 && std::find(seen.begin(), seen.end(), key) == seen.end()) {
+      seen.push_back(key);
+      worst = std::max(worst, simulate_range(seq, key.first, cnt));
+    }
+    start += cnt;
   }
-  return *std::max_element(cu.begin(), cu.end()) + combine;
+  return worst + combine;
 }
 
 void choose_splits(std::vector<SessPlan>& plans, int H) {
@@ -300,17 +324,23 @@ void choose_splits(std::vector<SessPlan>& plans, int H) {
   double work = 0;
   for (auto& p : plans) work += (double)H * p.n_qblk * p.nwin_total;
   const int target_env = env_int("FMD_ATTN_TARGET_ITEMS", 0);
+  if (target_env > 0) {
+    for (auto& p : plans) set_splits(p, plan_split_count(p, work / target_env));
+    return;
+  }
   double best_cost = 1e300, best_per_item = work;
-  for (int rounds = 1; rounds <= 40; ++rounds) {
-    const int target = target_env > 0 ? target_env : rounds * kTargetCUs;
+  std::vector<int> counts(plans.size()), last;
+  for (int target = 32; target <= 40 * kTargetCUs; target += target < 2048 ? 32 : 256) {
     const double per_item = work / target;
-    for (auto& p : plans) set_splits(p, plan_split_count(p, per_item));
+    for (size_t i = 0; i < plans.size(); ++i) counts[i] = plan_split_count(plans[i], per_item);
+    if (counts == last) continue;   // same plan as the previous candidate
+    last = counts;
+    for (size_t i = 0; i < plans.size(); ++i) set_splits(plans[i], counts[i]);
     const double cost = score_plan(plans, H);
     if (cost < best_cost - 1e-9) {
       best_cost = cost;
       best_per_item = per_item;
     }
-    if (target_env > 0) break;
   }
   for (auto& p : plans) set_splits(p, plan_split_count(p, best_per_item));
 }
