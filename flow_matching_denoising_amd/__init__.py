@@ -128,6 +128,7 @@ _denoise_unit_layers = _sig("fmd_denoise_unit_layers", ctypes.c_int, ctypes.POIN
 _strerror = _sig("fmd_strerror", ctypes.c_char_p, ctypes.c_int)
 _last_error = _sig("fmd_last_error", ctypes.c_char_p)
 _profile_enable = _sig("fmd_profile_enable", ctypes.c_int, ctypes.c_int)
+_profile_select = _sig("fmd_profile_select", ctypes.c_int, ctypes.c_uint32)
 _profile_read = _sig("fmd_profile_read", ctypes.c_int, ctypes.c_int,
                      ctypes.POINTER(ctypes.c_double), ctypes.POINTER(_i64))
 _version = _sig("fmd_version", ctypes.c_char_p)
@@ -137,7 +138,8 @@ EXPORTED = ["fmd_kv_append", "fmd_kv_append_batched", "fmd_workspace_bytes", "fm
             "fmd_unit_qkv_workspace_bytes", "fmd_denoise_unit_qkv",
             "fmd_unit_cfg_workspace_bytes", "fmd_denoise_unit_cfg",
             "fmd_unit_layers_workspace_bytes", "fmd_denoise_unit_layers", "fmd_strerror",
-            "fmd_last_error", "fmd_profile_enable", "fmd_profile_read", "fmd_version"]
+            "fmd_last_error", "fmd_profile_enable", "fmd_profile_select", "fmd_profile_read",
+            "fmd_version"]
 
 
 def _check(rc: int):
@@ -521,7 +523,15 @@ def denoise_unit_layers(sessions, w_qkv, w_o, workspace=None, stream=None):
                                 workspace.numel(), _stream_ptr(stream)))
 
 
-def profile_enable(on: bool = True):
+def profile_enable(on: bool = True, classes=None):
+    """Turn per-launch event timing on (clearing earlier records) or off.
+    `classes`: names from KERNEL_CLASSES to record (default: all)."""
+    mask = (1 << len(KERNEL_CLASSES)) - 1
+    if classes is not None:
+        mask = 0
+        for c in classes:
+            mask |= 1 << KERNEL_CLASSES[c]
+    _check(_profile_select(mask))
     _check(_profile_enable(1 if on else 0))
 
 

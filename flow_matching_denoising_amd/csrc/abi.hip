@@ -47,6 +47,7 @@ struct ProfRec {
 };
 std::mutex g_prof_mu;
 bool g_prof_on = false;
+uint32_t g_prof_mask = (1u << FMD_KERNEL_COUNT) - 1;
 std::vector<ProfRec> g_prof;
 std::vector<hipEvent_t> g_event_pool;
 
@@ -57,7 +58,8 @@ hipEvent_t take_event() {
     return e;
   }
   hipEvent_t e = nullptr;
-  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  // Timing only: no system-scope fence (no cache writeback or invalidate).
+  if (hipEventCreateWithFlags(&e, hipEventDisableSystemFence) != hipSuccess) return nullptr;
   return e;
 }
 
@@ -67,7 +69,7 @@ int timed_launch(int cls, hipStream_t st, F&& launch) {
   bool rec = false;
   {
     std::lock_guard<std::mutex> lk(g_prof_mu);
-    if (g_prof_on) {
+    if (g_prof_on && ((g_prof_mask >> cls) & 1u)) {
       a = take_event();
       b = take_event();
       rec = a && b;
@@ -1230,6 +1232,15 @@ int fmd_profile_enable(int enable) {
   }
   g_prof.clear();
   g_prof_on = enable != 0;
+  return FMD_OK;
+}
+
+int fmd_profile_select(uint32_t class_mask) {
+  if (class_mask >> FMD_KERNEL_COUNT)
+    return fail(FMD_E_INVAL, "class mask 0x%x has bits at or above %d", class_mask,
+                FMD_KERNEL_COUNT);
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  g_prof_mask = class_mask;
   return FMD_OK;
 }
 

@@ -352,11 +352,21 @@ enum {
 };
 
 /* Per-launch timing with HIP events recorded on the launch stream around
- * every kernel of the classes above.  enable != 0 turns recording on (and
+ * every kernel of the selected classes above (all of them unless
+ * fmd_profile_select narrowed the set).  enable != 0 turns recording on (and
  * clears earlier records); fmd_profile_read waits for the recorded events and
- * returns the summed duration in ms and the launch count of one class. */
+ * returns the summed duration in ms and the launch count of one class.  The
+ * events are created without a system-scope fence (timing only); each
+ * recorded launch still adds a few microseconds of queue time around it, which
+ * is why a caller timing a whole unit may record one class only. */
 int fmd_profile_enable(int enable);
 int fmd_profile_read(int kernel_class, double* total_ms, int64_t* launches);
+
+/* Kernel classes recorded while profiling is on: bit c of class_mask selects
+ * class c (default: every class).  Bits at or above FMD_KERNEL_COUNT ->
+ * FMD_E_INVAL.  Takes effect for launches enqueued after the call; records
+ * already taken are kept. */
+int fmd_profile_select(uint32_t class_mask);
 
 /* Library version, "major.minor.patch". */
 const char* fmd_version(void);

@@ -354,3 +354,13 @@ def test_overlapping_latents_are_rejected():
     assert fmd._unit_qkv_workspace_bytes(ok, 2, ctypes.byref(out)) == 0
     for x in (a, b, c, e):
         assert (x.len_tokens, x.head_tokens) == (96, 96)
+
+
+def test_profile_select_rejects_unknown_classes():
+    n = len(fmd.KERNEL_CLASSES)
+    assert fmd._profile_select(1 << n) == -1
+    assert fmd._last_error().decode()
+    assert fmd._profile_select(0xFFFFFFFF) == -1
+    assert fmd._profile_select((1 << n) - 1) == 0
+    assert fmd._profile_select(0) == 0
+    assert fmd._profile_select((1 << n) - 1) == 0
