@@ -24,9 +24,13 @@
 // so P never leaves the registers.  V^T rows are permuted so that each lane's
 // 16 output registers hold 16 consecutive features of its query.
 //
-// Softmax rescaling is lazy: O and the running sum are rescaled only when a
-// row maximum grows by more than 2^8 (in exp2 units), which is exact (the same
-// shift multiplies numerator and denominator) and bounds p <= 256.
+// Q^T is multiplied by scale * log2(e) (and rounded to bf16) once per work
+// item, and every QK product after the first window starts its accumulation
+// from -m (m: the row's running maximum), so the MFMA returns the shifted
+// score in exp2 units and exp2 takes it as it is: no per-score FMA.  Softmax
+// rescaling is lazy: m, O and the running sum move only when a row maximum
+// grows by more than 2^8, which is exact (the same shift multiplies numerator
+// and denominator) and bounds p <= 256.
 #include "fmd_internal.h"
 
 namespace fmd {
@@ -71,7 +75,7 @@ struct Tiles {
   static constexpr int V_BLOCKS = V_BYTES / 1024;
   static constexpr int K_PER_WAVE = K_BLOCKS / kAttnWaves;
   static constexpr int V_PER_WAVE = V_BLOCKS / kAttnWaves;
-  static constexpr int STAGES = 3;                       // K and V triple-buffered
+  static constexpr int STAGES = 4;                       // K and V quadruple-buffered
   static constexpr int LDS_BYTES = STAGES * (K_BYTES + V_BYTES);
 };
 
@@ -231,27 +235,37 @@ __device__ __forceinline__ void mask_scores(f32x16 (&s)[2], const Window& win) {
     }
 }
 
-// Row maximum of a window's scores for this lane's query, in exp2 units.
-__device__ __forceinline__ float row_max(const f32x16 (&s)[2], float scale_log2) {
+// Row maximum of a window's scores for this lane's query.
+__device__ __forceinline__ float row_max(const f32x16 (&s)[2]) {
   float m = fmaxf(s[0][0], s[1][0]);
 #pragma unroll
   for (int r = 1; r < 16; ++r) m = max3f(m, s[0][r], s[1][r]);
-  return max_xor32(m) * scale_log2;
+  return max_xor32(m);
 }
 
-// Lazy rescale: only when some row's maximum grew by more than the threshold.
+// Lazy rescale on shifted scores (score minus the running maximum m, which
+// the QK product starts from); mx is a window's shifted row maximum.  When
+// some row grew past the threshold, every row's m moves up by max(mx, 0), and
+// O, the row sum, the window's shifted scores and the QK start value (negm,
+// -m in every register) follow.
 template <int HB>
-__device__ __forceinline__ void maybe_rescale(float mx, f32x16 (&o)[HB], float& m_run,
-                                              float& l_run) {
-  if (__ballot(mx > m_run + kRescaleThreshold)) {
-    const float m_new = fmaxf(m_run, mx);
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-    m_run = m_new;
+__device__ __forceinline__ void maybe_rescale(float mx, f32x16 (&o)[HB], f32x16 (&s)[2],
+                                              f32x16& negm, float& m_run, float& l_run) {
+  if (__ballot(mx > kRescaleThreshold)) {
+    const float dm = fmaxf(mx, 0.f);
+    const float alpha = __builtin_amdgcn_exp2f(-dm);
+    m_run += dm;
     l_run *= alpha;
 #pragma unroll
     for (int hb = 0; hb < HB; ++hb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) o[hb][r] *= alpha;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[kb][r] -= dm;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) negm[r] = -m_run;
   }
 }
 
@@ -309,7 +323,7 @@ void attn_kernel(AttnArgs a) {
   const int lane = threadIdx.x & 63;
   const int j32 = lane & 31, g = lane >> 5;
   const int row0 = qblk * kAttnBlockM + wave * kAttnRowsPerWave;
-  const bool active = row0 < s.n_q;                   // wave-uniform
+  const bool active = __builtin_amdgcn_readfirstlane(row0 < s.n_q ? 1 : 0) != 0;   // wave-uniform
   const int qrow = row0 + j32;
 
   // Loop-invariant lane offsets (bytes) of the window loads.
@@ -336,15 +350,18 @@ void attn_kernel(AttnArgs a) {
     return *reinterpret_cast<const bf16x8*>(kt + kb * 64 * HD + kroff[kc]);
   };
 
-  // Prologue: K(0), V(0), K(1), V(1), K(2).
+  // Prologue: K(0), V(0), K(1), V(1), K(2), V(2), K(3).
   const Window w0 = win(0);
   load_tile<HD, true>(rk, w0.start, kbuf(0), koff, wave);
   load_tile<HD, true>(rv, w0.start, vbuf(0), voff, wave);
-  if (nw > 1) {
-    load_tile<HD, true>(rk, w0.start + kAttnWindow, kbuf(1), koff, wave);
-    load_tile<HD, true>(rv, w0.start + kAttnWindow, vbuf(1), voff, wave);
+#pragma unroll
+  for (int t = 1; t < 3; ++t) {
+    if (t < nw) {
+      load_tile<HD, true>(rk, w0.start + t * kAttnWindow, kbuf(t), koff, wave);
+      load_tile<HD, true>(rv, w0.start + t * kAttnWindow, vbuf(t), voff, wave);
+    }
   }
-  if (nw > 2) load_tile<HD, true>(rk, w0.start + 2 * kAttnWindow, kbuf(2), koff, wave);
+  if (nw > 3) load_tile<HD, true>(rk, w0.start + 3 * kAttnWindow, kbuf(3), koff, wave);
 
   // Q^T operand: lane (j, g) holds query row0+j, features 16kc+8g..+7.
   bf16x8 qr[T::KC];
@@ -353,47 +370,79 @@ void attn_kernel(AttnArgs a) {
     qr[kc] = qrow < s.n_q ? *reinterpret_cast<const bf16x8*>(
                                 s.q + ((int64_t)qrow * H + h) * HD + kc * 16 + g * 8)
                           : bf16x8{};
+  // Q^T pre-scaled by scale * log2(e): scores leave the MFMA in exp2 units.
+#pragma unroll
+  for (int kc = 0; kc < T::KC; ++kc)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) qr[kc][e] = (bf16)((float)qr[kc][e] * scale_log2);
 
   f32x16 o[T::HB];
 #pragma unroll
   for (int hb = 0; hb < T::HB; ++hb) o[hb] = f32x16{};
   float m_run = kNegInf, l_run = 0.f;
-  f32x16 s_cur[2];
+  f32x16 sA[2], sB[2];   // shifted scores of two windows (alternate steps)
+  f32x16 negm;           // -m_run in every register: the QK product's start value
+  // Per step: NQK + NPV MFMA slots; operand reads run D slots ahead in a ring
+  // of R registers, and the first D reads of a step are issued at the end of
+  // the step before (across its barrier).
+  constexpr int NQK = 2 * T::KC;
+  constexpr int NPV = 4 * T::HB;
+  constexpr int N = NQK + NPV;
+  constexpr int D = 3;                  // operand read distance (slots)
+  constexpr int R = D + 1;              // operand ring size
+  static_assert(N % R == 0, "the ring position of slot 0 repeats every step");
+  bf16x8 opr[R];
 
   wait_loads_and_sync<0>();
   // Window 0's invalid values are zeroed here; step 0's barrier publishes it.
   if (!w0.full) zero_invalid_v<HD>(vbuf(0), w0);
   if (active) {
-    s_cur[0] = s_cur[1] = f32x16{};
+    sA[0] = sA[1] = f32x16{};
 #pragma unroll
     for (int kc = 0; kc < T::KC; ++kc)
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
-        s_cur[kb] = mfma32x32x16(kread(kbuf(0), kb, kc), qr[kc], s_cur[kb]);
-    if (!w0.full) mask_scores(s_cur, w0);
-    maybe_rescale<T::HB>(row_max(s_cur, scale_log2), o, m_run, l_run);
+        sA[kb] = mfma32x32x16(kread(kbuf(0), kb, kc), qr[kc], sA[kb]);
+    if (!w0.full) mask_scores(sA, w0);
+    m_run = row_max(sA);   // finite: window 0 holds a valid key
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sA[kb][r] -= m_run;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) negm[r] = -m_run;
+#pragma unroll
+    for (int i = 0; i < D; ++i) opr[i] = kread(kbuf(1), 0, i);
   }
 
   // Step j: softmax and P*V of window j, scores of window j+1, with the loads
-  // of K(j+3) and V(j+2) in flight.  On entry s_cur holds window j's (masked)
-  // scores with m_run already updated for them; K(j+1) and V(j) were issued
-  // in step j-2 (or the prologue), K(j+2) and V(j+1) in step j-1.
-  // Steady steps (j + 5 <= nw) touch only full windows, issue every load and
-  // wait for a constant count: no branch but the rare rescale.  The last
-  // steps (TAIL) handle partial windows and the end of the pipeline.
-  // `stage` = j % 3 (a literal in the steady loop, folded after inlining).
-  auto step = [&](const int j, const int stage, const bool TAIL) __attribute__((always_inline)) {
-    const int st1 = stage == 2 ? 0 : stage + 1;   // (j+1) % 3
-    const int st2 = st1 == 2 ? 0 : st1 + 1;       // (j+2) % 3
+  // of K(j+3), K(j+4) and V(j+2), V(j+3) in flight (four LDS stages each).
+  // On entry window j's shifted (and masked) scores are in sA (j even) or sB
+  // (j odd), with m_run already updated for them, and the first D operands of
+  // QK(j+1) are in the ring.  Steady steps (j + 6 <= nw) touch only full
+  // windows, issue every load and wait for a constant count: no branch but the
+  // rare rescale.  The last steps (TAIL) handle partial windows and the end
+  // of the pipeline.  `stage` = j % 4 and PAR = j % 2 are literals after
+  // inlining.
+  auto step = [&](const int j, const int stage, const bool TAIL, const bool PAR)
+                  __attribute__((always_inline)) {
+    f32x16 (&sc)[2] = PAR ? sB : sA;   // window j (its P*V this step)
+    f32x16 (&sn)[2] = PAR ? sA : sB;   // window j+1 (its QK this step)
+    const int st1 = (stage + 1) & 3, st2 = (stage + 2) & 3, st3 = (stage + 3) & 3;
+    // On entry K(j+2) and V(j) must have landed (K(j+2) for the reads that
+    // end this step); loads are issued K before V, so the ones that may still
+    // be in flight are V(j+1) (step j-2), K(j+3) and V(j+2) (step j-1).
     if (!TAIL) {
-      wait_loads_and_sync<T::K_PER_WAVE + T::V_PER_WAVE>();
-      // K(j+3) -> the buffer of K(j) (read by QK(j) in step j-1);
-      // V(j+2) -> the buffer of V(j-1) (read by P*V(j-1)).
-      load_tile<HD, false>(rk, sp.start0 + (j + 3) * kAttnWindow, kbuf(stage), koff, wave);
-      load_tile<HD, false>(rv, sp.start0 + (j + 2) * kAttnWindow, vbuf(st2), voff, wave);
+      wait_loads_and_sync<2 * T::V_PER_WAVE + T::K_PER_WAVE>();
+      // K(j+4) -> the buffer of K(j) (read by QK(j) in step j-1);
+      // V(j+3) -> the buffer of V(j-1) (read by P*V(j-1)).
+      load_tile<HD, false>(rk, sp.start0 + (j + 4) * kAttnWindow, kbuf(stage), koff, wave);
+      load_tile<HD, false>(rv, sp.start0 + (j + 3) * kAttnWindow, vbuf(st3), voff, wave);
     } else {
-      if (j + 2 < nw)
-        wait_loads_and_sync<T::K_PER_WAVE + T::V_PER_WAVE>();
+      if (j + 3 < nw)
+        wait_loads_and_sync<2 * T::V_PER_WAVE + T::K_PER_WAVE>();
+      else if (j + 2 < nw)
+        wait_loads_and_sync<2 * T::V_PER_WAVE>();
       else if (j + 1 < nw)
         wait_loads_and_sync<T::V_PER_WAVE>();
       else
@@ -405,51 +454,36 @@ void attn_kernel(AttnArgs a) {
           __syncthreads();
         }
       }
+      if (j + 4 < nw)
+        load_tile<HD, true>(rk, sp.start0 + (j + 4) * kAttnWindow, kbuf(stage), koff, wave);
       if (j + 3 < nw)
-        load_tile<HD, true>(rk, sp.start0 + (j + 3) * kAttnWindow, kbuf(stage), koff, wave);
-      if (j + 2 < nw)
-        load_tile<HD, true>(rv, sp.start0 + (j + 2) * kAttnWindow, vbuf(st2), voff, wave);
+        load_tile<HD, true>(rv, sp.start0 + (j + 3) * kAttnWindow, vbuf(st3), voff, wave);
     }
     if (active) {
       // One step is NQK + NPV MFMA slots, issued in this order: the QK
-      // product of window j+1 (half kb = 0, then 1; C starts at zero), then
+      // product of window j+1 (half kb = 0, then 1; C starts at -m), then
       // the P*V product of window j (16-key chunks c = 0..3).  Each slot
       // issues the LDS read of the operand D slots ahead (a ring of D+1
       // registers), its MFMA, and a share of the softmax VALU work of window
       // j, so that the matrix core and the VALU stay busy together instead of
       // alternating phases:
-      //   x0/x1   shifted scores of window j (half 0 before slot 0; half 1
-      //           spread over the slots of half 0, before its scores are
-      //           overwritten);
       //   E(g)    two exp2, one bf16 pack and one row-sum dot2 (group g =
       //           8 kb + 4 c2 + t -> P chunk 2kb + c2, keys 8t'..), each done
       //           before the P*V chunk that needs it;
       //   max     the row maximum of window j+1's scores, after their MFMAs.
       // sched_barrier(0) after each slot keeps this order.
-      constexpr int NQK = 2 * T::KC;
-      constexpr int NPV = 4 * T::HB;
-      constexpr int N = NQK + NPV;
-      constexpr int D = 3;                  // operand read distance (slots)
-      constexpr int R = D + 1;              // operand ring size
       const char* kl = kbuf(st1);
       const bf16x8* vl = reinterpret_cast<const bf16x8*>(vbuf(stage));
       auto operand = [&](int i) {
         return i < NQK ? kread(kl, i / T::KC, i % T::KC)
                        : vl[((i - NQK) / T::HB * T::HB + (i - NQK) % T::HB) * 64 + lane];
       };
-      float x0[16], x1[16];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) x0[r] = __builtin_fmaf(s_cur[0][r], scale_log2, -m_run);
-      bf16x8 opr[R];
-#pragma unroll
-      for (int i = 0; i < D; ++i) opr[i] = operand(i);
       uint32_t pw[4][4];
       float mxa = kNegInf, mxb = kNegInf;
-      // Slot of E group g, of the r-th FMA of x1, of the k-th max op of half kb.
+      // Slot of E group g and of the k-th max op of half kb.
       auto e_slot = [](int g) {
         return T::KC == 8 ? (g < 8 ? 2 * g : 9 + 2 * (g - 8)) : (g < 8 ? g : 5 + (g - 8));
       };
-      auto f1_slot = [](int r) { return r * T::KC / 16; };
       auto max_slot = [](int kb, int k) {
         return (kb == 0 ? T::KC : NQK) + 3 + (T::KC == 8 ? k : k / 2);
       };
@@ -459,22 +493,18 @@ void attn_kernel(AttnArgs a) {
         if (i + D < N) opr[(i + D) % R] = operand(i + D);
         if (i < NQK) {
           const int kb = i / T::KC, kc = i % T::KC;
-          s_cur[kb] = mfma32x32x16(opr[i % R], qr[kc], kc == 0 ? f32x16{} : s_cur[kb]);
+          sn[kb] = mfma32x32x16(opr[i % R], qr[kc], kc == 0 ? negm : sn[kb]);
         } else {
           const int c = (i - NQK) / T::HB, hb = (i - NQK) % T::HB;
           const u32x4 pv4 = {pw[c][0], pw[c][1], pw[c][2], pw[c][3]};
           o[hb] = mfma32x32x16(opr[i % R], __builtin_bit_cast(bf16x8, pv4), o[hb]);
         }
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-          if (f1_slot(r) == i) x1[r] = __builtin_fmaf(s_cur[1][r], scale_log2, -m_run);
-#pragma unroll
         for (int g = 0; g < 16; ++g) {
           if (e_slot(g) != i) continue;
           const int kb = g >> 3, c2 = (g >> 2) & 1, t = g & 3;
-          const float* xv = kb == 0 ? x0 : x1;
-          const float e0 = __builtin_amdgcn_exp2f(xv[c2 * 8 + 2 * t]);
-          const float e1 = __builtin_amdgcn_exp2f(xv[c2 * 8 + 2 * t + 1]);
+          const float e0 = __builtin_amdgcn_exp2f(sc[kb][c2 * 8 + 2 * t]);
+          const float e1 = __builtin_amdgcn_exp2f(sc[kb][c2 * 8 + 2 * t + 1]);
           const uint32_t w2 = pack_bf16(e0, e1);
           pw[kb * 2 + c2][t] = w2;
           l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w2),
@@ -483,54 +513,70 @@ void attn_kernel(AttnArgs a) {
         }
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
-          if (max_slot(0, k) == i) mxa = max3f(mxa, s_cur[0][2 * k], s_cur[0][2 * k + 1]);
-          if (max_slot(1, k) == i) mxb = max3f(mxb, s_cur[1][2 * k], s_cur[1][2 * k + 1]);
+          if (max_slot(0, k) == i) mxa = max3f(mxa, sn[0][2 * k], sn[0][2 * k + 1]);
+          if (max_slot(1, k) == i) mxb = max3f(mxb, sn[1][2 * k], sn[1][2 * k + 1]);
         }
         __builtin_amdgcn_sched_barrier(0);
       }
-      float mx = max_xor32(fmaxf(mxa, mxb)) * scale_log2;
+      float mx = max_xor32(fmaxf(mxa, mxb));
       // (C) window j+1: mask a partial window, then the lazy rescale (which
       //     applies to O accumulated through window j).
       if (!TAIL) {
-        maybe_rescale<T::HB>(mx, o, m_run, l_run);
+        maybe_rescale<T::HB>(mx, o, sn, negm, m_run, l_run);
       } else if (j + 1 < nw) {
         const Window w1 = win(j + 1);
         if (!w1.full) {
-          mask_scores(s_cur, w1);
-          mx = row_max(s_cur, scale_log2);
+          mask_scores(sn, w1);
+          mx = row_max(sn);
         }
-        maybe_rescale<T::HB>(mx, o, m_run, l_run);
+        maybe_rescale<T::HB>(mx, o, sn, negm, m_run, l_run);
       }
+      // The next step's first D operands, read before its barrier: QK(j+2)
+      // reads K(j+2), which landed before this step's barrier and is not
+      // reloaded before the next one.
+#pragma unroll
+      for (int i = 0; i < D; ++i) opr[i] = kread(kbuf(st2), 0, i);
     }
   };
 
   int j = 0;
-  for (; j + 7 <= nw; j += 3) {        // steps j, j+1, j+2 are all steady
-    step(j, 0, false);
-    step(j + 1, 1, false);
-    step(j + 2, 2, false);
+  for (; j + 9 <= nw; j += 4) {        // steps j .. j+3 are all steady
+    step(j, 0, false, false);
+    step(j + 1, 1, false, true);
+    step(j + 2, 2, false, false);
+    step(j + 3, 3, false, true);
   }
-  for (; j < nw; ++j) step(j, j % 3, true);
+  // j is even here: window j's scores are in sA.
+  for (; j + 1 < nw; j += 2) {
+    step(j, j & 3, true, false);
+    step(j + 1, (j + 1) & 3, true, true);
+  }
+  if (j < nw) step(j, j & 3, true, false);
 
   if (!active) return;
   const float l_tot = sum_xor32(l_run);
-  if (qrow >= s.n_q) return;
+  // The output row is recomputed here from an opaque copy of the lane index,
+  // so that no address derived from it stays live through the key loop.
+  int lane_o = lane;
+  __asm__ volatile("" : "+v"(lane_o));
+  const int qrow_o = row0 + (lane_o & 31), g_o = lane_o >> 5;
+  if (qrow_o >= s.n_q) return;
   const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
   // nsplit == 1: the final O; else this split's normalised partial (bf16)
   // and its log-sum-exp, merged by the combine kernel.
-  bf16* const dst_row = s.nsplit == 1 ? s.o + ((int64_t)qrow * H + h) * HD
-                                      : s.opart + (((int64_t)split * s.n_q + qrow) * H + h) * HD;
+  bf16* const dst_row = s.nsplit == 1 ? s.o + ((int64_t)qrow_o * H + h) * HD
+                                      : s.opart + (((int64_t)split * s.n_q + qrow_o) * H + h) * HD;
 #pragma unroll
   for (int hb = 0; hb < T::HB; ++hb) {
     union { bf16x8 v[2]; bf16 b[16]; } u;
 #pragma unroll
     for (int r = 0; r < 16; ++r) u.b[r] = (bf16)(o[hb][r] * inv);
-    bf16* dst = dst_row + hb * 32 + g * 16;
+    bf16* dst = dst_row + hb * 32 + g_o * 16;
     reinterpret_cast<bf16x8*>(dst)[0] = u.v[0];
     reinterpret_cast<bf16x8*>(dst)[1] = u.v[1];
   }
-  if (s.nsplit > 1 && g == 0)
-    s.lse[((int64_t)split * s.n_q + qrow) * H + h] = l_tot > 0.f ? m_run + __log2f(l_tot) : kNegInf;
+  if (s.nsplit > 1 && g_o == 0)
+    s.lse[((int64_t)split * s.n_q + qrow_o) * H + h] = l_tot > 0.f ? m_run + __log2f(l_tot) : kNegInf;
 }
 
 // Merge key-split partials: O = sum_s w_s o_s / sum_s w_s, w_s = 2^(lse_s - max)
