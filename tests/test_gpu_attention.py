@@ -148,3 +148,52 @@ def test_attention_deterministic():
     a, _ = _attn_case(2, 128, 1024, 900, 300, 70, seed=9)
     b, _ = _attn_case(2, 128, 1024, 900, 300, 70, seed=9)
     assert np.array_equal(a, b)
+
+
+@pytest.mark.parametrize("hd,length,split", [(128, 1000, 1), (128, 1000, None), (64, 1000, 1),
+                                             (128, 300, 1), (128, 130, 1)])
+def test_rising_scores_move_the_running_maximum(hd, length, split):
+    # Keys along the ring order carry a growing component along the queries'
+    # common direction, so the scores rise by about 10 (exp2 units) per
+    # 64-key window: the running maximum passes the lazy-rescale threshold in
+    # nearly every window, in the first window, the steady steps and the last
+    # steps, and O is dominated by the newest keys.
+    rng = np.random.default_rng(100 + hd + length)
+    H, cap, n_q = 2, 2048, 40
+    head = (5 + length) % cap
+    u = np.ones(hd)
+    step_per_key = 10.0 / (64 * np.sqrt(hd) * np.log2(np.e))
+    alpha = step_per_key * np.arange(length)
+    ck = bits((rng.standard_normal((H, length, hd)) + alpha[None, :, None] * u).astype(np.float32))
+    cv = random_bits(rng, (H, length, hd))
+    rk = np.full((H, cap, hd), 0x7FC0, dtype=np.uint16)
+    rv = rk.copy()
+    slots = (head - length + np.arange(length)) % cap
+    rk[:, slots], rv[:, slots] = ck, cv
+    q = bits((u + 0.1 * rng.standard_normal((n_q, H, hd))).astype(np.float32))
+    ku, vu = random_bits(rng, (n_q, H, hd)), random_bits(rng, (n_q, H, hd))
+    shape = workload.custom_session(H, hd, n_q, 0, 0, cap, length, head, (1.0,))
+    cache = make_cache(fmd, shape, rk, rv)
+    old = os.environ.get("FMD_ATTN_SPLIT")
+    try:
+        if split is not None:
+            os.environ["FMD_ATTN_SPLIT"] = str(split)
+        got = host_f64(fmd.attention([fmd.UnitStep(cache, dev_bf16(q), dev_bf16(ku), dev_bf16(vu))]))
+    finally:
+        if split is not None:
+            if old is None:
+                del os.environ["FMD_ATTN_SPLIT"]
+            else:
+                os.environ["FMD_ATTN_SPLIT"] = old
+    ref = oracle.attention(q, rk, rv, length, head, ku, vu)
+    # The newest keys dominate: O is far from the plain mean of the values.
+    assert np.max(np.abs(ref - oracle.bf16_bits_to_f64(cv).mean(axis=1)[None])) > 0.5
+    assert_close(got, ref, f"O rising scores hd={hd} length={length} split={split}")
+
+
+@pytest.mark.parametrize("length", [400, 640, 1000])
+def test_attention_window_counts_hd64(length):
+    # 64-wide heads through the steady loop (8, 11 and 17 windows).
+    head = (5 + length) % 2048
+    got, ref = _attn_case(1, 64, 2048, length, head, 40, seed=length, split=1)
+    assert_close(got, ref, f"O hd=64 length={length}")
