@@ -244,3 +244,27 @@ def test_maximum_session_count_four_launch_chunks():
         gk, gv = cache_logical(fmd, c)
         assert np.array_equal(gk, ref["ring_k"]) and np.array_equal(gv, ref["ring_v"])
         assert (c.len_tokens, c.head_tokens) == (ref["length"], ref["head"])
+
+
+def test_profiling_records_only_the_selected_classes():
+    # One unit = one append, then per step the unit K/V staging, attention,
+    # the merge of key splits (if any) and the projection.  Recording is on
+    # for the attention class only, then for every class.
+    wl = workload.get("v01_unit")
+    n_steps = len(wl.sessions[0].h)
+    try:
+        fmd.profile_enable(True, classes=("attn",))
+        _, _, z_sel = _run_unit(wl)
+        rec = {k: fmd.profile_read(k) for k in fmd.KERNEL_CLASSES}
+        assert rec["attn"][1] == n_steps and rec["attn"][0] > 0
+        assert all(n == 0 for k, (_, n) in rec.items() if k != "attn")
+        fmd.profile_enable(True)
+        _, _, z_all = _run_unit(wl)
+        rec = {k: fmd.profile_read(k) for k in fmd.KERNEL_CLASSES}
+        assert rec["append"][1] == 1
+        assert rec["attn"][1] == rec["proj"][1] == rec["vt"][1] == n_steps
+        assert rec["qkv"][1] == rec["mix"][1] == 0
+    finally:
+        fmd.profile_enable(False)
+    # Timing events do not change the result.
+    assert torch.equal(z_sel[0], z_all[0])
