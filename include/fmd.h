@@ -134,7 +134,9 @@ int fmd_workspace_bytes(const fmd_unit_step* units, int32_t n_units, size_t* out
 /*
  * One solver step for n_units sessions:
  *   O = attention(q, [valid ring || k_u], [valid ring || v_u]) per head, scale
- *       1/sqrt(head_dim), no mask; fp32 softmax and accumulation, O rounded to
+ *       1/sqrt(head_dim), no mask; q is multiplied by log2(e)/sqrt(head_dim)
+ *       and rounded to bf16 once, scores, softmax and accumulation are fp32,
+ *       the probabilities enter the value product as bf16, O is rounded to
  *       bf16;
  *   v = O_flat * W_o^T with O_flat [n_q][d] (heads concatenated);
  *   z <- z - h * v  (fp32).
