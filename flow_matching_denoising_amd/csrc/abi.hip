@@ -267,22 +267,40 @@ void session_order(const SessPlan* plans, int n, int* order) {
   std::stable_sort(order, order + n, [&](int x, int y) { return len[x] > len[y]; });
 }
 
+constexpr double kItemOverhead = 2.0;      // Q load, pipeline fill, O/LSE store
+constexpr double kCombinePerSplit = 1.3;   // per split of a 928-query session
+
 // Finish time of one XCD whose range is `cnt` items of the periodic order
 // `seq`, starting at position `first` of the period.
 double simulate_range(const std::vector<int>& seq, int64_t first, int64_t cnt) {
-  constexpr double kItemOverhead = 2.0;   // Q load, pipeline fill, O/LSE store
-  std::vector<double> cu(kTargetCUs / kNumXcd, 0.0);   // min-heap of finish times
+  constexpr int kCus = kTargetCUs / kNumXcd;
+  double cu[kCus] = {};   // binary min-heap of the CUs' finish times
   const int64_t period = (int64_t)seq.size();
+  int64_t pos = first % period;
   for (int64_t i = 0; i < cnt; ++i) {
-    std::pop_heap(cu.begin(), cu.end(), std::greater<double>());
-    cu.back() += seq[(first + i) % period] + kItemOverhead;
-    std::push_heap(cu.begin(), cu.end(), std::greater<double>());
+    // The earliest free CU (the root) takes the item; sift its new finish
+    // time down to restore the heap.
+    const double t = cu[0] + seq[pos] + kItemOverhead;
+    if (++pos == period) pos = 0;
+    int k = 0;
+    for (;;) {
+      int c = 2 * k + 1;
+      if (c >= kCus) break;
+      if (c + 1 < kCus && cu[c + 1] < cu[c]) ++c;
+      if (cu[c] >= t) break;
+      cu[k] = cu[c];
+      k = c;
+    }
+    cu[k] = t;
   }
-  return *std::max_element(cu.begin(), cu.end());
+  return *std::max_element(cu, cu + kCus);
+}
+
+double combine_cost(const SessPlan& p) {
+  return p.nsplit > 1 ? kCombinePerSplit * p.nsplit * p.n_q / 928.0 : 0.0;
 }
 
 double score_plan(const std::vector<SessPlan>& plans, int H) {
-  constexpr double kCombinePerSplit = 1.3;   // per split of a 928-query session
   std::vector<int> seq;   // windows of one head's items, launch order
   double combine = 0;
   for (size_t c0 = 0; c0 < plans.size(); c0 += kMaxSessPerLaunch) {
@@ -292,7 +310,7 @@ double score_plan(const std::vector<SessPlan>& plans, int H) {
     for (int j = 0; j < cn; ++j) {
       const SessPlan& p = plans[c0 + order[j]];
       for (int sp = 0; sp < p.nsplit; ++sp) seq.insert(seq.end(), p.n_qblk, split_windows(p, sp));
-      if (p.nsplit > 1) combine += kCombinePerSplit * p.nsplit * p.n_q / 928.0;
+      combine += combine_cost(p);
     }
   }
   // XCD ranges as xcd_remap cuts them.  Ranges that start at the same point of
@@ -337,7 +355,15 @@ void choose_splits(std::vector<SessPlan>& plans, int H) {
     for (size_t i = 0; i < plans.size(); ++i) counts[i] = plan_split_count(plans[i], per_item);
     if (counts == last) continue;   // same plan as the previous candidate
     last = counts;
-    for (size_t i = 0; i < plans.size(); ++i) set_splits(plans[i], counts[i]);
+    // A lower bound of the score (the slowest XCD finishes no earlier than
+    // the average one) skips the simulation of candidates that cannot win.
+    double items = 0, combine = 0;
+    for (size_t i = 0; i < plans.size(); ++i) {
+      set_splits(plans[i], counts[i]);
+      items += (double)H * plans[i].n_qblk * plans[i].nsplit;
+      combine += combine_cost(plans[i]);
+    }
+    if ((work + kItemOverhead * items) / kTargetCUs + combine >= best_cost) continue;
     const double cost = score_plan(plans, H);
     if (cost < best_cost - 1e-9) {
       best_cost = cost;
