@@ -443,20 +443,24 @@ def main():
     # Inside the timed region only the attention launches (the roofline's
     # kernel) carry events: every recorded launch adds queue time around it.
     fmd.profile_enable(True, classes=("attn",))
-    # One pair of events per unit on the launch stream: the per-unit median
-    # and p90 beside the wall-clock mean.
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    for _ in range(args.steps):
+        one_unit()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    attn_rec = fmd.profile_read("attn")
+    fmd.profile_enable(False)
+    # Per-unit median and p90: an untimed pass with one pair of events per
+    # unit on the launch stream.
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
     for a, b in evs:
         a.record()
         one_unit()
         b.record()
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
     unit_ms = sorted(a.elapsed_time(b) for a, b in evs)
-    attn_rec = fmd.profile_read("attn")
     # The other kernels' durations: a second, untimed pass over the same
     # units with every class recorded.
     fmd.profile_enable(True)
