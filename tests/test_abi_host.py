@@ -364,3 +364,21 @@ def test_profile_select_rejects_unknown_classes():
     assert fmd._profile_select((1 << n) - 1) == 0
     assert fmd._profile_select(0) == 0
     assert fmd._profile_select((1 << n) - 1) == 0
+
+
+@pytest.mark.parametrize("H,head,splits", [(5, 59472, 12), (10, 59472, 8), (40, 59472, 10),
+                                           (40, 0, 9)])
+def test_split_planner_choices(H, head, splits):
+    # The key-split count the launch model picks for a full 60,416-key ring
+    # and a 928-query unit, read back from the workspace size (one bf16
+    # partial O and one fp32 log-sum-exp per split): 5 heads (one 8-way
+    # Ulysses rank) take 240 items, one dispatch round, and 10 heads 320;
+    # 40 heads take 9 or 10 splits (ring not wrapped or wrapped).
+    n_q, hd = 928, 128
+    c = _cache(H=H, hd=hd, cap=60416, ln=60416, head=head)
+    rc, nbytes = _ws([_step(c, 920, 8)])
+    assert rc == 0
+    staged = 2 * H * n_q * hd * 2 + n_q * H * hd * 2      # unit K, V (npad = n_q) and O
+    per_split = n_q * H * (hd * 2 + 4)
+    assert (nbytes - staged) % per_split == 0
+    assert (nbytes - staged) // per_split == splits
