@@ -132,6 +132,7 @@ _profile_select = _sig("fmd_profile_select", ctypes.c_int, ctypes.c_uint32)
 _profile_read = _sig("fmd_profile_read", ctypes.c_int, ctypes.c_int,
                      ctypes.POINTER(ctypes.c_double), ctypes.POINTER(_i64))
 _version = _sig("fmd_version", ctypes.c_char_p)
+_test_force_attn_splits = _sig("fmd_test_force_attn_splits", ctypes.c_int, _i32)
 
 EXPORTED = ["fmd_kv_append", "fmd_kv_append_batched", "fmd_workspace_bytes", "fmd_denoise_step",
             "fmd_attention", "fmd_unit_workspace_bytes", "fmd_denoise_unit",
@@ -139,7 +140,7 @@ EXPORTED = ["fmd_kv_append", "fmd_kv_append_batched", "fmd_workspace_bytes", "fm
             "fmd_unit_cfg_workspace_bytes", "fmd_denoise_unit_cfg",
             "fmd_unit_layers_workspace_bytes", "fmd_denoise_unit_layers", "fmd_strerror",
             "fmd_last_error", "fmd_profile_enable", "fmd_profile_select", "fmd_profile_read",
-            "fmd_version"]
+            "fmd_version", "fmd_test_force_attn_splits"]
 
 
 def _check(rc: int):
@@ -177,6 +178,35 @@ def _ptr(t, dtype, name, allow_none=False):
     return t.data_ptr()
 
 
+def _expect_shape(t, shape, name):
+    """Raise ValueError unless tensor t has exactly this shape.  The C ABI
+    receives bare pointers, so every extent it relies on is checked here."""
+    if t is None:
+        return
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def _expect_slices(k_slice, v_slice, H, hd, name="slice"):
+    if (k_slice is None) != (v_slice is None):
+        raise ValueError(f"k_{name} and v_{name} must both be given or both be None")
+    if k_slice is None:
+        return 0
+    if k_slice.dim() != 3:
+        raise ValueError(f"k_{name} must be [T][H][hd], got {tuple(k_slice.shape)}")
+    T = k_slice.shape[0]
+    _expect_shape(k_slice, (T, H, hd), f"k_{name}")
+    _expect_shape(v_slice, (T, H, hd), f"v_{name}")
+    return T
+
+
+def _sync_workspace(workspace, stream):
+    # A workspace allocated on torch's current stream but used on another one
+    # must not be recycled by the caching allocator before that stream is done.
+    if stream is not None and stream != torch.cuda.current_stream(workspace.device):
+        workspace.record_stream(stream)
+
+
 class KVCache:
     """One session's ring: device tensors k [H][cap][hd] and v
     [H][cap/16][hd][16] (bf16), plus the host-side (len, head) state that the
@@ -190,6 +220,10 @@ class KVCache:
         if v is None:
             v = torch.empty((n_heads, cap_tokens // FMD_CACHE_BLOCK, head_dim, FMD_CACHE_BLOCK),
                             dtype=torch.bfloat16, device=device)
+        _expect_shape(k, (n_heads, cap_tokens, head_dim), "k")
+        if cap_tokens % FMD_CACHE_BLOCK:
+            raise ValueError(f"cap_tokens {cap_tokens} must be a multiple of {FMD_CACHE_BLOCK}")
+        _expect_shape(v, (n_heads, cap_tokens // FMD_CACHE_BLOCK, head_dim, FMD_CACHE_BLOCK), "v")
         self.k, self.v = k, v
         self._c = _Cache(_ptr(k, torch.bfloat16, "k"), _ptr(v, torch.bfloat16, "v"), n_heads,
                          head_dim, cap_tokens, len_tokens, head_tokens)
@@ -224,6 +258,9 @@ class KVCache:
 
 def kv_append(cache: KVCache, k_slice, v_slice, stream=None):
     """Append one slice [T][H][hd] (bf16) to the ring; advances len/head."""
+    if k_slice is None or v_slice is None:
+        raise ValueError("k_slice and v_slice are required")
+    _expect_slices(k_slice, v_slice, cache.n_heads, cache.head_dim)
     _check(_kv_append(ctypes.byref(cache._c), _ptr(k_slice, torch.bfloat16, "k_slice"),
                       _ptr(v_slice, torch.bfloat16, "v_slice"), k_slice.shape[0],
                       _stream_ptr(stream)))
@@ -231,6 +268,12 @@ def kv_append(cache: KVCache, k_slice, v_slice, stream=None):
 
 def kv_append_batched(caches, k_slices, v_slices, stream=None):
     n = len(caches)
+    if len(k_slices) != n or len(v_slices) != n:
+        raise ValueError("one K and one V slice per cache")
+    for c, k, v in zip(caches, k_slices, v_slices):
+        if k is None or v is None:
+            raise ValueError("k_slices and v_slices must not hold None")
+        _expect_slices(k, v, c.n_heads, c.head_dim)
     arr_c = (ctypes.POINTER(_Cache) * n)(*[ctypes.pointer(c._c) for c in caches])
     arr_k = (_vp * n)(*[_ptr(t, torch.bfloat16, "k_slice") for t in k_slices])
     arr_v = (_vp * n)(*[_ptr(t, torch.bfloat16, "v_slice") for t in v_slices])
@@ -243,9 +286,17 @@ class UnitStep:
 
     def __init__(self, cache: KVCache, q, k_u, v_u, z=None, n_video=None, n_audio=0, h=1.0):
         self.cache, self.q, self.k_u, self.v_u, self.z = cache, q, k_u, v_u, z
+        H, hd = cache.n_heads, cache.head_dim
+        if q.dim() != 3:
+            raise ValueError(f"q must be [n_q][H][hd], got {tuple(q.shape)}")
         n_q = q.shape[0]
+        for t, nm in ((q, "q"), (k_u, "k_u"), (v_u, "v_u")):
+            _expect_shape(t, (n_q, H, hd), nm)
+        _expect_shape(z, (n_q, H * hd), "z")
         self.n_video = n_q - n_audio if n_video is None else n_video
         self.n_audio = n_audio
+        if self.n_video + self.n_audio != n_q:
+            raise ValueError(f"n_video + n_audio = {self.n_video + self.n_audio} != n_q = {n_q}")
         self.h = h
 
     def _struct(self):
@@ -280,10 +331,12 @@ def attention(units, o_out=None, workspace=None, stream=None):
     rows = sum(u.q.shape[0] for u in units)
     if o_out is None:
         o_out = torch.empty((rows, H, hd), dtype=torch.bfloat16, device=units[0].q.device)
+    _expect_shape(o_out, (rows, H, hd), "o_out")
     need = _sz(0)
     _check(_workspace_bytes(arr, n, ctypes.byref(need)))
     if workspace is None:
         workspace = alloc_workspace(need.value, units[0].q.device)
+    _sync_workspace(workspace, stream)
     _check(_attention(arr, n, _ptr(o_out, torch.bfloat16, "o_out"),
                       workspace.data_ptr(), workspace.numel(), _stream_ptr(stream)))
     return o_out
@@ -291,9 +344,14 @@ def attention(units, o_out=None, workspace=None, stream=None):
 
 def denoise_step(units, w_o, workspace=None, stream=None):
     """One solver step for every session: z <- z - h * (attention(...) W_o^T)."""
+    d = units[0].cache.n_heads * units[0].cache.head_dim
+    _expect_shape(w_o, (d, d), "w_o")
+    if any(u.z is None for u in units):
+        raise ValueError("every unit needs its latent z for a solver step")
     arr, n = _steps_array(units)
     if workspace is None:
         workspace = alloc_workspace(workspace_bytes(units), units[0].q.device)
+    _sync_workspace(workspace, stream)
     _check(_denoise_step(arr, n, _ptr(w_o, torch.bfloat16, "w_o"), workspace.data_ptr(),
                          workspace.numel(), _stream_ptr(stream)))
 
@@ -310,8 +368,19 @@ class UnitIO:
         self.q, self.k_u, self.v_u, self.z = q, k_u, v_u, z
         self.h = (ctypes.c_float * len(h))(*[float(x) for x in h])
         self.n_steps = len(h)
+        H, hd = cache.n_heads, cache.head_dim
+        if q.dim() not in (3, 4):
+            raise ValueError(f"q must be [S][n_q][H][hd] or [n_q][H][hd], got {tuple(q.shape)}")
         per_step = q.dim() == 4
         self.n_q = q.shape[1] if per_step else q.shape[0]
+        if per_step and q.shape[0] < self.n_steps:
+            raise ValueError(f"q holds {q.shape[0]} steps, {self.n_steps} step sizes given")
+        for t, nm in ((q, "q"), (k_u, "k_u"), (v_u, "v_u")):
+            _expect_shape(t, tuple(q.shape[:-2]) + (H, hd), nm)
+        _expect_shape(z, (self.n_q, H * hd), "z")
+        _expect_slices(k_slice, v_slice, H, hd)
+        if not 0 <= n_audio <= self.n_q:
+            raise ValueError(f"n_audio {n_audio} outside 0..n_q={self.n_q}")
         self.stride = q[0].numel() if per_step else 0
         self.n_audio = n_audio
 
@@ -343,8 +412,11 @@ def denoise_unit(sessions, w_o, workspace=None, stream=None):
     n_steps = sessions[0].n_steps
     if any(s.n_steps != n_steps for s in sessions):
         raise ValueError("all sessions must have the same number of steps")
+    d = sessions[0].cache.n_heads * sessions[0].cache.head_dim
+    _expect_shape(w_o, (d, d), "w_o")
     if workspace is None:
         workspace = alloc_workspace(unit_workspace_bytes(sessions), sessions[0].z.device)
+    _sync_workspace(workspace, stream)
     arr, n = _io_array(sessions)
     _check(_denoise_unit(arr, n, n_steps, _ptr(w_o, torch.bfloat16, "w_o"), workspace.data_ptr(),
                          workspace.numel(), _stream_ptr(stream)))
@@ -362,6 +434,10 @@ class UnitQkvIO:
         self.h = (ctypes.c_float * len(h))(*[float(x) for x in h])
         self.n_steps = len(h)
         self.n_q = z.shape[0]
+        _expect_shape(z, (self.n_q, cache.n_heads * cache.head_dim), "z")
+        _expect_slices(k_slice, v_slice, cache.n_heads, cache.head_dim)
+        if not 0 <= n_audio <= self.n_q:
+            raise ValueError(f"n_audio {n_audio} outside 0..n_q={self.n_q}")
         self.n_audio = n_audio
 
     def _struct(self):
@@ -392,8 +468,12 @@ def denoise_unit_qkv(sessions, w_qkv, w_o, workspace=None, stream=None):
     n_steps = sessions[0].n_steps
     if any(s.n_steps != n_steps for s in sessions):
         raise ValueError("all sessions must have the same number of steps")
+    d = sessions[0].cache.n_heads * sessions[0].cache.head_dim
+    _expect_shape(w_qkv, (3 * d, d), "w_qkv")
+    _expect_shape(w_o, (d, d), "w_o")
     if workspace is None:
         workspace = alloc_workspace(unit_qkv_workspace_bytes(sessions), sessions[0].z.device)
+    _sync_workspace(workspace, stream)
     arr, n = _qkv_array(sessions)
     _check(_denoise_unit_qkv(arr, n, n_steps, _ptr(w_qkv, torch.bfloat16, "w_qkv"),
                              _ptr(w_o, torch.bfloat16, "w_o"), workspace.data_ptr(),
@@ -413,6 +493,12 @@ class UnitCfgIO:
         self.h = (ctypes.c_float * len(h))(*[float(x) for x in h])
         self.n_steps = len(h)
         self.n_q = z.shape[0]
+        H, hd = cond.n_heads, cond.head_dim
+        _expect_shape(z, (self.n_q, H * hd), "z")
+        _expect_slices(*cond_slice, H, hd, "cond_slice")
+        _expect_slices(*uncond_slice, uncond.n_heads, uncond.head_dim, "uncond_slice")
+        if not 0 <= n_audio <= self.n_q:
+            raise ValueError(f"n_audio {n_audio} outside 0..n_q={self.n_q}")
         self.n_audio = n_audio
         self.guidance = float(guidance)
 
@@ -448,8 +534,12 @@ def denoise_unit_cfg(sessions, w_qkv, w_o, workspace=None, stream=None):
     n_steps = sessions[0].n_steps
     if any(s.n_steps != n_steps for s in sessions):
         raise ValueError("all sessions must have the same number of steps")
+    d = sessions[0].cond.n_heads * sessions[0].cond.head_dim
+    _expect_shape(w_qkv, (3 * d, d), "w_qkv")
+    _expect_shape(w_o, (d, d), "w_o")
     if workspace is None:
         workspace = alloc_workspace(unit_cfg_workspace_bytes(sessions), sessions[0].z.device)
+    _sync_workspace(workspace, stream)
     arr, n = _cfg_array(sessions)
     _check(_denoise_unit_cfg(arr, n, n_steps, _ptr(w_qkv, torch.bfloat16, "w_qkv"),
                              _ptr(w_o, torch.bfloat16, "w_o"), workspace.data_ptr(),
@@ -469,6 +559,19 @@ class UnitLayersIO:
         self.h = (ctypes.c_float * len(h))(*[float(x) for x in h])
         self.n_steps = len(h)
         self.n_q = z.shape[0]
+        H, hd = self.caches[0].n_heads, self.caches[0].head_dim
+        _expect_shape(z, (self.n_q, H * hd), "z")
+        if (self.k_slices is None) != (self.v_slices is None):
+            raise ValueError("k_slices and v_slices must both be given or both be None")
+        if self.k_slices is not None:
+            if len(self.k_slices) != len(self.caches) or len(self.v_slices) != len(self.caches):
+                raise ValueError("one K and one V slice per layer")
+            Ts = {_expect_slices(k, v, c.n_heads, c.head_dim, "slices")
+                  for k, v, c in zip(self.k_slices, self.v_slices, self.caches)}
+            if len(Ts) != 1:
+                raise ValueError("every layer appends the same number of tokens")
+        if not 0 <= n_audio <= self.n_q:
+            raise ValueError(f"n_audio {n_audio} outside 0..n_q={self.n_q}")
         self.n_audio = n_audio
 
     def _struct(self):
@@ -512,15 +615,41 @@ def denoise_unit_layers(sessions, w_qkv, w_o, workspace=None, stream=None):
     n_steps = sessions[0].n_steps
     if any(s.n_steps != n_steps for s in sessions):
         raise ValueError("all sessions must have the same number of steps")
-    if workspace is None:
-        workspace = alloc_workspace(unit_layers_workspace_bytes(sessions), sessions[0].z.device)
-    arr, n, L = _layers_array(sessions)
+    L = len(sessions[0].caches)
     if len(w_qkv) != L or len(w_o) != L:
         raise ValueError("one W_qkv and one W_o per layer")
+    d = sessions[0].caches[0].n_heads * sessions[0].caches[0].head_dim
+    for w in w_qkv:
+        _expect_shape(w, (3 * d, d), "w_qkv")
+    for w in w_o:
+        _expect_shape(w, (d, d), "w_o")
+    if workspace is None:
+        workspace = alloc_workspace(unit_layers_workspace_bytes(sessions), sessions[0].z.device)
+    _sync_workspace(workspace, stream)
+    arr, n, L = _layers_array(sessions)
     wq = (_vp * L)(*[_ptr(w, torch.bfloat16, "w_qkv") for w in w_qkv])
     wo = (_vp * L)(*[_ptr(w, torch.bfloat16, "w_o") for w in w_o])
     _check(_denoise_unit_layers(arr, n, L, n_steps, wq, wo, workspace.data_ptr(),
                                 workspace.numel(), _stream_ptr(stream)))
+
+
+class forced_attn_splits:
+    """Test helper: ``with forced_attn_splits(n): ...`` runs the enclosed calls
+    with every attention session cut into n key splits (see
+    ``fmd_test_force_attn_splits``); ``None`` leaves the planner's choice."""
+
+    def __init__(self, n_splits):
+        self.n = n_splits
+
+    def __enter__(self):
+        if self.n is not None:
+            _check(_test_force_attn_splits(int(self.n)))
+        return self
+
+    def __exit__(self, *exc):
+        if self.n is not None:
+            _check(_test_force_attn_splits(0))
+        return False
 
 
 def profile_enable(on: bool = True, classes=None):

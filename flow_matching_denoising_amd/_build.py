@@ -2,14 +2,18 @@
 
 Every HIP source is compiled to its own object (in parallel) and linked into
 ``flow_matching_denoising_amd/libfmd.so``.  Packed-FP32 code generation is
-switched off for the device code."""
+switched off for the device code, and the build fails if the gfx950 code of
+any object still holds a packed-FP32 add, multiply or FMA (its disassembly is
+checked after every compile)."""
 from __future__ import annotations
 
 import concurrent.futures as cf
 import glob
 import os
+import re
 import shutil
 import subprocess
+import tempfile
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
@@ -30,6 +34,41 @@ def _hipcc() -> str:
     raise RuntimeError("hipcc not found; the HIP toolchain (ROCm) is required to build libfmd")
 
 
+_PACKED_FP32 = re.compile(r"\bv_pk_(add|mul|fma)_f32\b")
+
+
+def _llvm_tool(name: str) -> str:
+    for cand in (os.path.join("/opt/rocm/llvm/bin", name), shutil.which(name)):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError(f"{name} not found (ROCm LLVM tools are required to check the build)")
+
+
+def check_device_code(obj: str) -> int:
+    """Disassemble the gfx950 code object inside a compiled HIP object and
+    raise if it holds packed-FP32 arithmetic.  Returns the number of MFMA
+    instructions found (a sanity check that the code was disassembled)."""
+    sections = subprocess.run([_llvm_tool("llvm-readelf"), "-S", obj], check=True,
+                              capture_output=True, text=True).stdout
+    if ".hip_fatbin" not in sections:
+        return 0   # host code only
+    with tempfile.TemporaryDirectory() as tmp:
+        fat = os.path.join(tmp, "fatbin")
+        co = os.path.join(tmp, "device.co")
+        subprocess.run([_llvm_tool("llvm-objcopy"), f"--dump-section=.hip_fatbin={fat}", obj],
+                       check=True, capture_output=True)
+        subprocess.run([_llvm_tool("clang-offload-bundler"), "--type=o", f"--input={fat}",
+                        f"--targets=hipv4-amdgcn-amd-amdhsa--{ARCH}", f"--output={co}",
+                        "--unbundle"], check=True, capture_output=True)
+        asm = subprocess.run([_llvm_tool("llvm-objdump"), "-d", co], check=True,
+                             capture_output=True, text=True).stdout
+    bad = [l.strip() for l in asm.splitlines() if _PACKED_FP32.search(l)]
+    if bad:
+        raise RuntimeError(f"{os.path.basename(obj)}: {len(bad)} packed-FP32 instruction(s) in "
+                           f"the {ARCH} code, e.g. {bad[0]}")
+    return sum(1 for l in asm.splitlines() if "v_mfma" in l)
+
+
 def build(verbose: bool = False, jobs: int = 8) -> str:
     hipcc = _hipcc()
     srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
@@ -46,6 +85,7 @@ def build(verbose: bool = False, jobs: int = 8) -> str:
             raise RuntimeError(f"hipcc failed on {os.path.basename(src)}:\n{msgs}")
         if verbose and msgs.strip():
             print(msgs)
+        check_device_code(obj)
         return obj
 
     with cf.ThreadPoolExecutor(max(1, min(jobs, len(srcs)))) as ex:

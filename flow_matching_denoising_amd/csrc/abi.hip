@@ -12,6 +12,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <atomic>
 #include <functional>
 #include <mutex>
 #include <string>
@@ -225,11 +226,8 @@ void plan_session(const fmd_kv_cache* c, int n_q, SessPlan& p) {
   set_splits(p, 1);
 }
 
-int env_int(const char* name, int dflt) {
-  const char* v = getenv(name);
-  if (!v || !*v) return dflt;
-  return atoi(v);
-}
+// Split count forced through fmd_test_force_attn_splits (0: the planner).
+std::atomic<int> g_forced_splits{0};
 
 // Key splits.  The item size (64-key windows per work item) trades the
 // dispatch tail against the combine pass, which reads every split's partial
@@ -239,8 +237,7 @@ int env_int(const char* name, int dflt) {
 // (xcd_remap), and its 32 CUs take the range's items in order, each the next
 // free CU (greedy list scheduling); the score is the slowest XCD's finish time
 // plus the combine work, both in units of one window of one item.  Depends
-// only on the shapes.  FMD_ATTN_SPLIT forces a split count per session,
-// FMD_ATTN_TARGET_ITEMS a target item count (both for experiments).
+// only on the shapes (a test can force a split count instead).
 int plan_split_count(const SessPlan& p, double per_item) {
   constexpr int kMinWindows = 16;
   int ns = (int)ceil(p.nwin_total / (per_item > 1 ? per_item : 1.0));
@@ -336,18 +333,13 @@ double score_plan(const std::vector<SessPlan>& plans, int H) {
 }
 
 void choose_splits(std::vector<SessPlan>& plans, int H) {
-  const int forced = env_int("FMD_ATTN_SPLIT", 0);
+  const int forced = g_forced_splits.load(std::memory_order_relaxed);
   if (forced > 0) {
     for (auto& p : plans) set_splits(p, forced);
     return;
   }
   double work = 0;
   for (auto& p : plans) work += (double)H * p.n_qblk * p.nwin_total;
-  const int target_env = env_int("FMD_ATTN_TARGET_ITEMS", 0);
-  if (target_env > 0) {
-    for (auto& p : plans) set_splits(p, plan_split_count(p, work / target_env));
-    return;
-  }
   double best_cost = 1e300, best_per_item = work;
   std::vector<int> counts(plans.size()), last;
   for (int target = 32; target <= 40 * kTargetCUs; target += target < 2048 ? 32 : 256) {
@@ -613,7 +605,14 @@ int enqueue_appends(fmd_kv_cache* const* caches, const void* const* ks, const vo
 
 extern "C" {
 
-const char* fmd_version(void) { return "0.1.0"; }
+const char* fmd_version(void) { return "0.2.0"; }
+
+int fmd_test_force_attn_splits(int32_t n_splits) {
+  g_last_error.clear();
+  if (n_splits < 0) return fail(FMD_E_INVAL, "n_splits=%d (must be >= 0)", n_splits);
+  g_forced_splits.store(n_splits, std::memory_order_relaxed);
+  return FMD_OK;
+}
 
 const char* fmd_strerror(int status) {
   switch (status) {

@@ -46,6 +46,58 @@ __device__ __forceinline__ void st16(void* p, u32x4 v) {
 }
 
 // ---------------------------------------------------------------------------
+// Global -> LDS loads through buffer resources (MUBUF loads with the lds bit).
+// ---------------------------------------------------------------------------
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+constexpr int kRsrcWord3 = 0x00020000;   // raw buffer, 32-bit data format
+
+// Buffer resource over [base, base + bytes): a lane whose range-checked offset
+// falls at or past `bytes` reads zeros instead of faulting.
+__device__ __forceinline__ i32x4 make_rsrc(const bf16* base, int bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  i32x4 r;
+  r.x = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+  r.y = __builtin_amdgcn_readfirstlane((int)((uint32_t)(a >> 32) & 0xFFFFu));   // stride 0
+  r.z = __builtin_amdgcn_readfirstlane(bytes);                                   // num_records
+  r.w = kRsrcWord3;
+  return r;
+}
+
+// One wave instruction: 16 bytes per lane from rs at voff + soff to
+// dst + 16*lane (dst wave-uniform; voff range-checked, soff not).  Issued
+// from inline assembly on purpose: it has no register outputs, and the
+// compiler, which cannot tell one LDS stage buffer from another, would
+// otherwise make every LDS read wait for every LDS load in flight.  Callers
+// order these loads themselves: s_waitcnt vmcnt(N) and a barrier before any
+// wave reads a tile (wait_loads_and_sync), a barrier between the last read of
+// a buffer and the next load into it.  One wait state separates the M0 write
+// from the load that reads it.
+__device__ __forceinline__ void dma16(const i32x4& rs, int voff, int soff, char* dst) {
+  const uint32_t m0 =
+      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)dst;
+  __asm__ volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+                   :
+                   : "s"(m0), "v"(voff), "s"(rs), "s"(soff)
+                   : "memory", "m0");
+}
+
+// s_waitcnt immediate (gfx9 encoding): vmcnt in bits 3:0 and 15:14,
+// expcnt (left at its maximum, 7) in bits 6:4, lgkmcnt in bits 11:8.
+constexpr int vmcnt_imm(int vm, int lgkm) {
+  return (vm & 15) | ((vm >> 4) << 14) | (7 << 4) | (lgkm << 8);
+}
+
+// Wait until at most N of this wave's loads are outstanding, then barrier.
+template <int N>
+__device__ __forceinline__ void wait_loads_and_sync() {
+  static_assert(N >= 0 && N < 64, "vmcnt is six bits");
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(N, 15));   // vmcnt(N); lgkmcnt unconstrained
+  __asm__ volatile("" ::: "memory");
+  __syncthreads();
+  __asm__ volatile("" ::: "memory");
+}
+
+// ---------------------------------------------------------------------------
 // Launch descriptors (passed by value).
 // ---------------------------------------------------------------------------
 

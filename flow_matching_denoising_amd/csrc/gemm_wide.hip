@@ -33,38 +33,6 @@ constexpr int WLOADS = (WA_BLOCKS + WB_BLOCKS) / WWAVES;       // 8 per wave per
 constexpr int WLDS_BYTES = 2 * WSTAGE_BYTES;                   // 128 KiB
 static_assert(WA_BLOCKS % WWAVES == 0, "A blocks split evenly over waves");
 
-typedef int i32x4 __attribute__((ext_vector_type(4)));
-constexpr int kRsrcWord3 = 0x00020000;   // raw buffer, 32-bit data format
-
-__device__ __forceinline__ i32x4 make_rsrc(const bf16* base, int bytes) {
-  const uint64_t a = reinterpret_cast<uint64_t>(base);
-  i32x4 r;
-  r.x = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
-  r.y = __builtin_amdgcn_readfirstlane((int)((uint32_t)(a >> 32) & 0xFFFFu));   // stride 0
-  r.z = __builtin_amdgcn_readfirstlane(bytes);                                   // num_records
-  r.w = kRsrcWord3;
-  return r;
-}
-
-// One wave instruction: 16 bytes per lane from rs at voff + soff to
-// dst + 16*lane (dst wave-uniform; voff range-checked).  Inline assembly so
-// that the compiler does not order LDS reads after every LDS load in flight;
-// the kernel waits (vmcnt) and synchronises (barrier) itself.
-__device__ __forceinline__ void dma16(const i32x4& rs, int voff, int soff, char* dst) {
-  const uint32_t m0 =
-      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)dst;
-  __asm__ volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
-                   :
-                   : "s"(m0), "v"(voff), "s"(rs), "s"(soff)
-                   : "memory", "m0");
-}
-
-// s_waitcnt immediate (gfx9 encoding): vmcnt in bits 3:0 and 15:14,
-// expcnt (left at its maximum, 7) in bits 6:4, lgkmcnt in bits 11:8.
-constexpr int vmcnt_imm(int vm, int lgkm) {
-  return (vm & 15) | ((vm >> 4) << 14) | (7 << 4) | (lgkm << 8);
-}
-
 __device__ __forceinline__ void wait_all_loads_and_sync() {
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0, 15));
   __asm__ volatile("" ::: "memory");

@@ -43,49 +43,6 @@ constexpr int LDS_BYTES = STAGES * STAGE_BYTES;     // 108 KiB
 static_assert(A_BLOCKS % WAVES == 0 && B_BLOCKS % WAVES == 0, "loads must split evenly over waves");
 static_assert(BN == 32 * WAVES, "one 32-feature column tile per wave");
 
-typedef int i32x4 __attribute__((ext_vector_type(4)));
-constexpr int kRsrcWord3 = 0x00020000;   // raw buffer, 32-bit data format
-
-__device__ __forceinline__ i32x4 make_rsrc(const bf16* base, int bytes) {
-  const uint64_t a = reinterpret_cast<uint64_t>(base);
-  i32x4 r;
-  r.x = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
-  r.y = __builtin_amdgcn_readfirstlane((int)((uint32_t)(a >> 32) & 0xFFFFu));   // stride 0
-  r.z = __builtin_amdgcn_readfirstlane(bytes);                                   // num_records
-  r.w = kRsrcWord3;
-  return r;
-}
-
-// One wave instruction: 16 bytes per lane from rs at voff + soff to
-// dst + 16*lane (dst wave-uniform; voff range-checked).  Issued from inline
-// assembly so that the compiler does not make every LDS read wait for every
-// LDS load in flight; the kernel orders them itself (vmcnt wait + barrier
-// before reading a stage, barrier before reloading it).  One wait state
-// separates the M0 write from the load that reads it.
-__device__ __forceinline__ void dma16(const i32x4& rs, int voff, int soff, char* dst) {
-  const uint32_t m0 =
-      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)dst;
-  __asm__ volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
-                   :
-                   : "s"(m0), "v"(voff), "s"(rs), "s"(soff)
-                   : "memory", "m0");
-}
-
-// s_waitcnt immediate (gfx9 encoding): vmcnt in bits 3:0 and 15:14,
-// expcnt (left at its maximum, 7) in bits 6:4, lgkmcnt in bits 11:8.
-constexpr int vmcnt_imm(int vm, int lgkm) {
-  return (vm & 15) | ((vm >> 4) << 14) | (7 << 4) | (lgkm << 8);
-}
-
-template <int N>
-__device__ __forceinline__ void wait_loads_and_sync() {
-  static_assert(N >= 0 && N < 64, "vmcnt is six bits");
-  __builtin_amdgcn_s_waitcnt(vmcnt_imm(N, 15));   // vmcnt(N); lgkmcnt unconstrained
-  __asm__ volatile("" ::: "memory");
-  __syncthreads();
-  __asm__ volatile("" ::: "memory");
-}
-
 }  // namespace
 
 template <int MODE>

@@ -1,6 +1,5 @@
 """GPU parity of the attention kernel (through fmd_attention) against the
 oracle, plus the oracle's invariants checked on the GPU."""
-import os
 
 import numpy as np
 import pytest
@@ -30,18 +29,9 @@ def _attn_case(H, hd, cap, length, head, n_q, seed=0, poison=True, split=None, n
     shape = workload.custom_session(H, hd, n_q - n_audio, n_audio, 0, cap, length, head, (1.0,))
     cache = make_cache(fmd, shape, rk, rv)
     unit = fmd.UnitStep(cache, dev_bf16(q), dev_bf16(ku), dev_bf16(vu), n_audio=n_audio)
-    old = os.environ.get("FMD_ATTN_SPLIT")
-    try:
-        if split is not None:
-            os.environ["FMD_ATTN_SPLIT"] = str(split)
+    with fmd.forced_attn_splits(split):
         o = fmd.attention([unit])
         torch.cuda.synchronize()
-    finally:
-        if split is not None:
-            if old is None:
-                del os.environ["FMD_ATTN_SPLIT"]
-            else:
-                os.environ["FMD_ATTN_SPLIT"] = old
     ref = oracle.attention(q, rk, rv, length, head, ku, vu)
     return host_f64(o), ref
 
@@ -174,17 +164,8 @@ def test_rising_scores_move_the_running_maximum(hd, length, split):
     ku, vu = random_bits(rng, (n_q, H, hd)), random_bits(rng, (n_q, H, hd))
     shape = workload.custom_session(H, hd, n_q, 0, 0, cap, length, head, (1.0,))
     cache = make_cache(fmd, shape, rk, rv)
-    old = os.environ.get("FMD_ATTN_SPLIT")
-    try:
-        if split is not None:
-            os.environ["FMD_ATTN_SPLIT"] = str(split)
+    with fmd.forced_attn_splits(split):
         got = host_f64(fmd.attention([fmd.UnitStep(cache, dev_bf16(q), dev_bf16(ku), dev_bf16(vu))]))
-    finally:
-        if split is not None:
-            if old is None:
-                del os.environ["FMD_ATTN_SPLIT"]
-            else:
-                os.environ["FMD_ATTN_SPLIT"] = old
     ref = oracle.attention(q, rk, rv, length, head, ku, vu)
     # The newest keys dominate: O is far from the plain mean of the values.
     assert np.max(np.abs(ref - oracle.bf16_bits_to_f64(cv).mean(axis=1)[None])) > 0.5

@@ -77,12 +77,11 @@ def test_unit_cfg_matches_oracle(name, g):
     _check(workload.get(name), g)
 
 
-def test_unit_cfg_640x368_first_step_sampled_rows():
+def test_unit_cfg_640x368_first_step_every_row():
     # The guided teacher's 640x368-class unit at full size (both branches
     # append 944 tokens to full 60,416-token rings), one step, in the launch
-    # configuration the benchmark times.  After one step each row of z
-    # depends only on that row's attention in the two branches, so the
-    # oracle computes sampled rows one by one (K_u, V_u from every row).
+    # configuration the benchmark times.  The oracle computes every row of
+    # both branches' attention, the guided velocity and the Euler step.
     wl = workload.get("v02_cfg_unit")
     g = workload.CFG_GUIDANCE
     h = wl.sessions[0].h[0]
@@ -90,20 +89,18 @@ def test_unit_cfg_640x368_first_step_sampled_rows():
     (cc, uc, z), = _run(wl, ui, uns, w_qkv, [h], [g])
     si, un = ui.sessions[0], uns[0]
     s = si.shape
-    rng = np.random.default_rng(11)
-    rows = np.unique(np.concatenate([[0, 1, 159, 160, 919, 920, s.n_q - 1],
-                                     rng.choice(s.n_q, 40, replace=False)]))
     q, k_u, v_u = oracle.qkv_projection(si.eps, w_qkv, s.n_heads)
     vs = []
     for rk, rv, sk, sv in ((si.ring_k, si.ring_v, si.slice_k, si.slice_v),
                            (un.ring_k, un.ring_v, un.slice_k, un.slice_v)):
         ring = oracle.kv_append(rk, rv, s.len_before, s.head_before, sk, sv)
-        o = oracle.attention(q, *ring, k_u, v_u, rows=rows)
-        vs.append(oracle.velocity(o.reshape(len(rows), -1), ui.w_o))
-    want = oracle.euler_step(si.eps[rows].astype(np.float64), h,
+        o = oracle.attention(q, *ring, k_u, v_u)
+        vs.append(oracle.velocity(o.reshape(s.n_q, -1), ui.w_o))
+        print("branch done", flush=True)
+    want = oracle.euler_step(si.eps.astype(np.float64), h,
                              oracle.guided_velocity(vs[0], vs[1], g))
-    zg = host_f64(z)[rows]
-    assert_close(zg - si.eps[rows], want - si.eps[rows], "v02 cfg sampled rows dz")
+    zg = host_f64(z)
+    assert_close(zg - si.eps, want - si.eps, "v02 cfg dz (every row)")
     for c, (rk, rv, sk, sv) in ((cc, (si.ring_k, si.ring_v, si.slice_k, si.slice_v)),
                                 (uc, (un.ring_k, un.ring_v, un.slice_k, un.slice_v))):
         _check_caches(c, oracle.kv_append(rk, rv, s.len_before, s.head_before, sk, sv))

@@ -1,0 +1,174 @@
+"""GPU parity at the workloads' full sizes, on every output row.
+
+Each workload runs as the benchmark launches it: every session of the unit in
+one ``denoise_unit`` call (append, then every solver step).  Afterwards the
+attention output of every step is taken through ``fmd_attention`` on the
+post-append rings, with the same key-split plan as inside the unit (the plan
+depends only on the shapes), and compared element by element with the oracle:
+every row and head of O for the steps named below, and ``dz = z - eps``.
+
+Tolerances: max-abs 2e-2 and rel-L2 1e-2 on O and dz (rel-L2 on its own is the
+binding check: with N(0,1) inputs |O| is about 0.007 at 60k keys).
+
+The attention these outputs follow: every block being denoised sees all
+earlier (clean) blocks and itself in full [Wan-Streamer (gongshangzheng blog),
+3.3 Block-Causal Transformer; 3.4 条件流匹配].
+"""
+import numpy as np
+import pytest
+
+import oracle
+import workload
+
+import flow_matching_denoising_amd as fmd  # noqa: E402  (no fallback: fails if not built)
+import torch  # noqa: E402
+from tests.gpu_util import DEV, assert_close, dev_bf16, host_f64, host_u16, make_cache  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+
+class _UnitRun:
+    """One full-size unit on the GPU and its per-step attention outputs."""
+
+    def __init__(self, name):
+        wl = workload.get(name)
+        ui = workload.make_inputs(wl, poison_invalid=True)
+        caches, ios, zs = [], [], []
+        for si in ui.sessions:
+            s = si.shape
+            c = make_cache(fmd, s, si.ring_k, si.ring_v)
+            z = torch.from_numpy(si.eps.copy()).to(DEV)
+            ios.append(fmd.UnitIO(c, dev_bf16(si.slice_k), dev_bf16(si.slice_v),
+                                  dev_bf16(np.stack(si.q)), dev_bf16(np.stack(si.k_u)),
+                                  dev_bf16(np.stack(si.v_u)), z, list(s.h), n_audio=s.n_audio))
+            caches.append(c)
+            zs.append(z)
+        print(f"{name}: {len(ui.sessions)} session(s), running the unit", flush=True)
+        fmd.denoise_unit(ios, dev_bf16(ui.w_o))
+        torch.cuda.synchronize()
+        self.name, self.wl, self.ui = name, wl, ui
+        self.z = [host_f64(z) for z in zs]
+        self.state = [(c.len_tokens, c.head_tokens) for c in caches]
+        # O of every step, all sessions in one launch (bf16 bits, per session).
+        self.o = []
+        n_steps = wl.sessions[0].n_steps
+        for st in range(n_steps):
+            units = [fmd.UnitStep(c, dev_bf16(si.q[st]), dev_bf16(si.k_u[st]),
+                                  dev_bf16(si.v_u[st]), n_audio=si.shape.n_audio)
+                     for si, c in zip(ui.sessions, caches)]
+            o = host_u16(fmd.attention(units))
+            per, r0 = [], 0
+            for si in ui.sessions:
+                per.append(o[r0:r0 + si.shape.n_q])
+                r0 += si.shape.n_q
+            self.o.append(per)
+        del caches, ios, zs
+        torch.cuda.empty_cache()
+
+    def post_append_ring(self, b):
+        si = self.ui.sessions[b]
+        s = si.shape
+        rk, rv, ln, hd_ = oracle.kv_append(si.ring_k, si.ring_v, s.len_before, s.head_before,
+                                           si.slice_k, si.slice_v)[:4]
+        assert self.state[b] == (ln, hd_), f"{self.name} session {b} ring state"
+        return rk, rv, ln, hd_
+
+    def oracle_o(self, b, st, ring, rows=None):
+        si = self.ui.sessions[b]
+        return oracle.attention(si.q[st], *ring, si.k_u[st], si.v_u[st], rows=rows)
+
+    def gpu_o(self, b, st, rows=None):
+        o = oracle.bf16_bits_to_f64(self.o[st][b])
+        return o if rows is None else o[rows]
+
+
+def _wave_slot_rows(n_q, salt=0):
+    """One row in every 32-row wave slot of every 256-row query block, at a
+    lane that varies from slot to slot, plus the last row."""
+    rows = [w * 32 + (w * 13 + salt * 7 + 5) % 32 for w in range((n_q + 31) // 32)]
+    rows = [min(r, n_q - 1) for r in rows] + [n_q - 1]
+    return np.unique(rows)
+
+
+@pytest.fixture(scope="module")
+def v02_unit():
+    return _UnitRun("v02_unit")
+
+
+@pytest.fixture(scope="module")
+def v02_long():
+    return _UnitRun("v02_long")
+
+
+@pytest.fixture(scope="module")
+def v02_batch8():
+    return _UnitRun("v02_batch8")
+
+
+def test_v02_unit_every_output(v02_unit):
+    # 640x368-class unit: O of all four steps on every row and head, and dz
+    # on every row after the four Euler steps.
+    run = v02_unit
+    s = run.wl.sessions[0]
+    ring = run.post_append_ring(0)
+    dz_ref = np.zeros((s.n_q, s.d))
+    for st in range(s.n_steps):
+        O = run.oracle_o(0, st, ring)
+        assert_close(run.gpu_o(0, st).reshape(s.n_q, -1), O.reshape(s.n_q, -1),
+                     f"v02_unit step {st} O (all {s.n_q} rows x {s.n_heads} heads)")
+        dz_ref -= s.h[st] * oracle.velocity(O.reshape(s.n_q, -1), run.ui.w_o)
+        del O
+    eps = run.ui.sessions[0].eps
+    assert_close(run.z[0] - eps, dz_ref, "v02_unit dz (every row, 4 steps)")
+
+
+def test_v02_long_every_row_first_step(v02_long):
+    # Wrapped 256-unit ring (241,664 keys in two segments): O of the first
+    # step on every row and head.
+    run = v02_long
+    s = run.wl.sessions[0]
+    ring = run.post_append_ring(0)
+    O = run.oracle_o(0, 0, ring)
+    assert_close(run.gpu_o(0, 0).reshape(s.n_q, -1), O.reshape(s.n_q, -1),
+                 f"v02_long step 0 O (all {s.n_q} rows x {s.n_heads} heads)")
+
+
+def test_v02_long_dz_wave_slots(v02_long):
+    # dz after the four steps on one row of every wave slot of every query
+    # block (every step's O computed by the oracle for those rows).
+    run = v02_long
+    s = run.wl.sessions[0]
+    ring = run.post_append_ring(0)
+    rows = _wave_slot_rows(s.n_q)
+    dz_ref = np.zeros((len(rows), s.d))
+    for st in range(s.n_steps):
+        O = run.oracle_o(0, st, ring, rows=rows)
+        assert_close(run.gpu_o(0, st, rows).reshape(len(rows), -1),
+                     O.reshape(len(rows), -1), f"v02_long step {st} O ({len(rows)} rows)")
+        dz_ref -= s.h[st] * oracle.velocity(O.reshape(len(rows), -1), run.ui.w_o)
+    eps = run.ui.sessions[0].eps[rows]
+    assert_close(run.z[0][rows] - eps, dz_ref, "v02_long dz (wave-slot rows, 4 steps)")
+
+
+@pytest.mark.parametrize("b", range(8))
+def test_v02_batch8_session(v02_batch8, b):
+    # Eight ragged sessions in one call: for session b, O of the first step
+    # on every row and head, O of the later steps and dz after the
+    # [0.4, 0.3, 0.2, 0.1] schedule on one row of every wave slot.
+    run = v02_batch8
+    s = run.wl.sessions[b]
+    ring = run.post_append_ring(b)
+    print(f"session {b}: {s.len_after} cached keys, ring head {s.head_after}", flush=True)
+    O = run.oracle_o(b, 0, ring)
+    assert_close(run.gpu_o(b, 0).reshape(s.n_q, -1), O.reshape(s.n_q, -1),
+                 f"v02_batch8 session {b} step 0 O (all rows)")
+    rows = _wave_slot_rows(s.n_q, salt=b)
+    dz_ref = -s.h[0] * oracle.velocity(O[rows].reshape(len(rows), -1), run.ui.w_o)
+    del O
+    for st in range(1, s.n_steps):
+        O = run.oracle_o(b, st, ring, rows=rows)
+        assert_close(run.gpu_o(b, st, rows).reshape(len(rows), -1), O.reshape(len(rows), -1),
+                     f"v02_batch8 session {b} step {st} O ({len(rows)} rows)")
+        dz_ref -= s.h[st] * oracle.velocity(O.reshape(len(rows), -1), run.ui.w_o)
+    eps = run.ui.sessions[b].eps[rows]
+    assert_close(run.z[b][rows] - eps, dz_ref, f"v02_batch8 session {b} dz (wave-slot rows)")
