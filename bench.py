@@ -355,35 +355,117 @@ def append_batch_probe(launches=20):
             "frac_hbm": round(nbytes / avg_s / 1e9 / HBM_PEAK_GBS, 4)}
 
 
-def cpu_baseline(wl, ui, args):
-    """The oracle, as it stands, on a bounded sample of one unit."""
-    import numpy as np
-    import oracle
+CPU_THREADS_MAX = 16   # the host cores one GPU's share of the box provides
+
+
+def _cpu_threads():
     try:
-        from threadpoolctl import threadpool_info
-        cores = max((p.get("num_threads", 1) for p in threadpool_info()), default=1)
-    except Exception:  # pragma: no cover
-        cores = len(os.sched_getaffinity(0))
-    si = ui.sessions[0]
-    s = si.shape
-    rk, rv, ln, hd_ = oracle.kv_append(si.ring_k, si.ring_v, s.len_before, s.head_before,
-                                       si.slice_k, si.slice_v)[:4]
-    heads = list(range(s.n_heads))
-    t0 = time.perf_counter()
-    O = oracle.attention(si.q[0], rk, rv, ln, hd_, si.k_u[0], si.v_u[0], heads=heads)
-    t_attn = time.perf_counter() - t0
-    t0 = time.perf_counter()
-    v = oracle.velocity(O.reshape(O.shape[0], -1), ui.w_o)
-    oracle.euler_step(si.eps, s.h[0], v)
-    t_proj = time.perf_counter() - t0
-    t_unit = s.n_steps * (t_attn * s.n_heads / len(heads) + t_proj)
-    _log(args, f"cpu oracle: attention {len(heads)} heads {t_attn:.2f}s, projection {t_proj:.2f}s"
-               f" -> {t_unit:.1f}s per unit")
-    return {"value": 1.0 / t_unit, "unit": "units/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"float64 oracle on one of the unit's {s.n_steps} solver steps: attention "
-                      f"of all {s.n_heads} heads ({s.n_q} queries x {s.keys_per_query} keys), the "
-                      f"{s.n_q}x{s.d}x{s.d} projection and the Euler update "
-                      f"({t_attn + t_proj:.1f} s), scaled by {s.n_steps} steps per unit"}
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        n = os.cpu_count() or 1
+    return max(1, min(CPU_THREADS_MAX, n))
+
+
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
+# Bounded samples of each configuration for the CPU baseline: the sessions,
+# heads and solver steps the oracle computes, scaled to whole units.
+CPU_SAMPLES = (
+    ("v01_unit", None, 12, None),    # the whole unit: every head, every step
+    ("v02_unit", None, 4, 1),        # 4 of 40 heads, 1 of 4 steps
+    ("v02_long", None, 2, 1),        # 2 of 40 heads, 1 of 4 steps
+    ("v02_batch8", None, 1, 1),      # every session, 1 of 40 heads, 1 of 4 steps
+)
+
+
+def cpu_baseline(args, reps=3):
+    """The oracle in its float32 mode (numpy + BLAS, the textbook two-pass
+    softmax, keys gathered per head) timed on this host's cores for every
+    configuration, on a bounded sample of each unit (some heads and steps;
+    the projection and Euler update at full size), scaled to whole units.
+    Median of `reps` repetitions; inputs drawn before the timed region."""
+    import dataclasses
+
+    import numpy as np
+    from threadpoolctl import threadpool_info, threadpool_limits
+
+    import oracle
+    import workload
+
+    threads = _cpu_threads()
+    out = {}
+    with threadpool_limits(limits=threads):
+        blas = [p for p in threadpool_info() if p.get("user_api") == "blas"]
+        for name, sess, heads, steps in CPU_SAMPLES:
+            wl = workload.get(name)
+            s0 = wl.sessions[0]
+            H, S = s0.n_heads, s0.n_steps
+            k = min(heads, H)
+            n_st = S if steps is None else min(steps, S)
+            idx = list(range(len(wl.sessions))) if sess is None else list(sess)
+            # The first k heads of each session: the workload draws every head
+            # from its own stream, so these are exactly the full unit's values.
+            sub = workload.custom_workload(
+                name, wl.seed, [dataclasses.replace(wl.sessions[i], n_heads=k) for i in idx])
+            ui = workload.make_inputs(sub)
+            w_o = workload.projection_weight(wl.seed, wl.d, wl.head_dim)
+            rng = np.random.default_rng(0)
+            o_full = rng.standard_normal((s0.n_q, wl.d)).astype(np.float32)
+            z_full = rng.standard_normal((s0.n_q, wl.d)).astype(np.float32)
+            rep_s = []
+            for _ in range(reps):
+                t_attn = t_app = 0.0
+                for si in ui.sessions:
+                    sh = si.shape
+                    t0 = time.perf_counter()
+                    rk, rv, ln, hd_ = oracle.kv_append(si.ring_k, si.ring_v, sh.len_before,
+                                                       sh.head_before, si.slice_k, si.slice_v)[:4]
+                    t_app += time.perf_counter() - t0
+                    t0 = time.perf_counter()
+                    for st in range(n_st):
+                        oracle.attention(si.q[st], rk, rv, ln, hd_, si.k_u[st], si.v_u[st],
+                                         dtype=np.float32)
+                    t_attn += time.perf_counter() - t0
+                # The projection and Euler update of one session and step at
+                # full size (their cost does not depend on the values).
+                t0 = time.perf_counter()
+                v = oracle.velocity(o_full, w_o, dtype=np.float32)
+                oracle.euler_step(z_full, s0.h[0], v, dtype=np.float32)
+                t_proj = time.perf_counter() - t0
+                scale_h = H / k
+                n_all = len(wl.sessions)
+                t_unit = (t_app * scale_h * n_all / len(idx)
+                          + t_attn * scale_h * (S / n_st) * n_all / len(idx)
+                          + t_proj * S * n_all)
+                rep_s.append(t_unit)
+            med = float(np.median(rep_s))
+            out[name] = {
+                "units_per_s": round(len(wl.sessions) / med, 6),
+                "s_per_unit_reps": [round(x, 3) for x in rep_s],
+                "sample": (f"{len(idx)} of {len(wl.sessions)} session(s), {k} of {H} heads, "
+                           f"{n_st} of {S} steps of attention (+ the append of those heads); "
+                           f"projection and Euler update at full size"),
+            }
+            _log(args, f"cpu oracle {name}: {med:.2f} s per unit (reps {rep_s})")
+            del ui
+    c2 = out["v02_unit"]
+    return {"value": c2["units_per_s"], "unit": "units/s", "cores": threads, "kind": "oracle",
+            "dtype": "f32",
+            "sample": "float32 oracle on v02_unit: " + c2["sample"] + f"; median of {reps} reps",
+            "cpu_model": _cpu_model(),
+            "blas": [{"vendor": b.get("internal_api"), "version": b.get("version"),
+                      "threads": b.get("num_threads")} for b in blas],
+            "per_config": out}
 
 
 def main():
@@ -539,7 +621,8 @@ def main():
         torch.cuda.empty_cache()
         out["append_batch8"] = append_batch_probe()
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(wl, ui, args)
+        del ui
+        out["cpu_baseline"] = cpu_baseline(args)
     print(json.dumps(out), flush=True)
 
 

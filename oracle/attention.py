@@ -16,6 +16,10 @@ rotary encoding is already in the given Q and K); sessions never see each other.
 The definition used is the textbook one: scores, the row maximum, exponentials
 of the shifted scores, their sum, and the weighted mean of the values
 (the maximum is subtracted only to keep exp finite; it cancels exactly).
+
+``dtype`` selects the arithmetic: float64 (the default, the parity reference)
+or float32 (the same steps with BLAS in single precision, used only to time
+the oracle as a CPU baseline; pinned against float64 in the tests).
 """
 from __future__ import annotations
 
@@ -34,18 +38,23 @@ def _softmax_rows(s):
     return p / p.sum(axis=1, keepdims=True)
 
 
-def _gather_head(ring_k, ring_v, length, head, k_u, v_u, h):
+def _widen(bits, dtype):
+    return bf16_bits_to_f64(bits).astype(dtype, copy=False)
+
+
+def _gather_head(ring_k, ring_v, length, head, k_u, v_u, h, dtype=np.float64):
     """Keys/values one head attends to: the valid ring slots, then the unit."""
     cap = ring_k.shape[1]
     slots = np.asarray(valid_slots(length, head, cap), dtype=np.int64)
-    K = np.concatenate([bf16_bits_to_f64(ring_k[h][slots]), bf16_bits_to_f64(k_u[:, h, :])])
-    V = np.concatenate([bf16_bits_to_f64(ring_v[h][slots]), bf16_bits_to_f64(v_u[:, h, :])])
+    K = np.concatenate([_widen(ring_k[h][slots], dtype), _widen(k_u[:, h, :], dtype)])
+    V = np.concatenate([_widen(ring_v[h][slots], dtype), _widen(v_u[:, h, :], dtype)])
     return K, V
 
 
 def attention(q, ring_k, ring_v, length: int, head: int, k_u, v_u,
-              rows=None, heads=None, row_chunk: int = 64):
-    """float64 attention output O [n_rows][H][hd] for one session.
+              rows=None, heads=None, row_chunk: int = 64, dtype=np.float64):
+    """Attention output O [n_rows][H][hd] for one session (float64 unless
+    ``dtype`` says otherwise).
 
     q, k_u, v_u: [n_q][H][hd] bf16 bits; ring_k/ring_v: [H][cap][hd] bf16 bits
     holding the post-append ring; (length, head) its state.
@@ -56,11 +65,11 @@ def attention(q, ring_k, ring_v, length: int, head: int, k_u, v_u,
     n_q, H, hd = q.shape
     rows = np.arange(n_q) if rows is None else np.asarray(rows)
     heads = range(H) if heads is None else heads
-    scale = 1.0 / math.sqrt(hd)
-    out = np.zeros((len(rows), H, hd), dtype=np.float64)
+    scale = dtype(1.0 / math.sqrt(hd))
+    out = np.zeros((len(rows), H, hd), dtype=dtype)
     for h in heads:
-        K, V = _gather_head(ring_k, ring_v, length, head, k_u, v_u, h)
-        Q = bf16_bits_to_f64(q[rows, h, :])
+        K, V = _gather_head(ring_k, ring_v, length, head, k_u, v_u, h, dtype)
+        Q = _widen(q[rows, h, :], dtype)
         for r0 in range(0, len(rows), row_chunk):
             s = (Q[r0:r0 + row_chunk] @ K.T) * scale          # scores
             out[r0:r0 + row_chunk, h, :] = _softmax_rows(s) @ V

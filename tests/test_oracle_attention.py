@@ -126,3 +126,25 @@ def test_attention_vs_sdpa_random_shapes():
                                          head0=head0, n_q=n_q)
         assert err <= 1e-12, (trial, err)
         _ = rel_l2  # noqa
+
+
+@pytest.mark.parametrize("H,hd,cap,length,head,n_q", [
+    (2, 64, 128, 128, 0, 16), (3, 128, 1024, 700, 913, 77), (1, 128, 4096, 4096, 1234, 130)])
+def test_float32_mode_matches_float64(H, hd, cap, length, head, n_q):
+    # The float32 mode (used only to time the oracle on the CPU) computes the
+    # same steps: against the float64 reference its error is single-precision
+    # rounding, and its dtype really is float32.
+    rng = np.random.default_rng(hd + cap)
+    rk, rv = random_bits(rng, (H, cap, hd)), random_bits(rng, (H, cap, hd))
+    q, ku, vu = (random_bits(rng, (n_q, H, hd)) for _ in range(3))
+    a = oracle.attention(q, rk, rv, length, head, ku, vu)
+    b = oracle.attention(q, rk, rv, length, head, ku, vu, dtype=np.float32)
+    assert b.dtype == np.float32
+    assert rel_l2(b, a) <= 1e-5, rel_l2(b, a)
+    w = random_bits(rng, (H * hd, H * hd), scale=(H * hd) ** -0.5)
+    va = oracle.velocity(a.reshape(n_q, -1), w)
+    vb = oracle.velocity(b.reshape(n_q, -1), w, dtype=np.float32)
+    assert vb.dtype == np.float32 and rel_l2(vb, va) <= 1e-5
+    z = rng.standard_normal((n_q, H * hd)).astype(np.float32)
+    za, zb = oracle.euler_step(z, 0.25, va), oracle.euler_step(z, 0.25, vb, dtype=np.float32)
+    assert zb.dtype == np.float32 and np.max(np.abs(zb - za)) <= 1e-5
