@@ -111,6 +111,9 @@ _unit_workspace_bytes = _sig("fmd_unit_workspace_bytes", ctypes.c_int, ctypes.PO
                              _i32, ctypes.POINTER(_sz))
 _denoise_unit = _sig("fmd_denoise_unit", ctypes.c_int, ctypes.POINTER(_UnitIO), _i32, _i32, _vp,
                      _vp, _sz, _vp)
+_denoise_unit_noalloc = _sig("fmd_denoise_unit_noalloc", ctypes.c_int, ctypes.POINTER(_UnitIO),
+                            _i32, _i32, _vp, _vp)
+FMD_NOALLOC_SCRATCH_BYTES = 128 << 20
 _unit_qkv_workspace_bytes = _sig("fmd_unit_qkv_workspace_bytes", ctypes.c_int,
                                  ctypes.POINTER(_UnitQkvIO), _i32, ctypes.POINTER(_sz))
 _denoise_unit_qkv = _sig("fmd_denoise_unit_qkv", ctypes.c_int, ctypes.POINTER(_UnitQkvIO), _i32,
@@ -136,6 +139,7 @@ _test_force_attn_splits = _sig("fmd_test_force_attn_splits", ctypes.c_int, _i32)
 
 EXPORTED = ["fmd_kv_append", "fmd_kv_append_batched", "fmd_workspace_bytes", "fmd_denoise_step",
             "fmd_attention", "fmd_unit_workspace_bytes", "fmd_denoise_unit",
+            "fmd_denoise_unit_noalloc",
             "fmd_unit_qkv_workspace_bytes", "fmd_denoise_unit_qkv",
             "fmd_unit_cfg_workspace_bytes", "fmd_denoise_unit_cfg",
             "fmd_unit_layers_workspace_bytes", "fmd_denoise_unit_layers", "fmd_strerror",
@@ -422,6 +426,20 @@ def denoise_unit(sessions, w_o, workspace=None, stream=None):
                          workspace.numel(), _stream_ptr(stream)))
     # The library advanced each cache's (len, head) in the struct array it was
     # given; the array holds pointers to the caches' own structs, so nothing to copy.
+
+
+def denoise_unit_noalloc(sessions, w_o, stream=None):
+    """denoise_unit without a workspace: the library's static device scratch
+    (FMD_NOALLOC_SCRATCH_BYTES per GPU) holds the kernels' scratch, so the call
+    allocates no device memory.  Calls that overlap on one GPU race."""
+    n_steps = sessions[0].n_steps
+    if any(s.n_steps != n_steps for s in sessions):
+        raise ValueError("all sessions must have the same number of steps")
+    d = sessions[0].cache.n_heads * sessions[0].cache.head_dim
+    _expect_shape(w_o, (d, d), "w_o")
+    arr, n = _io_array(sessions)
+    _check(_denoise_unit_noalloc(arr, n, n_steps, _ptr(w_o, torch.bfloat16, "w_o"),
+                                 _stream_ptr(stream)))
 
 
 class UnitQkvIO:

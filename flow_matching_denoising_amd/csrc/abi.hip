@@ -603,6 +603,47 @@ int enqueue_appends(fmd_kv_cache* const* caches, const void* const* ks, const vo
 
 }  // namespace
 
+// Scratch of fmd_denoise_unit_noalloc: one copy per GPU the library runs on,
+// held until the process ends.  Host code never passes `scratch` itself to a
+// kernel or a copy (in host code the name is a host-side stand-in, not a
+// device address): it uses the address hipGetSymbolAddress returns for the
+// current device, looked up once per device.
+static __device__ __align__(256) char scratch[FMD_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+std::mutex g_scratch_mu;
+std::vector<char*> g_scratch_ptr;   // per device ordinal; nullptr until looked up
+
+// The device address of this GPU's scratch.  `st` must belong to the current
+// device (the address is per device).
+int device_scratch(hipStream_t st, char** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(FMD_E_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (st) {
+    hipDevice_t sdev = -1;
+    e = hipStreamGetDevice(st, &sdev);
+    if (e != hipSuccess) return fail(FMD_E_HIP, "hipStreamGetDevice: %s", hipGetErrorString(e));
+    if (sdev != dev)
+      return fail(FMD_E_INVAL, "stream belongs to device %d, the current device is %d", sdev, dev);
+  }
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if ((int)g_scratch_ptr.size() <= dev) g_scratch_ptr.resize(dev + 1, nullptr);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(FMD_E_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev,
+                  hipGetErrorString(e));
+    g_scratch_ptr[dev] = static_cast<char*>(p);
+  }
+  *out = g_scratch_ptr[dev];
+  return FMD_OK;
+}
+
+}  // namespace
+
 extern "C" {
 
 const char* fmd_version(void) { return "0.2.0"; }
@@ -760,21 +801,12 @@ int fmd_unit_workspace_bytes(const fmd_unit_io* sessions, int32_t n_sessions, si
   return plan_steps(steps.data(), n_sessions, false, plans, out_bytes);
 }
 
-int fmd_denoise_unit(fmd_unit_io* sessions, int32_t n_sessions, int32_t n_steps, const void* w_o,
-                     void* workspace, size_t workspace_bytes, void* stream) {
-  g_last_error.clear();
-  int rc = validate_unit_io(sessions, n_sessions, n_steps);
-  if (rc) return rc;
-  if ((rc = check_tensor(w_o, 0, "w_o"))) return rc;
-  std::vector<fmd_kv_cache> after;
-  std::vector<fmd_unit_step> steps;
-  post_append_steps(sessions, n_sessions, after, steps);
-  std::vector<SessPlan> plans;
-  size_t need = 0;
-  plan_steps(steps.data(), n_sessions, false, plans, &need);
-  if ((rc = check_workspace(workspace, workspace_bytes, need))) return rc;
-
-  hipStream_t st = static_cast<hipStream_t>(stream);
+// One unit (validated, planned): the batched append, then the steps on the
+// given workspace.
+static int run_unit(fmd_unit_io* sessions, int n_sessions, int n_steps, const void* w_o,
+                    std::vector<fmd_unit_step>& steps, const std::vector<SessPlan>& plans,
+                    char* workspace, hipStream_t st) {
+  int rc;
   std::vector<fmd_kv_cache*> caches;
   std::vector<const void*> ks, vs;
   std::vector<int64_t> ts;
@@ -798,11 +830,50 @@ int fmd_denoise_unit(fmd_unit_io* sessions, int32_t n_sessions, int32_t n_steps,
       steps[i].v_u = static_cast<const bf16*>(sessions[i].v_u) + off;
       steps[i].h = sessions[i].h[s];
     }
-    if ((rc = enqueue_steps(steps.data(), n_sessions, plans, w_o, static_cast<char*>(workspace),
-                            nullptr, st)))
+    if ((rc = enqueue_steps(steps.data(), n_sessions, plans, w_o, workspace, nullptr, st)))
       return rc;
   }
   return FMD_OK;
+}
+
+int fmd_denoise_unit(fmd_unit_io* sessions, int32_t n_sessions, int32_t n_steps, const void* w_o,
+                     void* workspace, size_t workspace_bytes, void* stream) {
+  g_last_error.clear();
+  int rc = validate_unit_io(sessions, n_sessions, n_steps);
+  if (rc) return rc;
+  if ((rc = check_tensor(w_o, 0, "w_o"))) return rc;
+  std::vector<fmd_kv_cache> after;
+  std::vector<fmd_unit_step> steps;
+  post_append_steps(sessions, n_sessions, after, steps);
+  std::vector<SessPlan> plans;
+  size_t need = 0;
+  plan_steps(steps.data(), n_sessions, false, plans, &need);
+  if ((rc = check_workspace(workspace, workspace_bytes, need))) return rc;
+  return run_unit(sessions, n_sessions, n_steps, w_o, steps, plans,
+                  static_cast<char*>(workspace), static_cast<hipStream_t>(stream));
+}
+
+int fmd_denoise_unit_noalloc(fmd_unit_io* sessions, int32_t n_sessions, int32_t n_steps,
+                             const void* w_o, void* stream) {
+  g_last_error.clear();
+  int rc = validate_unit_io(sessions, n_sessions, n_steps);
+  if (rc) return rc;
+  if ((rc = check_tensor(w_o, 0, "w_o"))) return rc;
+  std::vector<fmd_kv_cache> after;
+  std::vector<fmd_unit_step> steps;
+  post_append_steps(sessions, n_sessions, after, steps);
+  std::vector<SessPlan> plans;
+  size_t need = 0;
+  plan_steps(steps.data(), n_sessions, false, plans, &need);
+  if (need > (size_t)FMD_NOALLOC_SCRATCH_BYTES)
+    return fail(FMD_E_WORKSPACE,
+                "this unit needs %zu bytes of scratch; the static scratch holds %zu "
+                "(use fmd_denoise_unit with a workspace)",
+                need, (size_t)FMD_NOALLOC_SCRATCH_BYTES);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  char* ws = nullptr;
+  if ((rc = device_scratch(st, &ws))) return rc;
+  return run_unit(sessions, n_sessions, n_steps, w_o, steps, plans, ws, st);
 }
 
 // The z-dependent solver's driver, shared by the plain, the guided and the

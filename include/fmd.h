@@ -194,6 +194,28 @@ int fmd_denoise_unit(fmd_unit_io* sessions, int32_t n_sessions, int32_t n_steps,
                      void* stream);
 
 /*
+ * fmd_denoise_unit without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  Same arguments, semantics, validation
+ * and errors as fmd_denoise_unit, and the same kernels; their scratch is a
+ * static device array of FMD_NOALLOC_SCRATCH_BYTES (128 MiB) that the
+ * library holds on every GPU it runs on until the process ends.  The call
+ * allocates no device memory.
+ *   - A unit whose scratch need (fmd_unit_workspace_bytes) exceeds
+ *     FMD_NOALLOC_SCRATCH_BYTES -> FMD_E_WORKSPACE, nothing enqueued.  The
+ *     640x368-class unit (40 heads x 928 queries, 60,416 cached keys) needs
+ *     about 115 MB and fits; the 242k-key ring of that shape does not.
+ *   - `stream` must belong to the current device (FMD_E_INVAL otherwise).
+ *   - Every call on one GPU shares that GPU's scratch: calls that overlap on
+ *     one GPU (different streams or host threads without ordering) race and
+ *     give wrong results.  Calls ordered on one stream are safe.  Nothing in
+ *     the scratch needs to start at zero; it keeps the last call's contents.
+ */
+#define FMD_NOALLOC_SCRATCH_BYTES (128u << 20)
+int fmd_denoise_unit_noalloc(fmd_unit_io* sessions, int32_t n_sessions, int32_t n_steps,
+                             const void* w_o, void* stream);
+
+/*
  * The solver with the unit's queries, keys and values re-derived from the
  * latent at every step: the velocity network is evaluated on the noisy
  * latents it integrates [Wan-Streamer (gongshangzheng blog), 3.4 条件流匹配:

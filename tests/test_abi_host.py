@@ -382,3 +382,27 @@ def test_split_planner_choices(H, head, splits):
     per_split = n_q * H * (hd * 2 + 4)
     assert (nbytes - staged) % per_split == 0
     assert (nbytes - staged) // per_split == splits
+
+
+def test_noalloc_rejects_units_beyond_the_static_scratch():
+    # The 640x368-class unit over a wrapped 256-unit (241,664-key) ring needs
+    # more scratch than FMD_NOALLOC_SCRATCH_BYTES: rejected with FMD_E_WORKSPACE
+    # before anything touches a device, cache state unchanged.  The same unit
+    # over a 64-unit ring fits (its workspace size is below the limit).
+    h = (ctypes.c_float * 4)(0.25, 0.25, 0.25, 0.25)
+    hp = ctypes.cast(h, ctypes.POINTER(ctypes.c_float))
+    for units, ln, head, fits in ((256, 256, 100, False), (64, 63, 63, True)):
+        cap = units * 944
+        c = _Cache(FAKE, FAKE + 0x100000, 40, 128, cap, ln * 944, head * 944)
+        io = _UnitIO(ctypes.pointer(c), FAKE, FAKE, 944, FAKE, FAKE, FAKE, 928 * 5120,
+                     FAKE, 920, 8, hp)
+        arr = (_UnitIO * 1)(io)
+        need = ctypes.c_size_t(0)
+        assert fmd._unit_workspace_bytes(arr, 1, ctypes.byref(need)) == 0
+        assert (need.value <= fmd.FMD_NOALLOC_SCRATCH_BYTES) == fits, need.value
+        if not fits:
+            assert fmd._denoise_unit_noalloc(arr, 1, 4, FAKE, None) == -5
+            assert b"static scratch" in fmd._last_error()
+            assert (c.len_tokens, c.head_tokens) == (ln * 944, head * 944)
+        # Validation comes first, as for fmd_denoise_unit.
+        assert fmd._denoise_unit_noalloc(arr, 1, 0, FAKE, None) == -1
