@@ -135,7 +135,7 @@ _profile_select = _sig("fmd_profile_select", ctypes.c_int, ctypes.c_uint32)
 _profile_read = _sig("fmd_profile_read", ctypes.c_int, ctypes.c_int,
                      ctypes.POINTER(ctypes.c_double), ctypes.POINTER(_i64))
 _version = _sig("fmd_version", ctypes.c_char_p)
-_test_force_attn_splits = _sig("fmd_test_force_attn_splits", ctypes.c_int, _i32)
+_test_force_attn_groups = _sig("fmd_test_force_attn_groups", ctypes.c_int, _i32)
 
 EXPORTED = ["fmd_kv_append", "fmd_kv_append_batched", "fmd_workspace_bytes", "fmd_denoise_step",
             "fmd_attention", "fmd_unit_workspace_bytes", "fmd_denoise_unit",
@@ -144,7 +144,7 @@ EXPORTED = ["fmd_kv_append", "fmd_kv_append_batched", "fmd_workspace_bytes", "fm
             "fmd_unit_cfg_workspace_bytes", "fmd_denoise_unit_cfg",
             "fmd_unit_layers_workspace_bytes", "fmd_denoise_unit_layers", "fmd_strerror",
             "fmd_last_error", "fmd_profile_enable", "fmd_profile_select", "fmd_profile_read",
-            "fmd_version", "fmd_test_force_attn_splits"]
+            "fmd_version", "fmd_test_force_attn_groups"]
 
 
 def _check(rc: int):
@@ -651,22 +651,22 @@ def denoise_unit_layers(sessions, w_qkv, w_o, workspace=None, stream=None):
                                 workspace.numel(), _stream_ptr(stream)))
 
 
-class forced_attn_splits:
-    """Test helper: ``with forced_attn_splits(n): ...`` runs the enclosed calls
-    with every attention session cut into n key splits (see
-    ``fmd_test_force_attn_splits``); ``None`` leaves the planner's choice."""
+class forced_attn_groups:
+    """Test helper: ``with forced_attn_groups(n): ...`` runs the enclosed calls
+    with every attention launch's window sequence cut into n ranges (see
+    ``fmd_test_force_attn_groups``); ``None`` leaves the planner's choice."""
 
-    def __init__(self, n_splits):
-        self.n = n_splits
+    def __init__(self, n_groups):
+        self.n = n_groups
 
     def __enter__(self):
         if self.n is not None:
-            _check(_test_force_attn_splits(int(self.n)))
+            _check(_test_force_attn_groups(int(self.n)))
         return self
 
     def __exit__(self, *exc):
         if self.n is not None:
-            _check(_test_force_attn_splits(0))
+            _check(_test_force_attn_groups(0))
         return False
 
 

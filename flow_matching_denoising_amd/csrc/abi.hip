@@ -173,8 +173,14 @@ struct SessPlan {
   int n_q, npad;
   int seg_lo[2], seg_hi[2];
   int nwin[3], nwin_total;
-  int split0[4];      // first key split of each segment (a split never crosses one)
-  int n_qblk, nsplit;
+  int n_qblk;
+  // The session's launch (sessions are launched in chunks of
+  // kMaxSessPerLaunch): its window sequence and groups, this session's first
+  // window among one head's, and the partial slots its lanes need (0 when
+  // every lane lies in one group).
+  int lane0, per_head, groups, qb;
+  int64_t total;
+  int npart;
   size_t off_kt, off_vt, off_o, off_opart, off_lse;   // workspace offsets
 };
 
@@ -182,23 +188,6 @@ int nwin_of(int lo, int hi) {
   if (hi <= lo) return 0;
   const int start = lo & ~15;
   return (hi - start + kAttnWindow - 1) / kAttnWindow;
-}
-
-// Distribute about `ns` key splits over the non-empty key segments in
-// proportion to their windows; every non-empty segment gets at least one
-// split and at most one per window, so a split covers >= 1 window of exactly
-// one segment.
-void set_splits(SessPlan& p, int ns) {
-  int acc = 0;
-  for (int t = 0; t < 3; ++t) {
-    p.split0[t] = acc;
-    if (p.nwin[t] > 0) {
-      const int share = (int)llround((double)ns * p.nwin[t] / p.nwin_total);
-      acc += std::max(1, std::min(share, p.nwin[t]));
-    }
-  }
-  p.split0[3] = acc;
-  p.nsplit = acc;
 }
 
 void plan_session(const fmd_kv_cache* c, int n_q, SessPlan& p) {
@@ -223,146 +212,56 @@ void plan_session(const fmd_kv_cache* c, int n_q, SessPlan& p) {
   p.nwin[2] = (n_q + kAttnWindow - 1) / kAttnWindow;
   p.nwin_total = p.nwin[0] + p.nwin[1] + p.nwin[2];
   p.n_qblk = (n_q + kAttnBlockM - 1) / kAttnBlockM;
-  set_splits(p, 1);
 }
 
-// Split count forced through fmd_test_force_attn_splits (0: the planner).
-std::atomic<int> g_forced_splits{0};
+// Group count forced through fmd_test_force_attn_groups (0: the planner).
+std::atomic<int> g_forced_groups{0};
 
-// Key splits.  The item size (64-key windows per work item) trades the
-// dispatch tail against the combine pass, which reads every split's partial
-// output once.  Candidate item counts (every 32 up to 2048 items, then every
-// 256 up to 40 dispatch rounds of the chip) are scored with a model of the
-// launch: every XCD takes a contiguous range of the head-major item order
-// (xcd_remap), and its 32 CUs take the range's items in order, each the next
-// free CU (greedy list scheduling); the score is the slowest XCD's finish time
-// plus the combine work, both in units of one window of one item.  Depends
-// only on the shapes (a test can force a split count instead).
-int plan_split_count(const SessPlan& p, double per_item) {
-  constexpr int kMinWindows = 16;
-  int ns = (int)ceil(p.nwin_total / (per_item > 1 ? per_item : 1.0));
-  ns = std::min(ns, std::max(1, p.nwin_total / kMinWindows));
-  return std::max(1, std::min(ns, p.nwin_total));
+// Groups of a launch.  One work-group per CU, all resident at once: each
+// XCD's 32 CUs take floor(32 / qb) groups, so a group never straddles two
+// XCDs (its work-groups share the keys in one L2).  A group's range costs
+// about two windows of pipeline fill and a piece to merge per lane it cuts,
+// so short sequences get fewer groups (at least kMinGroupWindows windows
+// each).  Queries beyond 32 blocks per session spread a group over XCDs.
+constexpr int kCusPerXcd = kTargetCUs / kNumXcd;
+constexpr int kMinGroupWindows = 8;
+
+int choose_groups(int qb, int64_t total) {
+  const int forced = g_forced_groups.load(std::memory_order_relaxed);
+  if (forced > 0) return (int)std::min<int64_t>(forced, total);
+  int g = qb <= kCusPerXcd ? kNumXcd * (kCusPerXcd / qb) : std::max(1, kTargetCUs / qb);
+  g = (int)std::min<int64_t>(g, std::max<int64_t>(1, total / kMinGroupWindows));
+  return std::max(1, g);
 }
 
-// Windows of split `split` of a session (as the kernel divides them).
-int split_windows(const SessPlan& p, int split) {
-  const int sg = split >= p.split0[2] ? 2 : (split >= p.split0[1] ? 1 : 0);
-  const int ns = p.split0[sg + 1] - p.split0[sg], ls = split - p.split0[sg];
-  return (ls + 1) * p.nwin[sg] / ns - ls * p.nwin[sg] / ns;
-}
-
-// Order of a launch's sessions inside each head's items: longest ring item
-// first, so each XCD ends its range on short items.
-void session_order(const SessPlan* plans, int n, int* order) {
-  std::vector<double> len(n);
-  for (int k = 0; k < n; ++k) {
-    const SessPlan& p = plans[k];
-    order[k] = k;
-    len[k] = p.split0[2] > 0 ? (double)(p.nwin[0] + p.nwin[1]) / p.split0[2] : p.nwin[2];
-  }
-  std::stable_sort(order, order + n, [&](int x, int y) { return len[x] > len[y]; });
-}
-
-constexpr double kItemOverhead = 2.0;      // Q load, pipeline fill, O/LSE store
-constexpr double kCombinePerSplit = 1.3;   // per split of a 928-query session
-
-// Finish time of one XCD whose range is `cnt` items of the periodic order
-// `seq`, starting at position `first` of the period.
-double simulate_range(const std::vector<int>& seq, int64_t first, int64_t cnt) {
-  constexpr int kCus = kTargetCUs / kNumXcd;
-  double cu[kCus] = {};   // binary min-heap of the CUs' finish times
-  const int64_t period = (int64_t)seq.size();
-  int64_t pos = first % period;
-  for (int64_t i = 0; i < cnt; ++i) {
-    // The earliest free CU (the root) takes the item; sift its new finish
-    // time down to restore the heap.
-    const double t = cu[0] + seq[pos] + kItemOverhead;
-    if (++pos == period) pos = 0;
-    int k = 0;
-    for (;;) {
-      int c = 2 * k + 1;
-      if (c >= kCus) break;
-      if (c + 1 < kCus && cu[c + 1] < cu[c]) ++c;
-      if (cu[c] >= t) break;
-      cu[k] = cu[c];
-      k = c;
+// Plan every launch chunk's window sequence and groups.
+void plan_groups(std::vector<SessPlan>& plans, int H) {
+  const int n = (int)plans.size();
+  for (int c0 = 0; c0 < n; c0 += kMaxSessPerLaunch) {
+    const int cn = std::min(kMaxSessPerLaunch, n - c0);
+    int per_head = 0, qb = 1;
+    for (int k = 0; k < cn; ++k) {
+      plans[c0 + k].lane0 = per_head;
+      per_head += plans[c0 + k].nwin_total;
+      qb = std::max(qb, plans[c0 + k].n_qblk);
     }
-    cu[k] = t;
-  }
-  return *std::max_element(cu, cu + kCus);
-}
-
-double combine_cost(const SessPlan& p) {
-  return p.nsplit > 1 ? kCombinePerSplit * p.nsplit * p.n_q / 928.0 : 0.0;
-}
-
-double score_plan(const std::vector<SessPlan>& plans, int H) {
-  std::vector<int> seq;   // windows of one head's items, launch order
-  double combine = 0;
-  for (size_t c0 = 0; c0 < plans.size(); c0 += kMaxSessPerLaunch) {
-    const int cn = (int)std::min<size_t>(kMaxSessPerLaunch, plans.size() - c0);
-    int order[kMaxSessPerLaunch];
-    session_order(plans.data() + c0, cn, order);
-    for (int j = 0; j < cn; ++j) {
-      const SessPlan& p = plans[c0 + order[j]];
-      for (int sp = 0; sp < p.nsplit; ++sp) seq.insert(seq.end(), p.n_qblk, split_windows(p, sp));
-      combine += combine_cost(p);
+    const int64_t total = (int64_t)H * per_head;
+    const int groups = choose_groups(qb, total);
+    for (int k = 0; k < cn; ++k) {
+      SessPlan& p = plans[c0 + k];
+      p.per_head = per_head;
+      p.qb = qb;
+      p.groups = groups;
+      p.total = total;
+      int most = 1;
+      for (int h = 0; h < H; ++h) {
+        const int64_t first = (int64_t)h * per_head + p.lane0;
+        most = std::max(most, piece_of(first, first + p.nwin_total - 1, p.nwin[0], p.nwin[1],
+                                       total, groups) + 1);
+      }
+      p.npart = most > 1 ? most : 0;
     }
   }
-  // XCD ranges as xcd_remap cuts them.  Ranges that start at the same point of
-  // the per-head period and have the same length finish together: each
-  // distinct one is simulated once (with H a multiple of 8, all are alike).
-  const int64_t period = (int64_t)seq.size();
-  const int64_t n = (int64_t)H * period;
-  const int64_t per = (n + kNumXcd - 1) / kNumXcd;
-  const int tall = n % kNumXcd == 0 ? kNumXcd : (int)(n % kNumXcd);
-  std::vector<std::pair<int64_t, int64_t>> seen;
-  double worst = 0;
-  int64_t start = 0;
-  for (int x = 0; x < kNumXcd; ++x) {
-    const int64_t cnt = x < tall ? per : per - 1;
-    const std::pair<int64_t, int64_t> key(start % period, cnt);
-    if (cnt > 0 && std::find(seen.begin(), seen.end(), key) == seen.end()) {
-      seen.push_back(key);
-      worst = std::max(worst, simulate_range(seq, key.first, cnt));
-    }
-    start += cnt;
-  }
-  return worst + combine;
-}
-
-void choose_splits(std::vector<SessPlan>& plans, int H) {
-  const int forced = g_forced_splits.load(std::memory_order_relaxed);
-  if (forced > 0) {
-    for (auto& p : plans) set_splits(p, forced);
-    return;
-  }
-  double work = 0;
-  for (auto& p : plans) work += (double)H * p.n_qblk * p.nwin_total;
-  double best_cost = 1e300, best_per_item = work;
-  std::vector<int> counts(plans.size()), last;
-  for (int target = 32; target <= 40 * kTargetCUs; target += target < 2048 ? 32 : 256) {
-    const double per_item = work / target;
-    for (size_t i = 0; i < plans.size(); ++i) counts[i] = plan_split_count(plans[i], per_item);
-    if (counts == last) continue;   // same plan as the previous candidate
-    last = counts;
-    // A lower bound of the score (the slowest XCD finishes no earlier than
-    // the average one) skips the simulation of candidates that cannot win.
-    double items = 0, combine = 0;
-    for (size_t i = 0; i < plans.size(); ++i) {
-      set_splits(plans[i], counts[i]);
-      items += (double)H * plans[i].n_qblk * plans[i].nsplit;
-      combine += combine_cost(plans[i]);
-    }
-    if ((work + kItemOverhead * items) / kTargetCUs + combine >= best_cost) continue;
-    const double cost = score_plan(plans, H);
-    if (cost < best_cost - 1e-9) {
-      best_cost = cost;
-      best_per_item = per_item;
-    }
-  }
-  for (auto& p : plans) set_splits(p, plan_split_count(p, best_per_item));
 }
 
 // Workspace layout, sessions in order.  With o_external, O goes to the
@@ -377,10 +276,10 @@ size_t layout_workspace(std::vector<SessPlan>& plans, int H, int hd, bool o_exte
     p.off_o = off;
     if (!o_external) off = align256(off + (size_t)p.n_q * H * hd * 2);
     p.off_opart = p.off_lse = off;
-    if (p.nsplit > 1) {
-      off = align256(off + (size_t)p.nsplit * p.n_q * H * hd * 2);
+    if (p.npart > 0) {
+      off = align256(off + (size_t)p.npart * p.n_q * H * hd * 2);
       p.off_lse = off;
-      off = align256(off + (size_t)p.nsplit * p.n_q * H * 4);
+      off = align256(off + (size_t)p.npart * p.n_q * H * 4);
     }
   }
   return off;
@@ -392,7 +291,7 @@ int plan_steps(const fmd_unit_step* units, int n, bool o_external, std::vector<S
   plans.resize(n);
   for (int i = 0; i < n; ++i)
     plan_session(units[i].cache, units[i].n_video + units[i].n_audio, plans[i]);
-  choose_splits(plans, H);
+  plan_groups(plans, H);
   *bytes = layout_workspace(plans, H, hd, o_external);
   return FMD_OK;
 }
@@ -460,7 +359,6 @@ int enqueue_steps(const fmd_unit_step* units, int n, const std::vector<SessPlan>
     pa.w = static_cast<const bf16*>(w_o);
     bool any_split = false;
     bf16* o_prev = nullptr;
-    AttnSess asess[kMaxSessPerLaunch];
     for (int k = 0; k < cn; ++k) {
       const fmd_unit_step& u = units[c0 + k];
       const SessPlan& p = plans[c0 + k];
@@ -480,7 +378,7 @@ int enqueue_steps(const fmd_unit_step* units, int n, const std::vector<SessPlan>
                        p.n_q, p.npad / 16, va.items, 0};
       if (!second) va.items += H * (p.npad / 16);
 
-      AttnSess& as = asess[k];
+      AttnSess& as = aa.s[k];
       as.q = static_cast<const bf16*>(u.q);
       as.kt_u = kt;
       as.vt_u = vt;
@@ -497,12 +395,17 @@ int enqueue_steps(const fmd_unit_step* units, int n, const std::vector<SessPlan>
         as.seg_hi[t] = p.seg_hi[t];
       }
       for (int t = 0; t < 3; ++t) as.nwin[t] = p.nwin[t];
-      for (int t = 0; t < 4; ++t) as.split0[t] = p.split0[t];
+      as.nwin_total = p.nwin_total;
       as.n_qblk = p.n_qblk;
-      as.nsplit = p.nsplit;
+      as.lane0 = p.lane0;
+      aa.per_head = ca.per_head = p.per_head;
+      aa.groups = ca.groups = p.groups;
+      aa.qb = p.qb;
+      aa.total = ca.total = p.total;
 
-      ca.s[k] = CombineSess{as.opart, as.lse, o, p.n_q, p.nsplit, ca.items, 0};
-      if (p.nsplit > 1) {
+      ca.s[k] = CombineSess{as.opart, as.lse, o,         p.n_q,       p.nwin_total,
+                            p.lane0,  p.nwin[0], p.nwin[1], ca.items};
+      if (p.npart > 0) {
         ca.items += p.n_q * H;
         any_split = true;
       }
@@ -521,21 +424,9 @@ int enqueue_steps(const fmd_unit_step* units, int n, const std::vector<SessPlan>
                          {nullptr, nullptr, nullptr}, p.n_q, mtiles, pa.items, u.h};
       pa.items += mtiles * ntiles;
     }
-    // Attention items, head-major over the sessions.  Inside a head the
-    // sessions go longest ring item first, so each XCD ends its range on short
-    // items.
-    {
-      int order[kMaxSessPerLaunch];
-      session_order(plans.data() + c0, cn, order);
-      for (int j = 0; j < cn; ++j) {
-        aa.s[j] = asess[order[j]];
-        aa.s[j].hoff = aa.per_head;
-        aa.per_head += aa.s[j].nsplit * aa.s[j].n_qblk;
-      }
-      aa.items = H * aa.per_head;
-    }
-    // Sessions without splits take no combine items; the combine kernel finds
-    // its session by item0, so give them an empty range at the current end.
+    // Sessions whose lanes all lie in one group take no combine items; the
+    // combine kernel finds its session by item0, so they get an empty range
+    // at the current end.
     int rc;
     if ((rc = timed_launch(FMD_KERNEL_VT, st, [&] { return launch_vt(va, hd, st); }))) return rc;
     if ((rc = timed_launch(FMD_KERNEL_ATTN, st, [&] { return launch_attn(aa, hd, st); })))
@@ -648,10 +539,10 @@ extern "C" {
 
 const char* fmd_version(void) { return "0.2.0"; }
 
-int fmd_test_force_attn_splits(int32_t n_splits) {
+int fmd_test_force_attn_groups(int32_t n_groups) {
   g_last_error.clear();
-  if (n_splits < 0) return fail(FMD_E_INVAL, "n_splits=%d (must be >= 0)", n_splits);
-  g_forced_splits.store(n_splits, std::memory_order_relaxed);
+  if (n_groups < 0) return fail(FMD_E_INVAL, "n_groups=%d (must be >= 0)", n_groups);
+  g_forced_groups.store(n_groups, std::memory_order_relaxed);
   return FMD_OK;
 }
 

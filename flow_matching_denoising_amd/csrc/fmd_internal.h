@@ -81,6 +81,18 @@ __device__ __forceinline__ void dma16(const i32x4& rs, int voff, int soff, char*
                    : "memory", "m0");
 }
 
+// The same with the LDS destination given as a wave-uniform base plus an
+// offset, added in the instruction sequence itself (s_add_u32 into M0): the
+// compiler then keeps one base register instead of one per destination.
+__device__ __forceinline__ void dma16_at(const i32x4& rs, int voff, int soff, uint32_t lds_base,
+                                         uint32_t lds_off) {
+  __asm__ volatile(
+      "s_add_u32 m0, %0, %1\n\ts_nop 0\n\tbuffer_load_dwordx4 %2, %3, %4 offen lds"
+      :
+      : "s"(lds_base), "s"(lds_off), "v"(voff), "s"(rs), "s"(soff)
+      : "memory", "m0", "scc");
+}
+
 // s_waitcnt immediate (gfx9 encoding): vmcnt in bits 3:0 and 15:14,
 // expcnt (left at its maximum, 7) in bits 6:4, lgkmcnt in bits 11:8.
 constexpr int vmcnt_imm(int vm, int lgkm) {
@@ -144,46 +156,79 @@ struct AttnSess {
   const bf16* vt_u;   // [H][npad/16][hd][16]   (workspace copy of the unit's values)
   const bf16* ring_k; // [H][cap][hd]
   const bf16* ring_v; // [H][cap/16][hd][16]
-  bf16* o;            // [n_q][H][hd]            (when nsplit == 1)
-  bf16* opart;        // [nsplit][n_q][H][hd]    (when nsplit > 1)
-  float* lse;         // [nsplit][n_q][H]
+  bf16* o;            // [n_q][H][hd]            (lanes that lie in one group)
+  bf16* opart;        // [npart][n_q][H][hd]     (pieces of lanes cut by group ends)
+  float* lse;         // [npart][n_q][H]
   int64_t cap;
   int32_t n_q;
   int32_t npad;       // n_q rounded up to 16
   int32_t seg_lo[2];  // valid ring slots: [seg_lo[i], seg_hi[i])
   int32_t seg_hi[2];
   int32_t nwin[3];    // 64-key windows over ring seg 0, ring seg 1, unit keys
-  int32_t split0[4];  // key splits of segment t: [split0[t], split0[t+1]); split0[3] = nsplit
+  int32_t nwin_total; // nwin[0] + nwin[1] + nwin[2]: the windows of one lane
   int32_t n_qblk;
-  int32_t nsplit;
-  int32_t hoff;       // first item of this session among one head's items
+  int32_t lane0;      // first window of this session among one head's windows
 };
-// Items are numbered head-major over all sessions of the launch: head h's
-// items are [h * per_head, (h + 1) * per_head), and inside them session i
-// takes [hoff, hoff + nsplit * n_qblk) (hoff increasing with i).  Every XCD's
-// contiguous range of items then holds the same mix of sessions.
+// The windows of a launch form one sequence: head-major, then session (lane =
+// (head, session), windows [lane0, lane0 + nwin_total) of the head's
+// per_head windows), then the session's segments in order.  The sequence is
+// cut into `groups` equal contiguous ranges; group g covers
+// [g*total/groups, (g+1)*total/groups) with `qb` work-groups, one per 256-row
+// query block, that walk the range together as spans (piece_of).
 struct AttnArgs {
   AttnSess s[kMaxSessPerLaunch];
   int32_t n_sess;
   int32_t H;
-  int32_t per_head;   // items per head, all sessions
-  int32_t items;      // H * per_head
+  int32_t per_head;   // windows of one head over all sessions of the launch
+  int32_t groups;
+  int32_t qb;         // work-groups per group (the largest n_qblk)
+  int64_t total;      // H * per_head
   float scale_log2;   // log2(e) / sqrt(head_dim)
 };
+
+// The group holding window x of a launch's window sequence (the largest g
+// with g*total/groups <= x), and the first window of group g.  Host and
+// device use these definitions.
+__host__ __device__ __forceinline__ int group_of(int64_t x, int64_t total, int groups) {
+  return (int)(((x + 1) * groups - 1) / total);
+}
+__host__ __device__ __forceinline__ int64_t group_start(int g, int64_t total, int groups) {
+  return (int64_t)g * total / groups;
+}
+
+// A lane's pieces: its windows [first, first + nwin_total) cut at every group
+// start inside it and at the starts of its second and third key segment
+// (first + n0 and first + n0 + n1, when the segment before is non-empty).
+// Returns the index of the piece holding window x (the number of distinct
+// cuts in (first, x]); a lane with piece_of(first, last) == 0 is one piece.
+__host__ __device__ inline int piece_of(int64_t first, int64_t x, int n0, int n1, int64_t total,
+                                        int groups) {
+  int k = group_of(x, total, groups) - group_of(first, total, groups);
+  const int64_t cuts[2] = {n0 > 0 ? first + n0 : -1, n1 > 0 ? first + n0 + n1 : -1};
+  for (int t = 0; t < 2; ++t) {
+    const int64_t c = cuts[t];
+    if (c > first && c <= x && group_start(group_of(c, total, groups), total, groups) != c) ++k;
+  }
+  return k;
+}
 
 struct CombineSess {
   const bf16* opart;
   const float* lse;
   bf16* o;
   int32_t n_q;
-  int32_t nsplit;
+  int32_t nwin_total;
+  int32_t lane0;
+  int32_t n0, n1;     // windows of the ring segments (the lane's cuts)
   int32_t item0;      // first (row, head) group handled by this session
-  int32_t pad_;
 };
 struct CombineArgs {
   CombineSess s[kMaxSessPerLaunch];
   int32_t n_sess;
   int32_t H;
+  int32_t per_head;
+  int32_t groups;
+  int64_t total;
   int32_t items;
 };
 

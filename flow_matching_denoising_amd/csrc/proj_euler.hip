@@ -20,7 +20,10 @@
 // which keeps the ds_read_b128 operand reads (16 lanes = 16 rows of one
 // chunk per LDS cycle) free of bank conflicts.  The buffer resources cover
 // exactly the tile's valid rows, so rows past n_q (or past d for W) read as
-// zeros.  Three LDS stages (108 KiB) keep two k steps of loads in flight.
+// zeros.  Four LDS stages (144 KiB) keep three k steps of loads in flight:
+// the operands come mostly from other work-groups' misses in L2 and the
+// Infinity Cache, so the bytes a CU has in flight, not the L2 bandwidth,
+// set its load rate.
 // Item order inside a session: output-feature tile major, row tile minor, so
 // the row tiles that share one slab of W are adjacent and run on the same XCD.
 #include "fmd_internal.h"
@@ -34,14 +37,15 @@ constexpr int BN = kProjTileN;                      // 128 output features
 constexpr int BK = 64;
 constexpr int WAVES = 4;
 constexpr int MT = BM / 32;                         // 5 row tiles of 32
-constexpr int STAGES = 3;
+constexpr int STAGES = 4;
 constexpr int A_BLOCKS = BM / 8;                    // 20 blocks of 8 rows x 64 k
 constexpr int B_BLOCKS = BN / 8;                    // 16
 constexpr int STAGE_BYTES = (A_BLOCKS + B_BLOCKS) * 1024;
 constexpr int LOADS_PER_WAVE = (A_BLOCKS + B_BLOCKS) / WAVES;   // 9
-constexpr int LDS_BYTES = STAGES * STAGE_BYTES;     // 108 KiB
+constexpr int LDS_BYTES = STAGES * STAGE_BYTES;     // 144 KiB
 static_assert(A_BLOCKS % WAVES == 0 && B_BLOCKS % WAVES == 0, "loads must split evenly over waves");
 static_assert(BN == 32 * WAVES, "one 32-feature column tile per wave");
+static_assert((STAGES & (STAGES - 1)) == 0, "the stage index wraps with a mask");
 
 }  // namespace
 
@@ -103,11 +107,11 @@ __global__ __launch_bounds__(WAVES * 64) void proj_kernel(ProjArgs a) {
 #pragma unroll
   for (int i = 0; i < MT; ++i) acc[i] = f32x16{};
   const int nk = d / BK;
-  // Pipeline: three LDS stages, k step t in buffer t % 3.  The barrier that
+  // Pipeline: four LDS stages, k step t in buffer t % 4.  The barrier that
   // publishes k step t+1 sits DA slots before the end of k step t, right
   // after every wave has issued its last read of buffer t: the reads of
   // k step t+1's first operands then overlap the last MFMAs of k step t, and
-  // the DMA of k step t+3 (into buffer t % 3) is issued after that barrier.
+  // the DMA of k step t+4 (into buffer t % 4) is issued after that barrier.
   // MFMA slot sl = kc*MT + i multiplies A fragment (kc, i) by B fragment kc;
   // every slot issues the read of the A fragment DA slots ahead (and the B
   // fragment of a k chunk that starts there), continuing into the next k step.
@@ -123,7 +127,10 @@ __global__ __launch_bounds__(WAVES * 64) void proj_kernel(ProjArgs a) {
   load_stage(0, 0);
   if (nk > 1) load_stage(1, 1);
   if (nk > 2) load_stage(2, 2);
-  if (nk > 2)
+  if (nk > 3) load_stage(3, 3);
+  if (nk > 3)
+    wait_loads_and_sync<3 * LOADS_PER_WAVE>();
+  else if (nk > 2)
     wait_loads_and_sync<2 * LOADS_PER_WAVE>();
   else if (nk > 1)
     wait_loads_and_sync<LOADS_PER_WAVE>();
@@ -135,7 +142,7 @@ __global__ __launch_bounds__(WAVES * 64) void proj_kernel(ProjArgs a) {
   for (int sl = 0; sl < DA; ++sl) ar[sl % RA] = aread(lds, sl);
   int st = 0;
   for (int kt = 0; kt < nk; ++kt) {
-    const int stn = st == 2 ? 0 : st + 1;       // buffer of k step kt+1
+    const int stn = (st + 1) & (STAGES - 1);    // buffer of k step kt+1
     const char* al = lds + st * STAGE_BYTES;
     const char* aln = lds + stn * STAGE_BYTES;
     const bool more = kt + 1 < nk;
@@ -144,15 +151,18 @@ __global__ __launch_bounds__(WAVES * 64) void proj_kernel(ProjArgs a) {
     for (int sl = 0; sl < NS; ++sl) {
       if (sl == NS - DA && more) {
         // This wave's reads of buffer st are all issued; wait for them and
-        // for k step kt+1's DMA, then barrier.
-        if (kt + 2 < nk)
+        // for k step kt+1's DMA (k steps kt+2 and kt+3 may stay in flight),
+        // then barrier.
+        if (kt + 3 < nk)
+          __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * LOADS_PER_WAVE, 0));
+        else if (kt + 2 < nk)
           __builtin_amdgcn_s_waitcnt(vmcnt_imm(LOADS_PER_WAVE, 0));
         else
           __builtin_amdgcn_s_waitcnt(vmcnt_imm(0, 0));
         __asm__ volatile("" ::: "memory");
         __syncthreads();
         __asm__ volatile("" ::: "memory");
-        if (kt + 3 < nk) load_stage(kt + 3, st);
+        if (kt + 4 < nk) load_stage(kt + 4, st);
       }
       const int nx = sl + DA;
       if (nx < NS) {
@@ -173,61 +183,64 @@ __global__ __launch_bounds__(WAVES * 64) void proj_kernel(ProjArgs a) {
   const int n = n0 + wave * 32 + r;
   if (n >= n_out) return;
   const bool full = m0 + BM <= n_q;                // uniform
+  // Every z (and r) value of the lane's 160 rows is loaded before the first
+  // store: the stores to z could alias later loads as far as the compiler
+  // knows, so loads issued per row tile would wait out the memory latency
+  // once per tile.
+  auto row = [&](int i, int q) { return m0 + i * 32 + (q >> 2) * 8 + g * 4 + (q & 3); };
   if constexpr (MODE == kProjEuler) {
-    // z[m][n] -= h * y[m][n] (and zb = bf16(z)).  All of a row tile's z
-    // values are loaded before any is stored, so the loads overlap.
+    // z[m][n] -= h * y[m][n] (and zb = bf16(z)).
     float* const zc = z + n;
     bf16* const zbc = s.zb ? s.zb + n : nullptr;
+    float zv[MT][16];
 #pragma unroll
-    for (int i = 0; i < MT; ++i) {
-      float zv[16];
+    for (int i = 0; i < MT; ++i)
+#pragma unroll
+      for (int q = 0; q < 16; ++q)
+        zv[i][q] = (full || row(i, q) < n_q) ? zc[(int64_t)row(i, q) * d] : 0.f;
+#pragma unroll
+    for (int i = 0; i < MT; ++i)
 #pragma unroll
       for (int q = 0; q < 16; ++q) {
-        const int m = m0 + i * 32 + (q >> 2) * 8 + g * 4 + (q & 3);
-        zv[q] = (full || m < n_q) ? zc[(int64_t)m * d] : 0.f;
-      }
-#pragma unroll
-      for (int q = 0; q < 16; ++q) {
-        const int m = m0 + i * 32 + (q >> 2) * 8 + g * 4 + (q & 3);
+        const int m = row(i, q);
         if (full || m < n_q) {
-          const float zn = zv[q] - hstep * acc[i][q];
+          const float zn = zv[i][q] - hstep * acc[i][q];
           zc[(int64_t)m * d] = zn;
           if (zbc) zbc[(int64_t)m * d] = (bf16)zn;
         }
       }
-    }
   } else if constexpr (MODE == kProjLayer || MODE == kProjLayerLast) {
     // Residual stream of a layer stack (see kProjLayer / kProjLayerLast).
     float* const zc = z + n;
     float* const rc = s.r + n;
     bf16* const zbc = s.zb ? s.zb + n : nullptr;
+    float zv[MT][16], rv[MT][16];
 #pragma unroll
-    for (int i = 0; i < MT; ++i) {
-      float zv[16], rv[16];
+    for (int i = 0; i < MT; ++i)
 #pragma unroll
       for (int q = 0; q < 16; ++q) {
-        const int m = m0 + i * 32 + (q >> 2) * 8 + g * 4 + (q & 3);
-        const bool in = full || m < n_q;
-        zv[q] = in ? zc[(int64_t)m * d] : 0.f;
-        rv[q] = in ? rc[(int64_t)m * d] : 0.f;
+        const bool in = full || row(i, q) < n_q;
+        zv[i][q] = in ? zc[(int64_t)row(i, q) * d] : 0.f;
+        rv[i][q] = in ? rc[(int64_t)row(i, q) * d] : 0.f;
       }
 #pragma unroll
+    for (int i = 0; i < MT; ++i)
+#pragma unroll
       for (int q = 0; q < 16; ++q) {
-        const int m = m0 + i * 32 + (q >> 2) * 8 + g * 4 + (q & 3);
+        const int m = row(i, q);
         if (full || m < n_q) {
-          const float rn = rv[q] + acc[i][q];
+          const float rn = rv[i][q] + acc[i][q];
           if constexpr (MODE == kProjLayer) {
             rc[(int64_t)m * d] = rn;
-            if (zbc) zbc[(int64_t)m * d] = (bf16)(zv[q] + rn);
+            if (zbc) zbc[(int64_t)m * d] = (bf16)(zv[i][q] + rn);
           } else {
-            const float zn = zv[q] - hstep * rn;
+            const float zn = zv[i][q] - hstep * rn;
             zc[(int64_t)m * d] = zn;
             rc[(int64_t)m * d] = 0.f;
             if (zbc) zbc[(int64_t)m * d] = (bf16)zn;
           }
         }
       }
-    }
   }
 }
 

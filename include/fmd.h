@@ -392,14 +392,14 @@ int fmd_profile_read(int kernel_class, double* total_ms, int64_t* launches);
  * already taken are kept. */
 int fmd_profile_select(uint32_t class_mask);
 
-/* TEST ENTRY (not for production callers).  Forces every session of later
- * attention launches to n_splits key splits (clamped per key segment to its
- * window count, as the planner clamps); 0 restores the planner's choice.
- * Process-wide: it changes the work decomposition of every later call from
- * any thread, never the result beyond fp32 summation order.  Lets tests
- * drive the kernel's single-split path and particular split counts.
- * n_splits < 0 -> FMD_E_INVAL. */
-int fmd_test_force_attn_splits(int32_t n_splits);
+/* TEST ENTRY (not for production callers).  Later attention launches cut
+ * their window sequence into n_groups ranges (at most one per window) instead
+ * of the planner's count; 0 restores the planner.  Process-wide: it changes
+ * the work decomposition of every later call from any thread, never the
+ * result beyond fp32 summation order.  Lets tests drive the one-group path
+ * (no piece to merge) and particular cuts of the lanes.
+ * n_groups < 0 -> FMD_E_INVAL. */
+int fmd_test_force_attn_groups(int32_t n_groups);
 
 /* Library version, "major.minor.patch". */
 const char* fmd_version(void);

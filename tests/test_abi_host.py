@@ -366,43 +366,77 @@ def test_profile_select_rejects_unknown_classes():
     assert fmd._profile_select((1 << n) - 1) == 0
 
 
-@pytest.mark.parametrize("H,head,splits", [(5, 59472, 12), (10, 59472, 8), (40, 59472, 10),
-                                           (40, 0, 9)])
-def test_split_planner_choices(H, head, splits):
-    # The key-split count the launch model picks for a full 60,416-key ring
-    # and a 928-query unit, read back from the workspace size (one bf16
-    # partial O and one fp32 log-sum-exp per split): 5 heads (one 8-way
-    # Ulysses rank) take 240 items, one dispatch round, and 10 heads 320;
-    # 40 heads take 9 or 10 splits (ring not wrapped or wrapped).
-    n_q, hd = 928, 128
-    c = _cache(H=H, hd=hd, cap=60416, ln=60416, head=head)
+def _model_pieces(H, per_head, lanes, groups):
+    """Pieces per lane of one launch, from the definition: the window
+    sequence (head-major, then session) is cut into `groups` ranges
+    [g*T//G, (g+1)*T//G); a lane's pieces are its windows cut at every range
+    start inside it and at the start of each non-empty segment after the first.
+    lanes: per session (lane0, [n0, n1, n2])."""
+    T = H * per_head
+    starts = {g * T // groups for g in range(1, groups)}
+    out = []
+    for lane0, segs in lanes:
+        most = 1
+        for h in range(H):
+            first = h * per_head + lane0
+            W = sum(segs)
+            cuts = {c for c in starts if first < c < first + W}
+            if segs[0] > 0:
+                cuts.add(first + segs[0])
+            if segs[1] > 0:
+                cuts.add(first + segs[0] + segs[1])
+            cuts = {c for c in cuts if first < c < first + W}
+            most = max(most, len(cuts) + 1)
+        out.append(most)
+    return out
+
+
+@pytest.mark.parametrize("H,head", [(5, 59472), (10, 59472), (40, 59472), (40, 0), (12, 8304)])
+def test_group_planner_pieces(H, head):
+    # A full 60,416-key ring and a 928-query unit (4 query blocks): 8 XCDs x
+    # 8 groups of 4 work-groups.  The partial slots the workspace holds (one
+    # bf16 piece of O and one fp32 log-sum-exp each) equal the most pieces any
+    # lane is cut into, by an independent model of the partition.
+    n_q, hd, cap = 928, 128, 60416
+    c = _cache(H=H, hd=hd, cap=cap, ln=cap, head=head)
     rc, nbytes = _ws([_step(c, 920, 8)])
     assert rc == 0
     staged = 2 * H * n_q * hd * 2 + n_q * H * hd * 2      # unit K, V (npad = n_q) and O
-    per_split = n_q * H * (hd * 2 + 4)
-    assert (nbytes - staged) % per_split == 0
-    assert (nbytes - staged) // per_split == splits
+    per_piece = n_q * H * (hd * 2 + 4)
+    start = head % cap                                     # the valid range starts at head
+    seg0 = cap - start
+    n0 = (cap - (start & ~15) + 63) // 64
+    n1 = (start + 63) // 64 if start else 0
+    n2 = (n_q + 63) // 64
+    assert seg0 > 0
+    per_head = n0 + n1 + n2
+    groups = min(64, H * per_head // 8)
+    want = _model_pieces(H, per_head, [(0, [n0, n1, n2])], groups)[0]
+    got = (nbytes - staged) // per_piece if nbytes > staged else 1
+    assert (nbytes - staged) % per_piece == 0
+    assert got == (want if want > 1 else 0) or (want == 1 and nbytes == staged)
 
 
 def test_noalloc_rejects_units_beyond_the_static_scratch():
-    # The 640x368-class unit over a wrapped 256-unit (241,664-key) ring needs
-    # more scratch than FMD_NOALLOC_SCRATCH_BYTES: rejected with FMD_E_WORKSPACE
-    # before anything touches a device, cache state unchanged.  The same unit
-    # over a 64-unit ring fits (its workspace size is below the limit).
+    # Two sessions of the 640x368-class unit over wrapped 256-unit (241,664-key)
+    # rings need more scratch than FMD_NOALLOC_SCRATCH_BYTES: rejected with
+    # FMD_E_WORKSPACE before anything touches a device, cache state unchanged.
+    # One such session fits (its workspace size is below the limit).
     h = (ctypes.c_float * 4)(0.25, 0.25, 0.25, 0.25)
     hp = ctypes.cast(h, ctypes.POINTER(ctypes.c_float))
-    for units, ln, head, fits in ((256, 256, 100, False), (64, 63, 63, True)):
-        cap = units * 944
-        c = _Cache(FAKE, FAKE + 0x100000, 40, 128, cap, ln * 944, head * 944)
-        io = _UnitIO(ctypes.pointer(c), FAKE, FAKE, 944, FAKE, FAKE, FAKE, 928 * 5120,
-                     FAKE, 920, 8, hp)
-        arr = (_UnitIO * 1)(io)
+    cap = 256 * 944
+    for n, fits in ((2, False), (1, True)):
+        cs = [_Cache(FAKE + i * 0x1000000, FAKE + 0x100000 + i * 0x1000000, 40, 128, cap, cap,
+                     100 * 944) for i in range(n)]
+        ios = [_UnitIO(ctypes.pointer(c), FAKE, FAKE, 944, FAKE, FAKE, FAKE, 928 * 5120,
+                       FAKE + 0x40000000 + i * 0x2000000, 920, 8, hp) for i, c in enumerate(cs)]
+        arr = (_UnitIO * n)(*ios)
         need = ctypes.c_size_t(0)
-        assert fmd._unit_workspace_bytes(arr, 1, ctypes.byref(need)) == 0
+        assert fmd._unit_workspace_bytes(arr, n, ctypes.byref(need)) == 0
         assert (need.value <= fmd.FMD_NOALLOC_SCRATCH_BYTES) == fits, need.value
         if not fits:
-            assert fmd._denoise_unit_noalloc(arr, 1, 4, FAKE, None) == -5
+            assert fmd._denoise_unit_noalloc(arr, n, 4, FAKE, None) == -5
             assert b"static scratch" in fmd._last_error()
-            assert (c.len_tokens, c.head_tokens) == (ln * 944, head * 944)
+            assert all((c.len_tokens, c.head_tokens) == (cap, 100 * 944) for c in cs)
         # Validation comes first, as for fmd_denoise_unit.
-        assert fmd._denoise_unit_noalloc(arr, 1, 0, FAKE, None) == -1
+        assert fmd._denoise_unit_noalloc(arr, n, 0, FAKE, None) == -1

@@ -115,5 +115,5 @@ def test_weight_shapes_checked_before_any_pointer():
 
 
 def test_forced_split_entry_rejects_negative():
-    assert fmd._test_force_attn_splits(-1) == -1
-    assert fmd._test_force_attn_splits(0) == 0
+    assert fmd._test_force_attn_groups(-1) == -1
+    assert fmd._test_force_attn_groups(0) == 0

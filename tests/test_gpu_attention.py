@@ -29,7 +29,7 @@ def _attn_case(H, hd, cap, length, head, n_q, seed=0, poison=True, split=None, n
     shape = workload.custom_session(H, hd, n_q - n_audio, n_audio, 0, cap, length, head, (1.0,))
     cache = make_cache(fmd, shape, rk, rv)
     unit = fmd.UnitStep(cache, dev_bf16(q), dev_bf16(ku), dev_bf16(vu), n_audio=n_audio)
-    with fmd.forced_attn_splits(split):
+    with fmd.forced_attn_groups(split):
         o = fmd.attention([unit])
         torch.cuda.synchronize()
     ref = oracle.attention(q, rk, rv, length, head, ku, vu)
@@ -164,7 +164,7 @@ def test_rising_scores_move_the_running_maximum(hd, length, split):
     ku, vu = random_bits(rng, (n_q, H, hd)), random_bits(rng, (n_q, H, hd))
     shape = workload.custom_session(H, hd, n_q, 0, 0, cap, length, head, (1.0,))
     cache = make_cache(fmd, shape, rk, rv)
-    with fmd.forced_attn_splits(split):
+    with fmd.forced_attn_groups(split):
         got = host_f64(fmd.attention([fmd.UnitStep(cache, dev_bf16(q), dev_bf16(ku), dev_bf16(vu))]))
     ref = oracle.attention(q, rk, rv, length, head, ku, vu)
     # The newest keys dominate: O is far from the plain mean of the values.

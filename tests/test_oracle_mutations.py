@@ -36,8 +36,8 @@ def test_wrong_valid_slots_is_caught(monkeypatch):
 def test_dropped_unit_keys_is_caught(monkeypatch):
     orig = att_mod._gather_head
 
-    def ring_only(ring_k, ring_v, length, head, k_u, v_u, h):
-        K, V = orig(ring_k, ring_v, length, head, k_u, v_u, h)
+    def ring_only(ring_k, ring_v, length, head, k_u, v_u, h, *rest):
+        K, V = orig(ring_k, ring_v, length, head, k_u, v_u, h, *rest)
         n = k_u.shape[0]
         return K[:-n], V[:-n]
     monkeypatch.setattr(att_mod, "_gather_head", ring_only)

@@ -49,9 +49,9 @@ def _compare(name, wl):
 
 
 def test_noalloc_two_calls_second_smaller():
-    # First the 640x368-class unit (about 115 MB of scratch, near the static
-    # array's 128 MiB), then three small ragged sessions reusing the same
-    # scratch with the first call's contents left in it.
+    # First the 640x368-class unit (about 67 MB of scratch), then three small
+    # ragged sessions reusing the same scratch with the first call's contents
+    # left in it.
     big = workload.get("v02_unit")
     small = workload.custom_workload("noalloc_small", 31, [
         workload.custom_session(4, 128, 60, 4, 48, 480, 480, 96, (0.4, 0.3, 0.2, 0.1)),
@@ -62,17 +62,21 @@ def test_noalloc_two_calls_second_smaller():
 
 
 def test_noalloc_rejects_a_unit_beyond_the_scratch_untouched():
-    # The wrapped 242k-key ring of the 640x368-class shape needs more scratch
-    # than the static array: FMD_E_WORKSPACE, no kernel, ring state unchanged.
+    # Two sessions over wrapped 242k-key rings of the 640x368-class shape need
+    # more scratch than the static array: FMD_E_WORKSPACE, no kernel, ring
+    # states unchanged.
     H, hd, units = 40, 128, 256
     cap = units * 944
-    cache = fmd.KVCache(H, hd, cap, device=DEV, len_tokens=cap, head_tokens=100 * 944)
-    q = torch.zeros((928, H, hd), dtype=torch.bfloat16, device=DEV)
-    z = torch.zeros((928, H * hd), dtype=torch.float32, device=DEV)
-    ks = torch.zeros((944, H, hd), dtype=torch.bfloat16, device=DEV)
-    io = fmd.UnitIO(cache, ks, ks, q, q, q, z, [0.5, 0.5], n_audio=8)
+    ios, caches = [], []
+    w = torch.zeros((H * hd, H * hd), dtype=torch.bfloat16, device=DEV)
+    for _ in range(2):
+        cache = fmd.KVCache(H, hd, cap, device=DEV, len_tokens=cap, head_tokens=100 * 944)
+        q = torch.zeros((928, H, hd), dtype=torch.bfloat16, device=DEV)
+        z = torch.zeros((928, H * hd), dtype=torch.float32, device=DEV)
+        ks = torch.zeros((944, H, hd), dtype=torch.bfloat16, device=DEV)
+        ios.append(fmd.UnitIO(cache, ks, ks, q, q, q, z, [0.5, 0.5], n_audio=8))
+        caches.append(cache)
     with pytest.raises(fmd.FmdError) as e:
-        fmd.denoise_unit_noalloc([io], torch.zeros((H * hd, H * hd), dtype=torch.bfloat16,
-                                                   device=DEV))
+        fmd.denoise_unit_noalloc(ios, w)
     assert e.value.code == -5
-    assert (cache.len_tokens, cache.head_tokens) == (cap, 100 * 944)
+    assert all((c.len_tokens, c.head_tokens) == (cap, 100 * 944) for c in caches)
