@@ -376,7 +376,7 @@ int enqueue_steps(const fmd_unit_step* units, int n, const std::vector<SessPlan>
       // A session without transpose work gets an empty range at the current end.
       va.s[k] = VtSess{static_cast<const bf16*>(u.k_u), static_cast<const bf16*>(u.v_u), kt, vt,
                        p.n_q, p.npad / 16, va.items, 0};
-      if (!second) va.items += H * (p.npad / 16);
+      if (!second) va.items += H * ((p.npad / 16 + kVtBlocks - 1) / kVtBlocks);
 
       AttnSess& as = aa.s[k];
       as.q = static_cast<const bf16*>(u.q);
@@ -406,7 +406,7 @@ int enqueue_steps(const fmd_unit_step* units, int n, const std::vector<SessPlan>
       ca.s[k] = CombineSess{as.opart, as.lse, o,         p.n_q,       p.nwin_total,
                             p.lane0,  p.nwin[0], p.nwin[1], ca.items};
       if (p.npart > 0) {
-        ca.items += p.n_q * H;
+        ca.items += H * ((p.n_q + kCombineRowsPerBlock - 1) / kCombineRowsPerBlock);
         any_split = true;
       }
 

@@ -316,7 +316,6 @@ void attn_kernel(AttnArgs a) {
     const int j32 = lane & 31, g = lane >> 5;
     const int row0 = qblk * kAttnBlockM + wave * kAttnRowsPerWave;
     const bool active = __builtin_amdgcn_readfirstlane(row0 < s.n_q ? 1 : 0) != 0;   // wave-uniform
-    const int qrow = row0 + j32;
 
     // Loop-invariant lane offsets (bytes) of the window loads.
     int koff[T::K_PER_WAVE], voff[T::V_PER_WAVE];
@@ -611,66 +610,76 @@ void attn_kernel(AttnArgs a) {
 
 // Merge the pieces of the lanes cut into several: O = sum_j w_j o_j /
 // sum_j w_j, w_j = 2^(lse_j - max) (o_j: bf16 pieces, each normalised by its
-// own row sum).  A lane lying in one group was written whole by the attention
-// kernel and is skipped.  One thread per (row, head, 8 features).
+// own row sum).  A lane lying in one piece was written whole by the attention
+// kernel and is skipped.  One block per (session, head, 64-row chunk): the
+// lane's piece count is computed once per block; one thread per (row, 8
+// features), the loads of all pieces of a row in flight together.
 template <int HD>
 __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
-  constexpr int TPR = HD / 8;              // threads per (row, head)
-  constexpr int GPB = 256 / TPR;           // (row, head) groups per block
-  const int grp = blockIdx.x * GPB + threadIdx.x / TPR;
-  if (grp >= a.items) return;
+  constexpr int TPR = HD / 8;              // threads per row
+  constexpr int RPP = 256 / TPR;           // rows per pass
+  const int item = blockIdx.x;
   int si = 0;
 #pragma unroll
   for (int i = 1; i < kMaxSessPerLaunch; ++i)
-    if (i < a.n_sess && grp >= a.s[i].item0) si = i;
+    if (i < a.n_sess && item >= a.s[i].item0) si = i;
   const CombineSess& s = a.s[si];
-  const int64_t rh = grp - s.item0;                 // row * H + head
-  const int h = (int)(rh % a.H);
+  const int chunks = (s.n_q + kCombineRowsPerBlock - 1) / kCombineRowsPerBlock;
+  const int local = item - s.item0;
+  const int h = local / chunks;
+  const int chunk = local - h * chunks;
   const int64_t lane_first = (int64_t)h * a.per_head + s.lane0;
   const int ns = piece_of(lane_first, lane_first + s.nwin_total - 1, s.n0, s.n1, a.total,
                           a.groups) + 1;
   if (ns == 1) return;
-  const int64_t stride = (int64_t)s.n_q * a.H;      // between pieces
+  const int64_t stride = (int64_t)s.n_q * a.H;      // (row, head) pairs between pieces
   const int e0 = (threadIdx.x % TPR) * 8;
-  const float* lse = s.lse + rh;
-  const bf16* part = s.opart + rh * HD + e0;
-  // One pass in batches of 8 pieces, every load of a batch issued before any
-  // is used; the running maximum rescales what is accumulated so far.
-  constexpr int B = 8;
-  float m = kNegInf, wsum = 0.f;
-  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  for (int k0 = 0; k0 < ns; k0 += B) {
-    float l[B];
-    bf16x8 x[B];
+  const int r_end = min(s.n_q, (chunk + 1) * kCombineRowsPerBlock);
+#pragma unroll 1
+  for (int r0 = chunk * kCombineRowsPerBlock; r0 < r_end; r0 += RPP) {
+    const int row = r0 + threadIdx.x / TPR;
+    if (row >= s.n_q) break;
+    const int64_t rh = (int64_t)row * a.H + h;
+    const float* lse = s.lse + rh;
+    const bf16* part = s.opart + rh * HD + e0;
+    // One pass in batches of 4 pieces, every load of a batch issued before
+    // any is used; the running maximum rescales what is accumulated so far.
+    constexpr int B = 4;
+    float m = kNegInf, wsum = 0.f;
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int k0 = 0; k0 < ns; k0 += B) {
+      float l[B];
+      bf16x8 x[B];
 #pragma unroll
-    for (int u = 0; u < B; ++u) {
-      const bool in = k0 + u < ns;
-      l[u] = in ? lse[(k0 + u) * stride] : kNegInf;
-      x[u] = in ? *reinterpret_cast<const bf16x8*>(part + (k0 + u) * stride * HD) : bf16x8{};
+      for (int u = 0; u < B; ++u) {
+        const bool in = k0 + u < ns;
+        l[u] = in ? lse[(k0 + u) * stride] : kNegInf;
+        x[u] = in ? *reinterpret_cast<const bf16x8*>(part + (k0 + u) * stride * HD) : bf16x8{};
+      }
+      float bm = l[0];
+#pragma unroll
+      for (int u = 1; u < B; ++u) bm = fmaxf(bm, l[u]);
+      const float m_new = fmaxf(m, bm);
+      if (m_new == kNegInf) continue;          // no key so far
+      const float c = __builtin_amdgcn_exp2f(m - m_new);   // 0 while m is -inf
+      wsum *= c;
+#pragma unroll
+      for (int t = 0; t < 8; ++t) acc[t] *= c;
+#pragma unroll
+      for (int u = 0; u < B; ++u) {
+        const float w = __builtin_amdgcn_exp2f(l[u] - m_new);
+        wsum += w;
+#pragma unroll
+        for (int t = 0; t < 8; ++t) acc[t] += w * (float)x[u][t];
+      }
+      m = m_new;
     }
-    float bm = l[0];
+    const float inv = wsum > 0.f ? 1.0f / wsum : 0.f;
+    bf16x8 out;
 #pragma unroll
-    for (int u = 1; u < B; ++u) bm = fmaxf(bm, l[u]);
-    const float m_new = fmaxf(m, bm);
-    if (m_new == kNegInf) continue;          // no key so far
-    const float c = __builtin_amdgcn_exp2f(m - m_new);   // 0 while m is -inf
-    wsum *= c;
-#pragma unroll
-    for (int t = 0; t < 8; ++t) acc[t] *= c;
-#pragma unroll
-    for (int u = 0; u < B; ++u) {
-      const float w = __builtin_amdgcn_exp2f(l[u] - m_new);
-      wsum += w;
-#pragma unroll
-      for (int t = 0; t < 8; ++t) acc[t] += w * (float)x[u][t];
-    }
-    m = m_new;
+    for (int t = 0; t < 8; ++t) out[t] = (bf16)(acc[t] * inv);
+    *reinterpret_cast<bf16x8*>(s.o + rh * HD + e0) = out;
   }
-  const float inv = wsum > 0.f ? 1.0f / wsum : 0.f;
-  bf16x8 out;
-#pragma unroll
-  for (int t = 0; t < 8; ++t) out[t] = (bf16)(acc[t] * inv);
-  *reinterpret_cast<bf16x8*>(s.o + rh * HD + e0) = out;
 }
 
 }  // namespace
@@ -701,12 +710,10 @@ hipError_t launch_attn(const AttnArgs& a, int head_dim, hipStream_t st) {
 
 hipError_t launch_combine(const CombineArgs& a, int head_dim, hipStream_t st) {
   if (a.items <= 0) return hipSuccess;
-  const int gpb = 256 / (head_dim / 8);
-  const int blocks = (a.items + gpb - 1) / gpb;
   if (head_dim == 128)
-    hipLaunchKernelGGL(combine_kernel<128>, dim3(blocks), dim3(256), 0, st, a);
+    hipLaunchKernelGGL(combine_kernel<128>, dim3(a.items), dim3(256), 0, st, a);
   else
-    hipLaunchKernelGGL(combine_kernel<64>, dim3(blocks), dim3(256), 0, st, a);
+    hipLaunchKernelGGL(combine_kernel<64>, dim3(a.items), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 

@@ -133,6 +133,8 @@ struct AppendArgs {
   int32_t items;
 };
 
+constexpr int kVtBlocks = 4;   // 16-token blocks per work-group of the unit K/V staging
+
 struct VtSess {
   const bf16* k;    // [n][H][hd]   the unit's keys
   const bf16* v;    // [n][H][hd]   the unit's values
@@ -140,7 +142,7 @@ struct VtSess {
   bf16* vt;         // [H][npad/16][hd][16]   values, 16-key blocks, zero past n
   int32_t n;
   int32_t nblk;     // npad/16
-  int32_t item0;
+  int32_t item0;    // first work-group: H * ceil(nblk / kVtBlocks) per session
   int32_t pad_;
 };
 struct VtArgs {
@@ -212,6 +214,8 @@ __host__ __device__ inline int piece_of(int64_t first, int64_t x, int n0, int n1
   return k;
 }
 
+constexpr int kCombineRowsPerBlock = 64;   // rows of one lane per combine block
+
 struct CombineSess {
   const bf16* opart;
   const float* lse;
@@ -220,7 +224,7 @@ struct CombineSess {
   int32_t nwin_total;
   int32_t lane0;
   int32_t n0, n1;     // windows of the ring segments (the lane's cuts)
-  int32_t item0;      // first (row, head) group handled by this session
+  int32_t item0;      // first block of this session: H * ceil(n_q / 64) blocks
 };
 struct CombineArgs {
   CombineSess s[kMaxSessPerLaunch];
@@ -229,7 +233,7 @@ struct CombineArgs {
   int32_t per_head;
   int32_t groups;
   int64_t total;
-  int32_t items;
+  int32_t items;      // blocks
 };
 
 // Projection GEMM  Y = A * W^T  (A [n_q][d] bf16, W [n_out][d] bf16 =

@@ -82,11 +82,16 @@ __global__ __launch_bounds__(2 * HD) void append_kernel(AppendArgs a) {
 // attention kernel streams every key segment the same way:
 //   keys   [n][H][hd] -> [H][npad][hd]
 //   values [n][H][hd] -> [H][npad/16][hd][16]
-// (npad = n rounded up to 16; rows past n are zero).
+// (npad = n rounded up to 16; rows past n are zero).  One work-group per
+// (session, head, kVtBlocks 16-token blocks); every load of a thread is
+// issued before its first store.
 template <int HD>
-__global__ __launch_bounds__(2 * HD) void vt_kernel(VtArgs a) {
-  constexpr int PARTS = HD / 8;
-  __shared__ __attribute__((aligned(16))) bf16 tile[16][HD + 8];
+__global__ __launch_bounds__(256) void vt_kernel(VtArgs a) {
+  constexpr int PARTS = HD / 8;            // 16-byte parts of one token row
+  constexpr int ROWS = 256 / PARTS;        // token rows per pass
+  constexpr int TOK = kVtBlocks * 16;      // tokens per work-group
+  constexpr int PASSES = TOK / ROWS;
+  __shared__ __attribute__((aligned(16))) bf16 tile[TOK][HD + 8];
 
   const int item = blockIdx.x;
   int si = 0;
@@ -95,29 +100,38 @@ __global__ __launch_bounds__(2 * HD) void vt_kernel(VtArgs a) {
     if (i < a.n_sess && item >= a.s[i].item0) si = i;
   const VtSess& s = a.s[si];
   const int local = item - s.item0;
-  const int h = local / s.nblk;
-  const int b = local % s.nblk;
+  const int nchunk = (s.nblk + kVtBlocks - 1) / kVtBlocks;
+  const int h = local / nchunk;
+  const int blk0 = (local - h * nchunk) * kVtBlocks;
+  const int nb = min(kVtBlocks, s.nblk - blk0);
   const int H = a.H;
-  {
-    const int r = threadIdx.x / PARTS;
-    const int part = threadIdx.x % PARTS;
-    const int tok = b * 16 + r;
-    u32x4 v = {0u, 0u, 0u, 0u}, k = {0u, 0u, 0u, 0u};
+  const int part = threadIdx.x % PARTS;
+  u32x4 kx[PASSES], vx[PASSES];
+#pragma unroll
+  for (int p = 0; p < PASSES; ++p) {
+    const int tok = blk0 * 16 + p * ROWS + threadIdx.x / PARTS;
+    kx[p] = vx[p] = u32x4{0u, 0u, 0u, 0u};
     if (tok < s.n) {
-      v = ld16(s.v + ((int64_t)tok * H + h) * HD + part * 8);
-      k = ld16(s.k + ((int64_t)tok * H + h) * HD + part * 8);
+      kx[p] = ld16(s.k + ((int64_t)tok * H + h) * HD + part * 8);
+      vx[p] = ld16(s.v + ((int64_t)tok * H + h) * HD + part * 8);
     }
-    st16(s.kt + ((int64_t)h * s.nblk * 16 + tok) * HD + part * 8, k);
-    st16(&tile[r][part * 8], v);
+  }
+#pragma unroll
+  for (int p = 0; p < PASSES; ++p) {
+    const int r = p * ROWS + threadIdx.x / PARTS;
+    if (r < nb * 16) {
+      st16(s.kt + ((int64_t)h * s.nblk * 16 + blk0 * 16 + r) * HD + part * 8, kx[p]);
+      st16(&tile[r][part * 8], vx[p]);
+    }
   }
   __syncthreads();
-  {
-    const int e = threadIdx.x >> 1;
-    const int hh = threadIdx.x & 1;
+  // Values: 16-byte chunks (8 keys of one feature) of the nb blocks.
+  for (int idx = threadIdx.x; idx < nb * HD * 2; idx += 256) {
+    const int b = idx / (HD * 2), e = (idx >> 1) % HD, hh = idx & 1;
     union { u32x4 v; bf16 b[8]; } u;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) u.b[i] = tile[hh * 8 + i][e];
-    st16(s.vt + (((int64_t)h * s.nblk + b) * HD + e) * 16 + hh * 8, u.v);
+    for (int i = 0; i < 8; ++i) u.b[i] = tile[b * 16 + hh * 8 + i][e];
+    st16(s.vt + (((int64_t)h * s.nblk + blk0 + b) * HD + e) * 16 + hh * 8, u.v);
   }
 }
 
@@ -135,7 +149,7 @@ hipError_t launch_vt(const VtArgs& a, int head_dim, hipStream_t st) {
   if (head_dim == 128)
     hipLaunchKernelGGL(vt_kernel<128>, dim3(a.items), dim3(256), 0, st, a);
   else
-    hipLaunchKernelGGL(vt_kernel<64>, dim3(a.items), dim3(128), 0, st, a);
+    hipLaunchKernelGGL(vt_kernel<64>, dim3(a.items), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
