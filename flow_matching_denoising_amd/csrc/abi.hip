@@ -333,10 +333,14 @@ int check_workspace(void* ws, size_t have, size_t need) {
 // one) and one projection updates z.
 // proj_mode: kProjEuler, or kProjLayer / kProjLayerLast for a layer of a
 // stack, with r_out (one fp32 residual per projected unit).
+// kv_staged: the unit keys and values already sit in each session's (each
+// pair's first branch's) kt/vt workspace slots, written there by the Q/K/V
+// projection; no staging launch.
 int enqueue_steps(const fmd_unit_step* units, int n, const std::vector<SessPlan>& plans,
                   const void* w_o, char* ws, bf16* o_out, hipStream_t st,
                   bf16* const* zb_out = nullptr, const float* guidance = nullptr,
-                  int proj_mode = kProjEuler, float* const* r_out = nullptr) {
+                  int proj_mode = kProjEuler, float* const* r_out = nullptr,
+                  bool kv_staged = false) {
   const int H = units[0].cache->n_heads, hd = units[0].cache->head_dim;
   const int d = H * hd;
   const float scale_log2 = (float)(1.4426950408889634 / sqrt((double)hd));
@@ -376,7 +380,7 @@ int enqueue_steps(const fmd_unit_step* units, int n, const std::vector<SessPlan>
       // A session without transpose work gets an empty range at the current end.
       va.s[k] = VtSess{static_cast<const bf16*>(u.k_u), static_cast<const bf16*>(u.v_u), kt, vt,
                        p.n_q, p.npad / 16, va.items, 0};
-      if (!second) va.items += H * ((p.npad / 16 + kVtBlocks - 1) / kVtBlocks);
+      if (!second && !kv_staged) va.items += H * ((p.npad / 16 + kVtBlocks - 1) / kVtBlocks);
 
       AttnSess& as = aa.s[k];
       as.q = static_cast<const bf16*>(u.q);
@@ -421,14 +425,16 @@ int enqueue_steps(const fmd_unit_step* units, int n, const std::vector<SessPlan>
       const int mtiles = (p.n_q + kProjTile - 1) / kProjTile;
       const int ntiles = (d + kProjTileN - 1) / kProjTileN;
       pa.s[j] = ProjSess{o, u.z, zb_out ? zb_out[unit] : nullptr, r_out ? r_out[unit] : nullptr,
-                         {nullptr, nullptr, nullptr}, p.n_q, mtiles, pa.items, u.h};
+                         p.n_q, mtiles, pa.items, u.h};
       pa.items += mtiles * ntiles;
     }
     // Sessions whose lanes all lie in one group take no combine items; the
     // combine kernel finds its session by item0, so they get an empty range
     // at the current end.
     int rc;
-    if ((rc = timed_launch(FMD_KERNEL_VT, st, [&] { return launch_vt(va, hd, st); }))) return rc;
+    if (va.items > 0 &&
+        (rc = timed_launch(FMD_KERNEL_VT, st, [&] { return launch_vt(va, hd, st); })))
+      return rc;
     if ((rc = timed_launch(FMD_KERNEL_ATTN, st, [&] { return launch_attn(aa, hd, st); })))
       return rc;
     if (any_split &&
@@ -782,15 +788,17 @@ struct SolverUnit {
   float g;
 };
 
-// Workspace: per unit bf16 z (the Q/K/V projection's input), Q, K_u, V_u
-// ([n_q][d] bf16 each) and, for a layer stack, the fp32 residual; then the
-// step workspace of fmd_denoise_step, sized for the largest layer (the layers
-// of a step run one after another and reuse it).
+// Workspace: per unit bf16 z (the Q/K/V projection's input) and Q ([n_q][d]
+// bf16 each) and, for a layer stack, the fp32 residual; then the step
+// workspace of fmd_denoise_step, sized for the largest layer (the layers of a
+// step run one after another and reuse it).  The projection writes K_u and V_u
+// straight into the step workspace's unit key/value slots (of the unit's
+// first attention session).
 struct SolverLayout {
   std::vector<std::vector<fmd_kv_cache>> after;   // per layer: per attention session
   std::vector<std::vector<fmd_unit_step>> steps;  // per layer
   std::vector<std::vector<SessPlan>> plans;       // per layer
-  std::vector<size_t> off;                        // per unit: zb, q, k, v, [r]
+  std::vector<size_t> off;                        // per unit: zb, q, [r]
   size_t slab_total = 0, bytes = 0;
 };
 
@@ -808,7 +816,7 @@ static void layout_solver(const std::vector<SolverUnit>& us, int nb, int n_layer
   for (int i = 0; i < n; ++i) {
     const int n_q = us[i].n_video + us[i].n_audio;
     L.off[i] = off;
-    off += 4 * unit_slab(n_q, d);
+    off += 2 * unit_slab(n_q, d);
     if (n_layers > 1) off += 2 * unit_slab(n_q, d);   // fp32 residual
   }
   L.slab_total = off;
@@ -846,15 +854,13 @@ static int run_solver(const std::vector<SolverUnit>& us, int nb, int n_layers, i
   const int n = (int)us.size();
   const int H = us[0].cache[0]->n_heads, hd = us[0].cache[0]->head_dim;
   const int d = H * hd;
-  std::vector<bf16*> zb(n), q(n), k(n), v(n);
+  std::vector<bf16*> zb(n), q(n);
   std::vector<float*> r(n, nullptr);
   for (int i = 0; i < n; ++i) {
     const size_t slab = unit_slab(us[i].n_video + us[i].n_audio, d);
     zb[i] = reinterpret_cast<bf16*>(ws + L.off[i]);
     q[i] = reinterpret_cast<bf16*>(ws + L.off[i] + slab);
-    k[i] = reinterpret_cast<bf16*>(ws + L.off[i] + 2 * slab);
-    v[i] = reinterpret_cast<bf16*>(ws + L.off[i] + 3 * slab);
-    if (n_layers > 1) r[i] = reinterpret_cast<float*>(ws + L.off[i] + 4 * slab);
+    if (n_layers > 1) r[i] = reinterpret_cast<float*>(ws + L.off[i] + 2 * slab);
   }
   int rc;
   for (int c0 = 0; c0 < n; c0 += kMaxSessPerLaunch) {
@@ -877,18 +883,20 @@ static int run_solver(const std::vector<SolverUnit>& us, int nb, int n_layers, i
     for (int l = 0; l < n_layers; ++l) {
       for (int c0 = 0; c0 < n; c0 += kMaxSessPerLaunch) {
         const int cn = std::min(kMaxSessPerLaunch, n - c0);
-        ProjArgs pa = {};
+        QkvArgs pa = {};
         pa.n_sess = cn;
         pa.d = d;
-        pa.n_out = 3 * d;
+        pa.hd = hd;
         pa.w = static_cast<const bf16*>(w_qkv[l]);
         const int ntiles = (3 * d + kQkvTile - 1) / kQkvTile;
         for (int j = 0; j < cn; ++j) {
           const int i = c0 + j;
           const int n_q = us[i].n_video + us[i].n_audio;
           const int mtiles = (n_q + kQkvTile - 1) / kQkvTile;
-          pa.s[j] = ProjSess{zb[i], nullptr, nullptr, nullptr, {q[i], k[i], v[i]}, n_q, mtiles,
-                             pa.items, 0.f};
+          const SessPlan& p = L.plans[l][(size_t)i * nb];
+          pa.s[j] = QkvSess{zb[i], q[i], reinterpret_cast<bf16*>(step_ws + p.off_kt),
+                            reinterpret_cast<bf16*>(step_ws + p.off_vt), n_q, p.npad, mtiles,
+                            pa.items};
           pa.items += mtiles * ntiles;
         }
         if ((rc = timed_launch(FMD_KERNEL_QKV, st, [&] { return launch_qkv_wide(pa, st); })))
@@ -900,8 +908,8 @@ static int run_solver(const std::vector<SolverUnit>& us, int nb, int n_layers, i
           fmd_unit_step& u = steps[(size_t)i * nb + b];
           u.cache = us[i].cache[n_layers > 1 ? l : b];   // now in its post-append state
           u.q = q[i];
-          u.k_u = k[i];
-          u.v_u = v[i];
+          u.k_u = nullptr;   // staged by the projection
+          u.v_u = nullptr;
           u.z = us[i].z;
           u.h = us[i].h[s];
         }
@@ -912,7 +920,7 @@ static int run_solver(const std::vector<SolverUnit>& us, int nb, int n_layers, i
       const bool need_zb = !(last_layer && s + 1 == n_steps);
       if ((rc = enqueue_steps(steps.data(), n * nb, L.plans[l], w_o[l], step_ws, nullptr, st,
                               need_zb ? zb.data() : nullptr, nb == 2 ? g.data() : nullptr, mode,
-                              n_layers > 1 ? r.data() : nullptr)))
+                              n_layers > 1 ? r.data() : nullptr, true)))
         return rc;
     }
   }

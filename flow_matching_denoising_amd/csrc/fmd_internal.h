@@ -237,27 +237,22 @@ struct CombineArgs {
 };
 
 // Projection GEMM  Y = A * W^T  (A [n_q][d] bf16, W [n_out][d] bf16 =
-// [d_out][d_in], fp32 accumulation), with one of two epilogues:
-//   kProjEuler: n_out = d; z <- z - h * Y (fp32, in place), and, if zb is set,
+// [d_out][d_in], fp32 accumulation, n_out = d), with one of three epilogues:
+//   kProjEuler: z <- z - h * Y (fp32, in place), and, if zb is set,
 //               zb <- bf16(z) (the next step's projection input);
-//   kProjQkv:   n_out = 3d; column c of Y goes to out[c / d], column c % d,
-//               rounded to bf16 (the unit's Q, K_u, V_u; launch_qkv_wide);
-//   kProjLayer: n_out = d; a layer of a stack adds its update to the fp32
-//               residual r <- r + Y and writes zb <- bf16(z + r), the next
-//               layer's input;
+//   kProjLayer: a layer of a stack adds its update to the fp32 residual
+//               r <- r + Y and writes zb <- bf16(z + r), the next layer's input;
 //   kProjLayerLast: the stack's last layer: z <- z - h * (r + Y), r <- 0,
 //               and, if zb is set, zb <- bf16(z).
 constexpr int kProjEuler = 0;
-constexpr int kProjQkv = 1;
 constexpr int kProjLayer = 2;
 constexpr int kProjLayerLast = 3;
 
 struct ProjSess {
   const bf16* a;      // [n_q][d]
-  float* z;           // kProjEuler, kProjLayer*: [n_q][d]
-  bf16* zb;           // kProjEuler, kProjLayer*: [n_q][d] or nullptr
+  float* z;           // [n_q][d]
+  bf16* zb;           // [n_q][d] or nullptr
   float* r;           // kProjLayer*: [n_q][d] residual
-  bf16* out[3];       // kProjQkv: Q, K_u, V_u, each [n_q][d]
   int32_t n_q;
   int32_t n_mtiles;
   int32_t item0;
@@ -269,6 +264,29 @@ struct ProjArgs {
   int32_t n_sess;
   int32_t d;
   int32_t n_out;
+  int32_t items;
+};
+
+// Q/K/V projection of the latent: [Q | K_u | V_u] = bf16(zb * W_qkv^T)
+// (W_qkv [3d][d]), each output written in the layout the attention reads:
+// Q [n_q][H][hd], K_u [H][npad][hd], V_u [H][npad/16][hd][16] (rows n_q..npad-1
+// of K_u and V_u zero).  256 x 256 tiles; n_mtiles counts 256-row tiles.
+struct QkvSess {
+  const bf16* zb;     // [n_q][d]
+  bf16* q;
+  bf16* kt;
+  bf16* vt;
+  int32_t n_q;
+  int32_t npad;       // n_q rounded up to 16
+  int32_t n_mtiles;
+  int32_t item0;
+};
+struct QkvArgs {
+  QkvSess s[kMaxSessPerLaunch];
+  const bf16* w;      // [3d][d]
+  int32_t n_sess;
+  int32_t d;
+  int32_t hd;
   int32_t items;
 };
 
@@ -309,9 +327,7 @@ hipError_t launch_combine(const CombineArgs& a, int head_dim, hipStream_t st);
 hipError_t launch_proj(const ProjArgs& a, int mode, hipStream_t st);
 hipError_t launch_cvt(const CvtArgs& a, hipStream_t st);
 hipError_t launch_mix(const MixArgs& a, hipStream_t st);
-// Q/K/V projection (kProjQkv semantics) with 256 x 256 tiles; ProjSess.n_mtiles
-// counts 256-row tiles.
-hipError_t launch_qkv_wide(const ProjArgs& a, hipStream_t st);
+hipError_t launch_qkv_wide(const QkvArgs& a, hipStream_t st);
 
 // Attention tiling shared by host planning and the kernel.
 constexpr int kAttnWaves = 8;

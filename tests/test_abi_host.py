@@ -215,8 +215,9 @@ def test_unit_qkv_workspace_holds_projections_and_step():
     out = ctypes.c_size_t(0)
     assert fmd._unit_qkv_workspace_bytes((_UnitQkvIO * 1)(io), 1, ctypes.byref(out)) == 0
     _, step = _ws([_step(c, 920, 8)])
-    # bf16 z, Q, K_u, V_u (4 x 928 x 5120 bf16) on top of the step workspace.
-    assert out.value >= step + 4 * 928 * 5120 * 2
+    # bf16 z and Q (2 x 928 x 5120 bf16) on top of the step workspace, whose
+    # unit key/value slots take K_u and V_u straight from the projection.
+    assert out.value == step + 2 * 928 * 5120 * 2
 
 
 def _cfg_io(cond, uncond, h, g=5.0, ct=32, ut=0, z=FAKE):
