@@ -108,7 +108,7 @@ _denoise_step = _sig("fmd_denoise_step", ctypes.c_int, ctypes.POINTER(_UnitStep)
 _attention = _sig("fmd_attention", ctypes.c_int, ctypes.POINTER(_UnitStep), _i32, _vp, _vp, _sz,
                   _vp)
 _unit_workspace_bytes = _sig("fmd_unit_workspace_bytes", ctypes.c_int, ctypes.POINTER(_UnitIO),
-                             _i32, ctypes.POINTER(_sz))
+                             _i32, _i32, ctypes.POINTER(_sz))
 _denoise_unit = _sig("fmd_denoise_unit", ctypes.c_int, ctypes.POINTER(_UnitIO), _i32, _i32, _vp,
                      _vp, _sz, _vp)
 _denoise_unit_noalloc = _sig("fmd_denoise_unit_noalloc", ctypes.c_int, ctypes.POINTER(_UnitIO),
@@ -407,7 +407,7 @@ def _io_array(sessions):
 def unit_workspace_bytes(sessions) -> int:
     arr, n = _io_array(sessions)
     out = _sz(0)
-    _check(_unit_workspace_bytes(arr, n, ctypes.byref(out)))
+    _check(_unit_workspace_bytes(arr, n, sessions[0].n_steps, ctypes.byref(out)))
     return out.value
 
 

@@ -181,7 +181,9 @@ struct SessPlan {
   int lane0, per_head, groups, qb;
   int64_t total;
   int npart;
-  size_t off_kt, off_vt, off_o, off_opart, off_lse;   // workspace offsets
+  int proj_splits;   // k-range parts of the launch's projection (1: none)
+  size_t off_kt, off_vt, off_o, off_opart, off_lse, off_part;   // workspace offsets
+  size_t kv_stride;  // bytes between copies of the staged unit keys/values
 };
 
 int nwin_of(int lo, int hi) {
@@ -265,14 +267,18 @@ void plan_groups(std::vector<SessPlan>& plans, int H) {
 }
 
 // Workspace layout, sessions in order.  With o_external, O goes to the
-// caller's buffer and takes no workspace.
-size_t layout_workspace(std::vector<SessPlan>& plans, int H, int hd, bool o_external) {
+// caller's buffer and takes no workspace.  kv_copies: copies of the staged
+// unit keys and values (one per solver step when a unit stages every step's
+// up front); copy c sits kv_stride * c bytes after the first.
+size_t layout_workspace(std::vector<SessPlan>& plans, int H, int hd, bool o_external,
+                        int kv_copies) {
   size_t off = 0;
   for (auto& p : plans) {
+    const size_t kvb = align256((size_t)H * p.npad * hd * 2);
     p.off_kt = off;
-    off = align256(off + (size_t)H * p.npad * hd * 2);
-    p.off_vt = off;
-    off = align256(off + (size_t)H * p.npad * hd * 2);
+    p.off_vt = off + kvb;
+    p.kv_stride = 2 * kvb;
+    off += (size_t)kv_copies * 2 * kvb;
     p.off_o = off;
     if (!o_external) off = align256(off + (size_t)p.n_q * H * hd * 2);
     p.off_opart = p.off_lse = off;
@@ -281,18 +287,38 @@ size_t layout_workspace(std::vector<SessPlan>& plans, int H, int hd, bool o_exte
       p.off_lse = off;
       off = align256(off + (size_t)p.npart * p.n_q * H * 4);
     }
+    p.off_part = off;
+    if (!o_external && p.proj_splits > 1)
+      off = align256(off + (size_t)p.proj_splits * p.n_q * H * hd * 4);
   }
   return off;
 }
 
+// The projection's k-range parts, per launch chunk (every session of a chunk
+// is counted as projected; a guided pair projects once, so this errs towards
+// fewer parts there).
+void plan_proj(std::vector<SessPlan>& plans, int d) {
+  const int n = (int)plans.size();
+  const int ntiles = (d + kProjTileN - 1) / kProjTileN;
+  for (int c0 = 0; c0 < n; c0 += kMaxSessPerLaunch) {
+    const int cn = std::min(kMaxSessPerLaunch, n - c0);
+    int64_t tiles = 0;
+    for (int k = 0; k < cn; ++k)
+      tiles += (int64_t)((plans[c0 + k].n_q + kProjTile - 1) / kProjTile) * ntiles;
+    const int splits = proj_splits(tiles, d / kProjBK);
+    for (int k = 0; k < cn; ++k) plans[c0 + k].proj_splits = splits;
+  }
+}
+
 int plan_steps(const fmd_unit_step* units, int n, bool o_external, std::vector<SessPlan>& plans,
-               size_t* bytes) {
+               size_t* bytes, int kv_copies = 1) {
   const int H = units[0].cache->n_heads, hd = units[0].cache->head_dim;
   plans.resize(n);
   for (int i = 0; i < n; ++i)
     plan_session(units[i].cache, units[i].n_video + units[i].n_audio, plans[i]);
   plan_groups(plans, H);
-  *bytes = layout_workspace(plans, H, hd, o_external);
+  plan_proj(plans, H * hd);
+  *bytes = layout_workspace(plans, H, hd, o_external, kv_copies);
   return FMD_OK;
 }
 
@@ -334,13 +360,14 @@ int check_workspace(void* ws, size_t have, size_t need) {
 // proj_mode: kProjEuler, or kProjLayer / kProjLayerLast for a layer of a
 // stack, with r_out (one fp32 residual per projected unit).
 // kv_staged: the unit keys and values already sit in each session's (each
-// pair's first branch's) kt/vt workspace slots, written there by the Q/K/V
-// projection; no staging launch.
+// pair's first branch's) kt/vt workspace slots, copy kv_copy (written there by
+// the Q/K/V projection, or by a unit's staging of every step up front); no
+// staging launch.
 int enqueue_steps(const fmd_unit_step* units, int n, const std::vector<SessPlan>& plans,
                   const void* w_o, char* ws, bf16* o_out, hipStream_t st,
                   bf16* const* zb_out = nullptr, const float* guidance = nullptr,
                   int proj_mode = kProjEuler, float* const* r_out = nullptr,
-                  bool kv_staged = false) {
+                  bool kv_staged = false, int kv_copy = 0) {
   const int H = units[0].cache->n_heads, hd = units[0].cache->head_dim;
   const int d = H * hd;
   const float scale_log2 = (float)(1.4426950408889634 / sqrt((double)hd));
@@ -361,6 +388,7 @@ int enqueue_steps(const fmd_unit_step* units, int n, const std::vector<SessPlan>
     pa.d = d;
     pa.n_out = d;
     pa.w = static_cast<const bf16*>(w_o);
+    pa.splits = plans[c0].proj_splits;
     bool any_split = false;
     bf16* o_prev = nullptr;
     for (int k = 0; k < cn; ++k) {
@@ -368,12 +396,9 @@ int enqueue_steps(const fmd_unit_step* units, int n, const std::vector<SessPlan>
       const SessPlan& p = plans[c0 + k];
       const fmd_kv_cache* c = u.cache;
       const bool second = guidance && (k & 1);
-      bf16* kt = reinterpret_cast<bf16*>(ws + p.off_kt);
-      bf16* vt = reinterpret_cast<bf16*>(ws + p.off_vt);
-      if (second) {   // the conditional branch's transposed unit keys/values
-        kt = reinterpret_cast<bf16*>(ws + plans[c0 + k - 1].off_kt);
-        vt = reinterpret_cast<bf16*>(ws + plans[c0 + k - 1].off_vt);
-      }
+      const SessPlan& pk = second ? plans[c0 + k - 1] : p;   // a pair shares the first's
+      bf16* kt = reinterpret_cast<bf16*>(ws + pk.off_kt + kv_copy * pk.kv_stride);
+      bf16* vt = reinterpret_cast<bf16*>(ws + pk.off_vt + kv_copy * pk.kv_stride);
       bf16* o = o_out ? o_out + o_row * d : reinterpret_cast<bf16*>(ws + p.off_o);
       o_row += p.n_q;
 
@@ -424,9 +449,11 @@ int enqueue_steps(const fmd_unit_step* units, int n, const std::vector<SessPlan>
       const int j = k / per_proj, unit = (c0 + k) / per_proj;
       const int mtiles = (p.n_q + kProjTile - 1) / kProjTile;
       const int ntiles = (d + kProjTileN - 1) / kProjTileN;
-      pa.s[j] = ProjSess{o, u.z, zb_out ? zb_out[unit] : nullptr, r_out ? r_out[unit] : nullptr,
-                         p.n_q, mtiles, pa.items, u.h};
-      pa.items += mtiles * ntiles;
+      pa.s[j] = ProjSess{o,        u.z,     zb_out ? zb_out[unit] : nullptr,
+                         r_out ? r_out[unit] : nullptr,
+                         reinterpret_cast<float*>(ws + p.off_part),
+                         p.n_q,    mtiles,  pa.items, u.h};
+      pa.items += mtiles * ntiles * pa.splits;
     }
     // Sessions whose lanes all lie in one group take no combine items; the
     // combine kernel finds its session by item0, so they get an empty range
@@ -443,8 +470,10 @@ int enqueue_steps(const fmd_unit_step* units, int n, const std::vector<SessPlan>
     if (guidance &&
         (rc = timed_launch(FMD_KERNEL_MIX, st, [&] { return launch_mix(ma, st); })))
       return rc;
-    if (!o_out &&
-        (rc = timed_launch(FMD_KERNEL_PROJ, st, [&] { return launch_proj(pa, proj_mode, st); })))
+    if (!o_out && (rc = timed_launch(FMD_KERNEL_PROJ, st, [&] {
+                     hipError_t e = launch_proj(pa, proj_mode, st);
+                     return e == hipSuccess ? launch_proj_reduce(pa, proj_mode, st) : e;
+                   })))
       return rc;
   }
   return FMD_OK;
@@ -686,20 +715,72 @@ static void post_append_steps(const fmd_unit_io* ss, int n, std::vector<fmd_kv_c
   }
 }
 
-int fmd_unit_workspace_bytes(const fmd_unit_io* sessions, int32_t n_sessions, size_t* out_bytes) {
+// Copies of the staged unit keys and values a unit needs: every step's are
+// staged up front, once when every session reuses one set for all steps.
+static int unit_kv_copies(const fmd_unit_io* ss, int n, int n_steps) {
+  for (int i = 0; i < n; ++i)
+    if (ss[i].step_stride_elems != 0) return n_steps;
+  return 1;
+}
+
+// Plan a validated unit: post-append ring states, the step plans and the
+// workspace bytes.
+static void plan_unit(const fmd_unit_io* sessions, int n_sessions, int n_steps,
+                      std::vector<fmd_kv_cache>& after, std::vector<fmd_unit_step>& steps,
+                      std::vector<SessPlan>& plans, size_t* need) {
+  post_append_steps(sessions, n_sessions, after, steps);
+  plan_steps(steps.data(), n_sessions, false, plans, need,
+             unit_kv_copies(sessions, n_sessions, n_steps));
+}
+
+int fmd_unit_workspace_bytes(const fmd_unit_io* sessions, int32_t n_sessions, int32_t n_steps,
+                             size_t* out_bytes) {
   g_last_error.clear();
   if (!out_bytes) return fail(FMD_E_INVAL, "out_bytes is NULL");
-  int rc = validate_unit_io(sessions, n_sessions, 1);
+  int rc = validate_unit_io(sessions, n_sessions, n_steps);
   if (rc) return rc;
   std::vector<fmd_kv_cache> after;
   std::vector<fmd_unit_step> steps;
-  post_append_steps(sessions, n_sessions, after, steps);
   std::vector<SessPlan> plans;
-  return plan_steps(steps.data(), n_sessions, false, plans, out_bytes);
+  plan_unit(sessions, n_sessions, n_steps, after, steps, plans, out_bytes);
+  return FMD_OK;
 }
 
-// One unit (validated, planned): the batched append, then the steps on the
-// given workspace.
+// One launch chunk at a time, the unit keys and values of every step of
+// every session into their staging copies (copy s for step s).
+static int enqueue_unit_staging(const fmd_unit_io* ss, int n, int n_steps,
+                                const std::vector<SessPlan>& plans, char* ws, hipStream_t st) {
+  const int H = ss[0].cache->n_heads, hd = ss[0].cache->head_dim;
+  const int copies = unit_kv_copies(ss, n, n_steps);
+  std::vector<VtSess> all;
+  for (int s = 0; s < copies; ++s)
+    for (int i = 0; i < n; ++i) {
+      const SessPlan& p = plans[i];
+      const int64_t off = (int64_t)s * ss[i].step_stride_elems;
+      all.push_back(VtSess{static_cast<const bf16*>(ss[i].k_u) + off,
+                           static_cast<const bf16*>(ss[i].v_u) + off,
+                           reinterpret_cast<bf16*>(ws + p.off_kt + s * p.kv_stride),
+                           reinterpret_cast<bf16*>(ws + p.off_vt + s * p.kv_stride), p.n_q,
+                           p.npad / 16, 0, 0});
+    }
+  for (size_t c0 = 0; c0 < all.size(); c0 += kMaxSessPerLaunch) {
+    const int cn = (int)std::min<size_t>(kMaxSessPerLaunch, all.size() - c0);
+    VtArgs va = {};
+    va.n_sess = cn;
+    va.H = H;
+    for (int k = 0; k < cn; ++k) {
+      va.s[k] = all[c0 + k];
+      va.s[k].item0 = va.items;
+      va.items += H * ((va.s[k].nblk + kVtBlocks - 1) / kVtBlocks);
+    }
+    int rc;
+    if ((rc = timed_launch(FMD_KERNEL_VT, st, [&] { return launch_vt(va, hd, st); }))) return rc;
+  }
+  return FMD_OK;
+}
+
+// One unit (validated, planned): the batched append, the staging of every
+// step's unit keys and values, then the steps on the given workspace.
 static int run_unit(fmd_unit_io* sessions, int n_sessions, int n_steps, const void* w_o,
                     std::vector<fmd_unit_step>& steps, const std::vector<SessPlan>& plans,
                     char* workspace, hipStream_t st) {
@@ -718,6 +799,8 @@ static int run_unit(fmd_unit_io* sessions, int n_sessions, int n_steps, const vo
   if (!caches.empty() &&
       (rc = enqueue_appends(caches.data(), ks.data(), vs.data(), ts.data(), (int)caches.size(), st)))
     return rc;
+  if ((rc = enqueue_unit_staging(sessions, n_sessions, n_steps, plans, workspace, st))) return rc;
+  const bool one_copy = unit_kv_copies(sessions, n_sessions, n_steps) == 1;
   for (int s = 0; s < n_steps; ++s) {
     for (int i = 0; i < n_sessions; ++i) {
       const int64_t off = (int64_t)s * sessions[i].step_stride_elems;
@@ -727,7 +810,8 @@ static int run_unit(fmd_unit_io* sessions, int n_sessions, int n_steps, const vo
       steps[i].v_u = static_cast<const bf16*>(sessions[i].v_u) + off;
       steps[i].h = sessions[i].h[s];
     }
-    if ((rc = enqueue_steps(steps.data(), n_sessions, plans, w_o, workspace, nullptr, st)))
+    if ((rc = enqueue_steps(steps.data(), n_sessions, plans, w_o, workspace, nullptr, st,
+                            nullptr, nullptr, kProjEuler, nullptr, true, one_copy ? 0 : s)))
       return rc;
   }
   return FMD_OK;
@@ -741,10 +825,9 @@ int fmd_denoise_unit(fmd_unit_io* sessions, int32_t n_sessions, int32_t n_steps,
   if ((rc = check_tensor(w_o, 0, "w_o"))) return rc;
   std::vector<fmd_kv_cache> after;
   std::vector<fmd_unit_step> steps;
-  post_append_steps(sessions, n_sessions, after, steps);
   std::vector<SessPlan> plans;
   size_t need = 0;
-  plan_steps(steps.data(), n_sessions, false, plans, &need);
+  plan_unit(sessions, n_sessions, n_steps, after, steps, plans, &need);
   if ((rc = check_workspace(workspace, workspace_bytes, need))) return rc;
   return run_unit(sessions, n_sessions, n_steps, w_o, steps, plans,
                   static_cast<char*>(workspace), static_cast<hipStream_t>(stream));
@@ -758,10 +841,9 @@ int fmd_denoise_unit_noalloc(fmd_unit_io* sessions, int32_t n_sessions, int32_t 
   if ((rc = check_tensor(w_o, 0, "w_o"))) return rc;
   std::vector<fmd_kv_cache> after;
   std::vector<fmd_unit_step> steps;
-  post_append_steps(sessions, n_sessions, after, steps);
   std::vector<SessPlan> plans;
   size_t need = 0;
-  plan_steps(steps.data(), n_sessions, false, plans, &need);
+  plan_unit(sessions, n_sessions, n_steps, after, steps, plans, &need);
   if (need > (size_t)FMD_NOALLOC_SCRATCH_BYTES)
     return fail(FMD_E_WORKSPACE,
                 "this unit needs %zu bytes of scratch; the static scratch holds %zu "

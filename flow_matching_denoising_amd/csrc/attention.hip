@@ -611,7 +611,7 @@ void attn_kernel(AttnArgs a) {
 // Merge the pieces of the lanes cut into several: O = sum_j w_j o_j /
 // sum_j w_j, w_j = 2^(lse_j - max) (o_j: bf16 pieces, each normalised by its
 // own row sum).  A lane lying in one piece was written whole by the attention
-// kernel and is skipped.  One block per (session, head, 64-row chunk): the
+// kernel and is skipped.  One block per (session, head, 16-row chunk): the
 // lane's piece count is computed once per block; one thread per (row, 8
 // features), the loads of all pieces of a row in flight together.
 template <int HD>

@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
+
 #include "../../include/fmd.h"
 
 namespace fmd {
@@ -214,7 +216,7 @@ __host__ __device__ inline int piece_of(int64_t first, int64_t x, int n0, int n1
   return k;
 }
 
-constexpr int kCombineRowsPerBlock = 64;   // rows of one lane per combine block
+constexpr int kCombineRowsPerBlock = 16;   // rows of one lane per combine block
 
 struct CombineSess {
   const bf16* opart;
@@ -224,7 +226,7 @@ struct CombineSess {
   int32_t nwin_total;
   int32_t lane0;
   int32_t n0, n1;     // windows of the ring segments (the lane's cuts)
-  int32_t item0;      // first block of this session: H * ceil(n_q / 64) blocks
+  int32_t item0;      // first block of this session: H * ceil(n_q / 16) blocks
 };
 struct CombineArgs {
   CombineSess s[kMaxSessPerLaunch];
@@ -244,6 +246,11 @@ struct CombineArgs {
 //               r <- r + Y and writes zb <- bf16(z + r), the next layer's input;
 //   kProjLayerLast: the stack's last layer: z <- z - h * (r + Y), r <- 0,
 //               and, if zb is set, zb <- bf16(z).
+// With splits > 1 the k range is cut into `splits` equal parts: work-group
+// (tile, split j) writes its fp32 partial product to part[j] ([splits][n_q][d]
+// per session), and launch_proj_reduce sums the parts in order j = 0, 1, ...
+// and applies the epilogue.  Used when the tiles alone would leave most CUs
+// idle (small units).
 constexpr int kProjEuler = 0;
 constexpr int kProjLayer = 2;
 constexpr int kProjLayerLast = 3;
@@ -253,9 +260,10 @@ struct ProjSess {
   float* z;           // [n_q][d]
   bf16* zb;           // [n_q][d] or nullptr
   float* r;           // kProjLayer*: [n_q][d] residual
+  float* part;        // splits > 1: [splits][n_q][d] fp32 partial products
   int32_t n_q;
   int32_t n_mtiles;
-  int32_t item0;
+  int32_t item0;      // first work-group: n_mtiles * n-tiles * splits per session
   float h;
 };
 struct ProjArgs {
@@ -265,6 +273,7 @@ struct ProjArgs {
   int32_t d;
   int32_t n_out;
   int32_t items;
+  int32_t splits;     // k-range parts (1: the epilogue runs in the GEMM)
 };
 
 // Q/K/V projection of the latent: [Q | K_u | V_u] = bf16(zb * W_qkv^T)
@@ -325,6 +334,8 @@ hipError_t launch_vt(const VtArgs& a, int head_dim, hipStream_t st);
 hipError_t launch_attn(const AttnArgs& a, int head_dim, hipStream_t st);
 hipError_t launch_combine(const CombineArgs& a, int head_dim, hipStream_t st);
 hipError_t launch_proj(const ProjArgs& a, int mode, hipStream_t st);
+// The sum of the split parts and the epilogue of `mode`, 4 elements per thread.
+hipError_t launch_proj_reduce(const ProjArgs& a, int mode, hipStream_t st);
 hipError_t launch_cvt(const CvtArgs& a, hipStream_t st);
 hipError_t launch_mix(const MixArgs& a, hipStream_t st);
 hipError_t launch_qkv_wide(const QkvArgs& a, hipStream_t st);
@@ -339,6 +350,15 @@ constexpr int kAttnWindow = 64;                              // keys per window
 // Projection tiling: 160 rows x 128 output features per block.
 constexpr int kProjTile = 160;
 constexpr int kProjTileN = 128;
+constexpr int kProjBK = 64;
+// k-range parts of a projection launch with `tiles` output tiles and nk k
+// steps: enough work-groups to fill the chip when the tiles fill less than
+// half of it, with at least two k steps per part.
+inline int proj_splits(int64_t tiles, int nk) {
+  if (tiles <= 0 || tiles * 2 >= kTargetCUs) return 1;
+  const int64_t want = kTargetCUs / tiles;
+  return (int)std::max<int64_t>(1, std::min<int64_t>(want, nk / 2));
+}
 // Q/K/V projection tiling: 256 rows x 256 output features per block.
 constexpr int kQkvTile = 256;
 

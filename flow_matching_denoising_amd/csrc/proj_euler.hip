@@ -24,8 +24,11 @@
 // the operands come mostly from other work-groups' misses in L2 and the
 // Infinity Cache, so the bytes a CU has in flight, not the L2 bandwidth,
 // set its load rate.
-// Item order inside a session: output-feature tile major, row tile minor, so
-// the row tiles that share one slab of W are adjacent and run on the same XCD.
+// Item order inside a session: k part major, then output-feature tile, then
+// row tile, so the row tiles that share one slab of W are adjacent and run on
+// the same XCD.  With k parts (small units), each work-group multiplies one
+// part of the k range and stores its fp32 partial tile; proj_reduce_kernel
+// sums the parts in a fixed order and applies the epilogue.
 #include "fmd_internal.h"
 
 namespace fmd {
@@ -34,7 +37,7 @@ namespace {
 
 constexpr int BM = kProjTile;                       // 160 rows
 constexpr int BN = kProjTileN;                      // 128 output features
-constexpr int BK = 64;
+constexpr int BK = kProjBK;
 constexpr int WAVES = 4;
 constexpr int MT = BM / 32;                         // 5 row tiles of 32
 constexpr int STAGES = 4;
@@ -48,6 +51,8 @@ static_assert(BN == 32 * WAVES, "one 32-feature column tile per wave");
 static_assert((STAGES & (STAGES - 1)) == 0, "the stage index wraps with a mask");
 
 }  // namespace
+
+constexpr int kProjPartial = -1;   // epilogue: store the fp32 partial tile
 
 template <int MODE>
 __global__ __launch_bounds__(WAVES * 64) void proj_kernel(ProjArgs a) {
@@ -63,9 +68,13 @@ __global__ __launch_bounds__(WAVES * 64) void proj_kernel(ProjArgs a) {
   const int n_q = s.n_q;
   const float hstep = s.h;
   const int d = a.d;
+  const int ntn = (a.n_out + BN - 1) / BN;
+  const int tiles = s.n_mtiles * ntn;
   const int local = item - s.item0;
-  const int mt = local % s.n_mtiles;
-  const int nt = local / s.n_mtiles;
+  const int part = local / tiles;
+  const int tl = local - part * tiles;
+  const int mt = tl % s.n_mtiles;
+  const int nt = tl / s.n_mtiles;
   const int m0 = mt * BM, n0 = nt * BN;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
@@ -87,7 +96,11 @@ __global__ __launch_bounds__(WAVES * 64) void proj_kernel(ProjArgs a) {
     const int chunk = (lane & 7) ^ ((rt >> 1) & 7);
     voff[i] = rt * d * 2 + chunk * 16;
   }
+  const int nk_all = d / BK;
+  const int kb = part * nk_all / a.splits;
+  const int nk = (part + 1) * nk_all / a.splits - kb;      // this work-group's k steps
   auto load_stage = [&](int kt, int st) __attribute__((always_inline)) {
+    kt += kb;
     char* base = lds + st * STAGE_BYTES;
 #pragma unroll
     for (int i = 0; i < LOADS_PER_WAVE; ++i) {
@@ -106,7 +119,6 @@ __global__ __launch_bounds__(WAVES * 64) void proj_kernel(ProjArgs a) {
   f32x16 acc[MT];
 #pragma unroll
   for (int i = 0; i < MT; ++i) acc[i] = f32x16{};
-  const int nk = d / BK;
   // Pipeline: four LDS stages, k step t in buffer t % 4.  The barrier that
   // publishes k step t+1 sits DA slots before the end of k step t, right
   // after every wave has issued its last read of buffer t: the reads of
@@ -188,7 +200,14 @@ __global__ __launch_bounds__(WAVES * 64) void proj_kernel(ProjArgs a) {
   // knows, so loads issued per row tile would wait out the memory latency
   // once per tile.
   auto row = [&](int i, int q) { return m0 + i * 32 + (q >> 2) * 8 + g * 4 + (q & 3); };
-  if constexpr (MODE == kProjEuler) {
+  if constexpr (MODE == kProjPartial) {
+    float* const pc = s.part + (int64_t)part * n_q * d + n;
+#pragma unroll
+    for (int i = 0; i < MT; ++i)
+#pragma unroll
+      for (int q = 0; q < 16; ++q)
+        if (full || row(i, q) < n_q) pc[(int64_t)row(i, q) * d] = acc[i][q];
+  } else if constexpr (MODE == kProjEuler) {
     // z[m][n] -= h * y[m][n] (and zb = bf16(z)).
     float* const zc = z + n;
     bf16* const zbc = s.zb ? s.zb + n : nullptr;
@@ -290,12 +309,79 @@ __global__ __launch_bounds__(256) void mix_kernel(MixArgs a) {
   *reinterpret_cast<bf16x8*>(s.oc + e) = y;
 }
 
+// The split projection's second half: y = part[0] + part[1] + ... (in that
+// order), then the epilogue of MODE on 4 consecutive elements per thread.
+template <int MODE>
+__global__ __launch_bounds__(256) void proj_reduce_kernel(ProjArgs a) {
+  // Element E of the launch: sessions' [n_q][d] outputs back to back.
+  const int64_t E = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  const int d = a.d;
+  int si = -1;
+  int64_t base = 0, e = 0;
+#pragma unroll
+  for (int i = 0; i < kMaxSessPerLaunch; ++i) {
+    if (i < a.n_sess) {
+      const int64_t ne_i = (int64_t)a.s[i].n_q * d;
+      if (si < 0 && E < base + ne_i) {
+        si = i;
+        e = E - base;       // row * d + feature within session i
+      }
+      base += ne_i;
+    }
+  }
+  if (si < 0) return;
+  const ProjSess& s = a.s[si];
+  const int64_t ne = (int64_t)s.n_q * d;
+  const float* const pp = s.part + e;
+  f32x4 y = *reinterpret_cast<const f32x4*>(pp);
+  // Parts 1, 2, ... added in order, their loads issued four at a time.
+  for (int j0 = 1; j0 < a.splits; j0 += 4) {
+    f32x4 p[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      p[u] = j0 + u < a.splits ? *reinterpret_cast<const f32x4*>(pp + (j0 + u) * ne)
+                               : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (j0 + u < a.splits)
+#pragma unroll
+        for (int t = 0; t < 4; ++t) y[t] += p[u][t];
+  }
+  f32x4 zv = *reinterpret_cast<const f32x4*>(s.z + e);
+  if constexpr (MODE == kProjEuler) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) zv[t] = zv[t] - s.h * y[t];
+    *reinterpret_cast<f32x4*>(s.z + e) = zv;
+  } else {
+    f32x4 rv = *reinterpret_cast<const f32x4*>(s.r + e);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) rv[t] += y[t];
+    if constexpr (MODE == kProjLayer) {
+      *reinterpret_cast<f32x4*>(s.r + e) = rv;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) zv[t] += rv[t];   // the next layer's input z + r
+    } else {
+#pragma unroll
+      for (int t = 0; t < 4; ++t) zv[t] = zv[t] - s.h * rv[t];
+      *reinterpret_cast<f32x4*>(s.z + e) = zv;
+      *reinterpret_cast<f32x4*>(s.r + e) = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+  }
+  if (s.zb) {
+    union { bf16 b[4]; uint2 u; } o;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) o.b[t] = (bf16)zv[t];
+    *reinterpret_cast<uint2*>(s.zb + e) = o.u;
+  }
+}
+
 hipError_t launch_proj(const ProjArgs& a, int mode, hipStream_t st) {
   if (a.items <= 0) return hipSuccess;
   static const hipError_t attr_err = [] {
     const void* fns[] = {reinterpret_cast<const void*>(&proj_kernel<kProjEuler>),
                          reinterpret_cast<const void*>(&proj_kernel<kProjLayer>),
-                         reinterpret_cast<const void*>(&proj_kernel<kProjLayerLast>)};
+                         reinterpret_cast<const void*>(&proj_kernel<kProjLayerLast>),
+                         reinterpret_cast<const void*>(&proj_kernel<kProjPartial>)};
     hipError_t e = hipSuccess;
     for (const void* f : fns)
       if (e == hipSuccess)
@@ -304,11 +390,32 @@ hipError_t launch_proj(const ProjArgs& a, int mode, hipStream_t st) {
   }();
   if (attr_err != hipSuccess) return attr_err;
   const dim3 grid(a.items), block(WAVES * 64);
+  if (a.splits > 1) mode = kProjPartial;
   switch (mode) {
+    case kProjPartial:
+      hipLaunchKernelGGL(proj_kernel<kProjPartial>, grid, block, LDS_BYTES, st, a);
+      break;
     case kProjEuler: hipLaunchKernelGGL(proj_kernel<kProjEuler>, grid, block, LDS_BYTES, st, a); break;
     case kProjLayer: hipLaunchKernelGGL(proj_kernel<kProjLayer>, grid, block, LDS_BYTES, st, a); break;
     case kProjLayerLast:
       hipLaunchKernelGGL(proj_kernel<kProjLayerLast>, grid, block, LDS_BYTES, st, a);
+      break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_proj_reduce(const ProjArgs& a, int mode, hipStream_t st) {
+  if (a.items <= 0 || a.splits <= 1) return hipSuccess;
+  int64_t rows = 0;   // one thread per 4 elements of the sessions' outputs
+  for (int i = 0; i < a.n_sess; ++i) rows += a.s[i].n_q;
+  const int64_t threads = rows * a.d / 4;
+  const dim3 grid((unsigned)((threads + 255) / 256)), block(256);
+  switch (mode) {
+    case kProjEuler: hipLaunchKernelGGL(proj_reduce_kernel<kProjEuler>, grid, block, 0, st, a); break;
+    case kProjLayer: hipLaunchKernelGGL(proj_reduce_kernel<kProjLayer>, grid, block, 0, st, a); break;
+    case kProjLayerLast:
+      hipLaunchKernelGGL(proj_reduce_kernel<kProjLayerLast>, grid, block, 0, st, a);
       break;
     default: return hipErrorInvalidValue;
   }

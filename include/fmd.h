@@ -180,8 +180,12 @@ typedef struct fmd_unit_io {
   const float* h;
 } fmd_unit_io;
 
-/* Workspace bytes fmd_denoise_unit needs (pure host arithmetic). */
-int fmd_unit_workspace_bytes(const fmd_unit_io* sessions, int32_t n_sessions,
+/* Workspace bytes fmd_denoise_unit needs for n_steps steps (pure host
+ * arithmetic).  The unit keys and values of all n_steps steps are staged in
+ * the attention's layouts by one launch before the first step, so the
+ * workspace holds n_steps copies of them (one when every session's
+ * step_stride_elems is 0).  Errors: as fmd_denoise_unit's validation. */
+int fmd_unit_workspace_bytes(const fmd_unit_io* sessions, int32_t n_sessions, int32_t n_steps,
                              size_t* out_bytes);
 
 /*

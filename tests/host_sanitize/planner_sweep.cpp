@@ -112,12 +112,12 @@ int main(int argc, char** argv) {
       st[i] = {&after[i], io[i].q, io[i].k_u, io[i].v_u, io[i].z, s.n_video, s.n_audio, 0.5f};
     }
     size_t a = 0, b = 0, a2 = 0;
-    int rc = fmd_unit_workspace_bytes(io.data(), n, &a);
+    int rc = fmd_unit_workspace_bytes(io.data(), n, 1, &a);
     CHECK(rc == FMD_OK, "case %d: unit planner rc=%d", c, rc);
     rc = fmd_workspace_bytes(st.data(), n, &b);
     CHECK(rc == FMD_OK, "case %d: step planner rc=%d", c, rc);
     CHECK(a == b, "case %d: unit %zu vs step %zu bytes", c, a, b);
-    rc = fmd_unit_workspace_bytes(io.data(), n, &a2);
+    rc = fmd_unit_workspace_bytes(io.data(), n, 1, &a2);
     CHECK(rc == FMD_OK && a2 == a, "case %d: planner not deterministic", c);
     int64_t min_bytes = 0;
     for (int i = 0; i < n; ++i) {

@@ -158,7 +158,7 @@ def test_denoise_unit_validation_leaves_state():
     io.step_stride_elems = 0
     arr = (_UnitIO * 1)(io)
     out = ctypes.c_size_t(0)
-    assert fmd._unit_workspace_bytes(arr, 1, ctypes.byref(out)) == 0 and out.value > 0
+    assert fmd._unit_workspace_bytes(arr, 1, 2, ctypes.byref(out)) == 0 and out.value > 0
 
 
 def test_profile_read_rejects_bad_class():
@@ -392,6 +392,34 @@ def _model_pieces(H, per_head, lanes, groups):
     return out
 
 
+def _proj_part_bytes(n_q, d):
+    """fp32 partial products of a split projection: 160 x 128 output tiles;
+    when they fill less than half of 256 CUs, the k range (d / 64 steps) is
+    cut into enough parts to fill the chip, at least two k steps each."""
+    tiles = -(-n_q // 160) * -(-d // 128)
+    if tiles * 2 >= 256:
+        return 0
+    splits = max(1, min(256 // tiles, (d // 64) // 2))
+    return splits * n_q * d * 4 if splits > 1 else 0
+
+
+def test_projection_split_workspace():
+    # The 192x336-class unit (12 heads x 128, 260 queries): 2 x 12 tiles, so
+    # the k range of 24 steps is cut into 10 parts of fp32 partials.
+    c = _cache(H=12, hd=128, cap=8576, ln=8576, head=0)
+    rc, n_split = _ws([_step(c, 252, 8)])
+    assert rc == 0
+    assert _proj_part_bytes(260, 1536) == 10 * 260 * 1536 * 4
+    big = _cache(H=40, hd=128, cap=60416, ln=60416, head=0)
+    rc, n_big = _ws([_step(big, 920, 8)])
+    assert rc == 0 and _proj_part_bytes(928, 5120) == 0
+    # Staged unit K and V (npad = 272), O and the partials; the 8,836 keys per
+    # query make few windows, so no lane is cut into pieces here or the
+    # pieces' bytes come on top.
+    base = 2 * 12 * 272 * 128 * 2 + 260 * 1536 * 2 + 10 * 260 * 1536 * 4
+    assert n_split >= base
+
+
 @pytest.mark.parametrize("H,head", [(5, 59472), (10, 59472), (40, 59472), (40, 0), (12, 8304)])
 def test_group_planner_pieces(H, head):
     # A full 60,416-key ring and a 928-query unit (4 query blocks): 8 XCDs x
@@ -403,6 +431,7 @@ def test_group_planner_pieces(H, head):
     rc, nbytes = _ws([_step(c, 920, 8)])
     assert rc == 0
     staged = 2 * H * n_q * hd * 2 + n_q * H * hd * 2      # unit K, V (npad = n_q) and O
+    staged += _proj_part_bytes(n_q, H * hd)
     per_piece = n_q * H * (hd * 2 + 4)
     start = head % cap                                     # the valid range starts at head
     seg0 = cap - start
@@ -433,7 +462,7 @@ def test_noalloc_rejects_units_beyond_the_static_scratch():
                        FAKE + 0x40000000 + i * 0x2000000, 920, 8, hp) for i, c in enumerate(cs)]
         arr = (_UnitIO * n)(*ios)
         need = ctypes.c_size_t(0)
-        assert fmd._unit_workspace_bytes(arr, n, ctypes.byref(need)) == 0
+        assert fmd._unit_workspace_bytes(arr, n, 4, ctypes.byref(need)) == 0
         assert (need.value <= fmd.FMD_NOALLOC_SCRATCH_BYTES) == fits, need.value
         if not fits:
             assert fmd._denoise_unit_noalloc(arr, n, 4, FAKE, None) == -5
