@@ -313,8 +313,11 @@ def append_batch_probe(launches=20):
     """The batched ring append at the 8-session shape (rings of 8..128 units of
     944 tokens, 40 heads x 128, per-session append offsets): one launch appends
     all 8 slices (309 MB read + written).  Timed with HIP events recorded on the
-    launch stream; every launch appends at the same offsets.  The rings' contents
-    do not affect the append, so they are left uninitialised."""
+    launch stream.  Launches alternate between two sets of slices and two append
+    offsets per ring (half a ring apart), so consecutive launches touch disjoint
+    bytes: 618 MB per cycle, more than the 256 MB Infinity Cache holds, so the
+    rate is not one of that cache.  The rings' contents do not affect the
+    append, so they are left uninitialised."""
     import torch
 
     import flow_matching_denoising_amd as fmd
@@ -323,34 +326,39 @@ def append_batch_probe(launches=20):
     wl = workload.get("v02_batch8")
     dev = torch.device("cuda:0")
     g = torch.Generator(device=dev).manual_seed(5)
-    caches, ks, vs, states = [], [], [], []
+    caches, sets = [], [([], [], []), ([], [], [])]
     for s in wl.sessions:
         caches.append(fmd.KVCache(s.n_heads, s.head_dim, s.cap_tokens, device=dev,
                                   len_tokens=s.len_before, head_tokens=s.head_before))
         shape = (s.slice_tokens, s.n_heads, s.head_dim)
-        ks.append(torch.randn(shape, generator=g, device=dev).to(torch.bfloat16))
-        vs.append(torch.randn(shape, generator=g, device=dev).to(torch.bfloat16))
-        states.append((s.len_before, s.head_before))
+        assert 2 * s.slice_tokens <= s.cap_tokens, "the two offsets' blocks must not overlap"
+        for k, (ks, vs, states) in enumerate(sets):
+            ks.append(torch.randn(shape, generator=g, device=dev).to(torch.bfloat16))
+            vs.append(torch.randn(shape, generator=g, device=dev).to(torch.bfloat16))
+            head = (s.head_before + k * (s.cap_tokens // 2)) % s.cap_tokens
+            states.append((s.len_before, head))
 
-    def once():
+    def once(k):
+        ks, vs, states = sets[k]
         for c, (ln, hd_) in zip(caches, states):
             c.set_state(ln, hd_)
         fmd.kv_append_batched(caches, ks, vs)
 
-    for _ in range(3):
-        once()
+    for i in range(4):
+        once(i & 1)
     torch.cuda.synchronize()
     fmd.profile_enable(True)
-    for _ in range(launches):
-        once()
+    for i in range(launches):
+        once(i & 1)
     torch.cuda.synchronize()
     ms, n = fmd.profile_read("append")
     fmd.profile_enable(False)
     avg_s = ms / n / 1e3
     nbytes = wl.append_bytes()
-    del caches, ks, vs
+    del caches, sets
     torch.cuda.empty_cache()
     return {"workload": "v02_batch8", "bytes_per_launch": nbytes, "launches": n,
+            "bytes_touched_per_cycle": 2 * nbytes,
             "avg_launch_us": round(avg_s * 1e6, 2), "GBps": round(nbytes / avg_s / 1e9, 1),
             "frac_hbm": round(nbytes / avg_s / 1e9 / HBM_PEAK_GBS, 4)}
 
