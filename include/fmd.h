@@ -70,6 +70,10 @@ typedef enum {
  *   v : bf16 [n_heads][cap_tokens/16][head_dim][16]       (16-token blocks, each
  *       stored feature-major: element (h, slot p, e) is at
  *       ((h*(cap/16) + p/16)*head_dim + e)*16 + p%16)
+ *   The pages fix no layout; they pre-shard the cache so that no step has to
+ *   rearrange it [精读笔记 (paper.gecl.asia), Key Insight].  V is kept in
+ *   16-token feature-major blocks so that the attention's P*V product reads
+ *   its operand straight from the stored bytes, hence cap_tokens % 16 == 0.
  *   head_dim   : 64 or 128
  *   cap_tokens : ring capacity in tokens, a positive multiple of 16, with
  *                cap_tokens*head_dim*2 < 2^31 (one head's slice is addressed
@@ -137,7 +141,11 @@ int fmd_workspace_bytes(const fmd_unit_step* units, int32_t n_units, size_t* out
  *       1/sqrt(head_dim), no mask; q is multiplied by log2(e)/sqrt(head_dim)
  *       and rounded to bf16 once, scores, softmax and accumulation are fp32,
  *       the probabilities enter the value product as bf16, O is rounded to
- *       bf16;
+ *       bf16.  The keys of one launch are cut into equal ranges, one per
+ *       group of work-groups; the rows of a (head, session) whose keys a cut
+ *       splits get each piece's normalised output stored as bf16 (with an
+ *       fp32 log-sum-exp) and merged, and the merged O is rounded to bf16
+ *       again: one extra bf16 rounding (<= 2^-9 relative) for those rows;
  *   v = O_flat * W_o^T with O_flat [n_q][d] (heads concatenated);
  *   z <- z - h * v  (fp32).
  *   w_o: bf16 [d][d] stored [d_out][d_in], d = n_heads*head_dim, shared.
@@ -206,9 +214,10 @@ int fmd_denoise_unit(fmd_unit_io* sessions, int32_t n_sessions, int32_t n_steps,
  * library holds on every GPU it runs on until the process ends.  The call
  * allocates no device memory.
  *   - A unit whose scratch need (fmd_unit_workspace_bytes) exceeds
- *     FMD_NOALLOC_SCRATCH_BYTES -> FMD_E_WORKSPACE, nothing enqueued.  The
- *     640x368-class unit (40 heads x 928 queries, 60,416 cached keys) needs
- *     about 115 MB and fits; the 242k-key ring of that shape does not.
+ *     FMD_NOALLOC_SCRATCH_BYTES -> FMD_E_WORKSPACE, nothing enqueued.  One
+ *     640x368-class session (40 heads x 928 queries, 4 steps with their own
+ *     Q/K/V) needs 124 MB with 60,416 cached keys and 134 MB with the wrapped
+ *     241,664-key ring, and fits; two such sessions do not.
  *   - `stream` must belong to the current device (FMD_E_INVAL otherwise).
  *   - Every call on one GPU shares that GPU's scratch: calls that overlap on
  *     one GPU (different streams or host threads without ordering) race and
