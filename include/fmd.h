@@ -378,9 +378,9 @@ const char* fmd_last_error(void);
 /* Kernel classes that fmd_profile_* report on. */
 enum {
   FMD_KERNEL_APPEND = 0,    /* ring append */
-  FMD_KERNEL_VT = 1,        /* 16-token transpose of the unit's values */
+  FMD_KERNEL_VT = 1,        /* staging of the unit's keys/values in the ring layouts */
   FMD_KERNEL_ATTN = 2,      /* attention main kernel */
-  FMD_KERNEL_COMBINE = 3,   /* merge of key-split partial results */
+  FMD_KERNEL_COMBINE = 3,   /* merge of the pieces of cut (head, session) lanes */
   FMD_KERNEL_PROJ = 4,      /* projection GEMM with the Euler update */
   FMD_KERNEL_QKV = 5,       /* projection of the latent to Q, K_u, V_u */
   FMD_KERNEL_CVT = 6,       /* bf16 copy of the starting latent */

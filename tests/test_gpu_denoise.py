@@ -181,7 +181,7 @@ def test_maximum_session_count_four_launch_chunks():
 
 def test_profiling_records_only_the_selected_classes():
     # One unit = one append, one staging of every step's unit K/V, then per
-    # step attention, the merge of key splits (if any) and the projection.
+    # step attention, the merge of cut lanes (if any) and the projection.
     # Recording is on for the attention class only, then for every class.
     wl = workload.get("v01_unit")
     n_steps = len(wl.sessions[0].h)

@@ -3,8 +3,9 @@
 Each workload runs as the benchmark launches it: every session of the unit in
 one ``denoise_unit`` call (append, then every solver step).  Afterwards the
 attention output of every step is taken through ``fmd_attention`` on the
-post-append rings, with the same key-split plan as inside the unit (the plan
-depends only on the shapes), and compared element by element with the oracle:
+post-append rings, with the same cut of the keys into group ranges as inside
+the unit (the plan depends only on the shapes), and compared element by
+element with the oracle:
 every row and head of O for the steps named below, and ``dz = z - eps``.
 
 Tolerances: max-abs 2e-2 and rel-L2 1e-2 on O and dz (rel-L2 on its own is the
