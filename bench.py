@@ -610,6 +610,9 @@ def main():
         },
         "per_kernel_us": {k: (round(v, 2) if v is not None else None)
                           for k, v in per_kernel_us.items()},
+        # launches of each class per unit (the staging launch covers every step)
+        "launches_per_unit": {k: (round(v[1] / min(args.steps, 10), 2) if v[1] else 0)
+                              for k, v in kt.items() if k != "attn"},
         "append_GBps": round(append_gbs, 1) if append_gbs else None,
         "append_frac_hbm": round(append_gbs / HBM_PEAK_GBS, 4) if append_gbs else None,
         "proj_TFLOPs": round(proj_tflops, 1) if proj_tflops else None,
