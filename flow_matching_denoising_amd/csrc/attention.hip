@@ -35,8 +35,8 @@
 // so P never leaves the registers.  V^T rows are permuted so that each lane's
 // 16 output registers hold 16 consecutive features of its query.
 //
-// Q^T is multiplied by scale * log2(e) (and rounded to bf16) once per work
-// item, and every QK product after the first window starts its accumulation
+// Q^T is multiplied by scale * log2(e) (and rounded to bf16) once per span,
+// and every QK product after the first window starts its accumulation
 // from -m (m: the row's running maximum), so the MFMA returns the shifted
 // score in exp2 units and exp2 takes it as it is: no per-score FMA.  Softmax
 // rescaling is lazy: m, O and the running sum move only when a row maximum
