@@ -46,6 +46,13 @@ __device__ __forceinline__ u32x4 ld16(const void* p) {
 __device__ __forceinline__ void st16(void* p, u32x4 v) {
   *reinterpret_cast<u32x4*>(p) = v;
 }
+// The same with the non-temporal hint (data streamed once).
+__device__ __forceinline__ u32x4 ld16_nt(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+__device__ __forceinline__ void st16_nt(void* p, u32x4 v) {
+  __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
+}
 
 // ---------------------------------------------------------------------------
 // Global -> LDS loads through buffer resources (MUBUF loads with the lds bit).
