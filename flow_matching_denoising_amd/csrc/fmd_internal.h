@@ -80,7 +80,10 @@ __device__ __forceinline__ i32x4 make_rsrc(const bf16* base, int bytes) {
 // order these loads themselves: s_waitcnt vmcnt(N) and a barrier before any
 // wave reads a tile (wait_loads_and_sync), a barrier between the last read of
 // a buffer and the next load into it.  One wait state separates the M0 write
-// from the load that reads it.
+// from the load that reads it.  The compiler treats M0 as reserved and does
+// not honour it in a clobber list; these kernels leave M0 to these helpers
+// alone (a build check asserts that no compiler-generated instruction reads
+// or writes it).
 __device__ __forceinline__ void dma16(const i32x4& rs, int voff, int soff, char* dst) {
   const uint32_t m0 =
       (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)dst;

@@ -184,7 +184,7 @@ void qkv_wide_kernel(QkvArgs a) {
       }
   __syncthreads();
 
-  const int H = d / a.hd, hd = a.hd;
+  const int hd = a.hd;
   const int npad = s.npad;
   const int nblk = npad / 16;
   // Q and K_u: one thread per (row, 16-byte chunk); a wave writes two rows.

@@ -180,6 +180,17 @@ def test_device_code_has_no_packed_fp32_arithmetic():
             asm = open(out).read()
             assert not re.search(r"v_pk_(add|mul|fma)_f32", asm), name
             assert "scratch_" not in asm, f"{name}: register spills to scratch"
+            # M0 is set by the LDS-DMA helpers' inline assembly; the compiler
+            # ignores it in their clobber lists, so none of its own code may use it.
+            outside, inside = [], False
+            for line in asm.splitlines():
+                if ";;#ASMSTART" in line:
+                    inside = True
+                elif ";;#ASMEND" in line:
+                    inside = False
+                elif not inside and not line.lstrip().startswith(";"):
+                    outside.append(line)
+            assert not [l for l in outside if re.search(r"\bm0\b", l)], f"{name}: compiler uses M0"
 
 
 def test_denoise_unit_qkv_validation_leaves_state():
