@@ -285,6 +285,30 @@ def kv_append_batched(caches, k_slices, v_slices, stream=None):
     _check(_kv_append_batched(arr_c, arr_k, arr_v, arr_t, n, _stream_ptr(stream)))
 
 
+class PreparedAppend:
+    """``kv_append_batched`` with its argument arrays built once, for loops
+    that append from the same slice buffers into the same caches every time:
+    ``launch()`` only enqueues.  The caches' host state (len, head) is read and
+    advanced by each launch, as with ``kv_append_batched``."""
+
+    def __init__(self, caches, k_slices, v_slices):
+        n = len(caches)
+        if len(k_slices) != n or len(v_slices) != n:
+            raise ValueError("one K and one V slice per cache")
+        for c, k, v in zip(caches, k_slices, v_slices):
+            if k is None or v is None:
+                raise ValueError("k_slices and v_slices must not hold None")
+            _expect_slices(k, v, c.n_heads, c.head_dim)
+        self._keep = (list(caches), list(k_slices), list(v_slices))
+        self._args = ((ctypes.POINTER(_Cache) * n)(*[ctypes.pointer(c._c) for c in caches]),
+                      (_vp * n)(*[_ptr(t, torch.bfloat16, "k_slice") for t in k_slices]),
+                      (_vp * n)(*[_ptr(t, torch.bfloat16, "v_slice") for t in v_slices]),
+                      (_i64 * n)(*[t.shape[0] for t in k_slices]), n)
+
+    def launch(self, stream=None):
+        _check(_kv_append_batched(*self._args, _stream_ptr(stream)))
+
+
 class UnitStep:
     """One session's inputs for one solver step (see ``fmd_unit_step``)."""
 

@@ -117,3 +117,13 @@ def test_weight_shapes_checked_before_any_pointer():
 def test_forced_split_entry_rejects_negative():
     assert fmd._test_force_attn_groups(-1) == -1
     assert fmd._test_force_attn_groups(0) == 0
+
+
+def test_prepared_append_shapes():
+    with pytest.raises(ValueError, match="one K and one V slice per cache"):
+        fmd.PreparedAppend([C], [], [])
+    with pytest.raises(ValueError):
+        fmd.PreparedAppend([C], [_t(5, H + 1, HD)], [_t(5, H + 1, HD)])
+    with pytest.raises(ValueError):
+        fmd.PreparedAppend([C], [_t(5, H, HD)], [_t(6, H, HD)])
+

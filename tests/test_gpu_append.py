@@ -71,6 +71,32 @@ def test_append_batched_matches_single():
         assert np.array_equal(gk, ok) and np.array_equal(gv, ov)
 
 
+def test_prepared_append_matches_oracle_twice():
+    # The prepared call reads the caches' current state at every launch: two
+    # launches without resetting it append twice, as two batched calls would.
+    rng = np.random.default_rng(4)
+    specs = [(96, 40, 17), (64, 63, 30)]   # (cap, head0, T)
+    H, hd = 2, 64
+    caches, ks, vs, refs = [], [], [], []
+    for cap, head0, T in specs:
+        rk, rv = random_bits(rng, (H, cap, hd)), random_bits(rng, (H, cap, hd))
+        shape = workload.custom_session(H, hd, 1, 0, 0, cap, cap, head0, (1.0,))
+        caches.append(make_cache(fmd, shape, rk, rv))
+        sk, sv = random_bits(rng, (T, H, hd)), random_bits(rng, (T, H, hd))
+        ks.append(dev_bf16(sk))
+        vs.append(dev_bf16(sv))
+        k1, v1, l1, h1 = oracle.kv_append(rk, rv, cap, head0, sk, sv)
+        refs.append(oracle.kv_append(k1, v1, l1, h1, sk, sv))
+    prep = fmd.PreparedAppend(caches, ks, vs)
+    prep.launch()
+    prep.launch()
+    torch.cuda.synchronize()
+    for c, (ok, ov, ol, oh) in zip(caches, refs):
+        gk, gv = cache_logical(fmd, c)
+        assert (c.len_tokens, c.head_tokens) == (ol, oh)
+        assert np.array_equal(gk, ok) and np.array_equal(gv, ov)
+
+
 @pytest.mark.parametrize("name", ["v01_unit", "v02_unit"])
 def test_append_full_size(name):
     # The unit's append at the full shapes (poisoned last unit gets overwritten).
