@@ -18,8 +18,7 @@
 // log-sum-exp and merged by the combine kernel.
 //
 // Per work-group: 8 waves (two per SIMD, so one wave's MFMAs overlap the
-// other's softmax), 32 query rows per wave; the first wave of each SIMD issues
-// the window loads.  Keys stream through LDS in
+// other's softmax), 32 query rows per wave.  Keys stream through LDS in
 // 64-key windows aligned to 16-slot blocks (the first and last window of a
 // ring segment may be partial; their out-of-range keys are masked and their
 // values zeroed).
@@ -77,12 +76,6 @@ __device__ __forceinline__ float sum_xor32(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// Waves that issue the window loads: the first wave of each SIMD.  The
-// oldest wave of a SIMD wins the matrix pipe and finishes each window's
-// MFMAs first; giving it all the loads keeps their issue off the later
-// wave, which sets each step's length.
-constexpr int kAttnLoaders = 4;
-
 template <int HD>
 struct Tiles {
   static constexpr int KC = HD / 16;           // 16-wide k chunks of the QK product
@@ -91,8 +84,8 @@ struct Tiles {
   static constexpr int V_BYTES = kAttnWindow * HD * 2;
   static constexpr int K_BLOCKS = K_BYTES / 1024;        // 1 KiB operand blocks
   static constexpr int V_BLOCKS = V_BYTES / 1024;
-  static constexpr int K_PER_WAVE = K_BLOCKS / kAttnLoaders;   // per loading wave
-  static constexpr int V_PER_WAVE = V_BLOCKS / kAttnLoaders;
+  static constexpr int K_PER_WAVE = K_BLOCKS / kAttnWaves;
+  static constexpr int V_PER_WAVE = V_BLOCKS / kAttnWaves;
   static constexpr int STAGES = 4;                       // K and V quadruple-buffered
   static constexpr int LDS_BYTES = STAGES * (K_BYTES + V_BYTES);
 };
@@ -150,22 +143,19 @@ __device__ __forceinline__ Window window_of(const Span& sp, int j) {
 // segment's end (start * HD * 2 < 2^31) can reach up to 16 KiB past it, which
 // the range check turns into zeros.
 template <int HD, bool CHECKED, int N>
-__device__ __forceinline__ void load_tile(const i32x4& rs, int start, char* dst, int off0,
-                                          int wave) {
-  if (wave >= kAttnLoaders) return;
+__device__ __forceinline__ void load_tile(const i32x4& rs, int start, char* dst,
+                                          const int (&off)[N], int wave) {
   const uint32_t woff = (uint32_t)start * (HD * 2);
   // LDS destination: one wave-uniform base (the tile plus this wave's first
-  // 1 KiB block) and a constant offset per instruction.  Block i of this
-  // wave sits kAttnLoaders KiB after block i-1, in the window and in LDS.
+  // 1 KiB block) and a constant offset per instruction.
   const uint32_t base =
       (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)dst + wave * 1024;
 #pragma unroll
   for (int i = 0; i < N; ++i) {
-    const uint32_t step = (uint32_t)(kAttnLoaders * i * 1024);
     if (CHECKED)
-      dma16_at(rs, (int)((uint32_t)off0 + woff + step), 0, base, step);
+      dma16_at(rs, (int)((uint32_t)off[i] + woff), 0, base, kAttnWaves * i * 1024);
     else
-      dma16_at(rs, off0, (int)(woff + step), base, step);
+      dma16_at(rs, off[i], (int)woff, base, kAttnWaves * i * 1024);
   }
 }
 
@@ -340,13 +330,20 @@ void attn_kernel(AttnArgs a) {
     const int row0 = qblk * kAttnBlockM + wave * kAttnRowsPerWave;
     const bool active = __builtin_amdgcn_readfirstlane(row0 < s.n_q ? 1 : 0) != 0;   // wave-uniform
 
-    // Loop-invariant lane offsets (bytes) of this wave's first K and V block
-    // of a window (block `wave`); its later blocks follow at a fixed stride.
-    constexpr int CPR = HD / 8;                     // 16-byte chunks per key row
-    const int key0 = wave * (1024 / (2 * HD)) + lane / CPR;
-    const int koff = (key0 * HD + ((lane % CPR) ^ kswz<HD>(key0)) * 8) * 2;
+    // Loop-invariant lane offsets (bytes) of the window loads.
+    int koff[T::K_PER_WAVE], voff[T::V_PER_WAVE];
+#pragma unroll
+    for (int i = 0; i < T::K_PER_WAVE; ++i) {
+      constexpr int CPR = HD / 8;                   // 16-byte chunks per key row
+      const int key = (wave + kAttnWaves * i) * (1024 / (2 * HD)) + lane / CPR;
+      koff[i] = (key * HD + ((lane % CPR) ^ kswz<HD>(key)) * 8) * 2;
+    }
     const int sigma = (j32 & 3) | (((j32 >> 3) & 3) << 2) | (((j32 >> 2) & 1) << 4);
-    const int voff = ((wave / T::HB) * 16 * HD + ((wave % T::HB) * 32 + sigma) * 16 + g * 8) * 2;
+#pragma unroll
+    for (int i = 0; i < T::V_PER_WAVE; ++i) {
+      const int b = wave + kAttnWaves * i;
+      voff[i] = ((b / T::HB) * 16 * HD + ((b % T::HB) * 32 + sigma) * 16 + g * 8) * 2;
+    }
     // QK operand reads: lane (g, rho) wants key 32kb + perm_k(rho), chunk 2kc+g;
     // byte offsets within the K tile for kb = 0 (kb adds 64*HD).
     int kroff[T::KC];
@@ -359,16 +356,16 @@ void attn_kernel(AttnArgs a) {
 
     // Prologue: K(0), V(0), K(1), V(1), K(2), V(2), K(3).
     const Window w0 = win(0);
-    load_tile<HD, true, T::K_PER_WAVE>(rk, w0.start, kbuf(0), koff, wave);
-    load_tile<HD, true, T::V_PER_WAVE>(rv, w0.start, vbuf(0), voff, wave);
+    load_tile<HD, true>(rk, w0.start, kbuf(0), koff, wave);
+    load_tile<HD, true>(rv, w0.start, vbuf(0), voff, wave);
 #pragma unroll
     for (int t = 1; t < 3; ++t) {
       if (t < nw) {
-        load_tile<HD, true, T::K_PER_WAVE>(rk, w0.start + t * kAttnWindow, kbuf(t), koff, wave);
-        load_tile<HD, true, T::V_PER_WAVE>(rv, w0.start + t * kAttnWindow, vbuf(t), voff, wave);
+        load_tile<HD, true>(rk, w0.start + t * kAttnWindow, kbuf(t), koff, wave);
+        load_tile<HD, true>(rv, w0.start + t * kAttnWindow, vbuf(t), voff, wave);
       }
     }
-    if (nw > 3) load_tile<HD, true, T::K_PER_WAVE>(rk, w0.start + 3 * kAttnWindow, kbuf(3), koff, wave);
+    if (nw > 3) load_tile<HD, true>(rk, w0.start + 3 * kAttnWindow, kbuf(3), koff, wave);
 
     // Q^T operand: lane (j, g) holds query row0+j, features 16kc+8g..+7.  The
     // address comes from an opaque copy of the lane index, so that nothing
@@ -452,8 +449,8 @@ void attn_kernel(AttnArgs a) {
         wait_loads_and_barrier<2 * T::V_PER_WAVE + T::K_PER_WAVE>();
         // K(j+4) -> the buffer of K(j) (read by QK(j) in step j-1);
         // V(j+3) -> the buffer of V(j-1) (read by P*V(j-1)).
-        load_tile<HD, false, T::K_PER_WAVE>(rk, sp.start0 + (j + 4) * kAttnWindow, kbuf(stage), koff, wave);
-        load_tile<HD, false, T::V_PER_WAVE>(rv, sp.start0 + (j + 3) * kAttnWindow, vbuf(st3), voff, wave);
+        load_tile<HD, false>(rk, sp.start0 + (j + 4) * kAttnWindow, kbuf(stage), koff, wave);
+        load_tile<HD, false>(rv, sp.start0 + (j + 3) * kAttnWindow, vbuf(st3), voff, wave);
       } else {
         if (j + 3 < nw)
           wait_loads_and_sync<2 * T::V_PER_WAVE + T::K_PER_WAVE>();
@@ -471,9 +468,9 @@ void attn_kernel(AttnArgs a) {
           }
         }
         if (j + 4 < nw)
-          load_tile<HD, true, T::K_PER_WAVE>(rk, sp.start0 + (j + 4) * kAttnWindow, kbuf(stage), koff, wave);
+          load_tile<HD, true>(rk, sp.start0 + (j + 4) * kAttnWindow, kbuf(stage), koff, wave);
         if (j + 3 < nw)
-          load_tile<HD, true, T::V_PER_WAVE>(rv, sp.start0 + (j + 3) * kAttnWindow, vbuf(st3), voff, wave);
+          load_tile<HD, true>(rv, sp.start0 + (j + 3) * kAttnWindow, vbuf(st3), voff, wave);
       }
       if (active) {
         // One step is NQK + NPV MFMA slots, issued in this order: the QK
