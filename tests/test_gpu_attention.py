@@ -54,6 +54,16 @@ def test_attention_matches_oracle(case):
     assert_close(got, ref, f"O {case}")
 
 
+@pytest.mark.parametrize("H", [3, 20])
+def test_attention_head_aligned_groups(H):
+    # A full, wrapped 16,384-key ring and 300 queries (two query blocks): the
+    # default planner takes a multiple of the head count (96 groups for 3
+    # heads, 120 for 20), so group boundaries fall on lane boundaries and on
+    # window boundaries inside lanes; every row of every head is compared.
+    got, ref = _attn_case(H, 128, 16384, 16384, 5000, 300, seed=11 + H)
+    assert_close(got, ref, f"O H={H}")
+
+
 @pytest.mark.parametrize("split", [1, 2, 3, 7])
 def test_attention_key_splits_agree(split):
     got, ref = _attn_case(2, 128, 4096, 3000, 100, 100, seed=5, split=split)
