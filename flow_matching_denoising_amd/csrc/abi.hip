@@ -169,6 +169,14 @@ ZRange z_range(const float* z, int64_t n_q, int d, int idx) {
 // ---------------------------------------------------------------------------
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// Whether the attention reads a step's unit keys where the caller keeps them
+// ([n][H][hd], one head's keys every H*hd elements) instead of a staged
+// [H][npad][hd] copy: when they are given (not produced by the Q/K/V
+// projection) and their bytes fit the kernels' 32-bit buffer offsets.
+bool unit_keys_in_place(const void* k_u, int n_q, int d) {
+  return k_u != nullptr && (int64_t)n_q * d * 2 < ((int64_t)1 << 31);
+}
+
 struct SessPlan {
   int n_q, npad;
   int seg_lo[2], seg_hi[2];
@@ -412,14 +420,25 @@ int enqueue_steps(const fmd_unit_step* units, int n, const std::vector<SessPlan>
       bf16* o = o_out ? o_out + o_row * d : reinterpret_cast<bf16*>(ws + p.off_o);
       o_row += p.n_q;
 
+      const bool k_in_place = unit_keys_in_place(u.k_u, p.n_q, d);
       // A session without transpose work gets an empty range at the current end.
-      va.s[k] = VtSess{static_cast<const bf16*>(u.k_u), static_cast<const bf16*>(u.v_u), kt, vt,
-                       p.n_q, p.npad / 16, va.items, 0};
+      va.s[k] = VtSess{static_cast<const bf16*>(u.k_u), static_cast<const bf16*>(u.v_u),
+                       k_in_place ? nullptr : kt, vt, p.n_q, p.npad / 16, va.items, 0};
       if (!second && !kv_staged) va.items += H * ((p.npad / 16 + kVtBlocks - 1) / kVtBlocks);
 
       AttnSess& as = aa.s[k];
       as.q = static_cast<const bf16*>(u.q);
-      as.kt_u = kt;
+      if (k_in_place) {
+        as.kt_u = static_cast<const bf16*>(u.k_u);
+        as.ku_head = hd;
+        as.ku_stride = d;
+        as.ku_bytes = (int32_t)(((int64_t)(p.n_q - 1) * d + hd) * 2);
+      } else {
+        as.kt_u = kt;
+        as.ku_head = (int64_t)p.npad * hd;
+        as.ku_stride = hd;
+        as.ku_bytes = p.npad * hd * 2;
+      }
       as.vt_u = vt;
       as.ring_k = static_cast<const bf16*>(c->k);
       as.ring_v = static_cast<const bf16*>(c->v);
@@ -767,9 +786,13 @@ static int enqueue_unit_staging(const fmd_unit_io* ss, int n, int n_steps,
     for (int i = 0; i < n; ++i) {
       const SessPlan& p = plans[i];
       const int64_t off = (int64_t)s * ss[i].step_stride_elems;
+      // Keys the attention reads in place (the same test as enqueue_steps')
+      // are not copied.
+      const bool k_in_place = unit_keys_in_place(ss[i].k_u, p.n_q, H * hd);
       all.push_back(VtSess{static_cast<const bf16*>(ss[i].k_u) + off,
                            static_cast<const bf16*>(ss[i].v_u) + off,
-                           reinterpret_cast<bf16*>(ws + p.off_kt + s * p.kv_stride),
+                           k_in_place ? nullptr
+                                      : reinterpret_cast<bf16*>(ws + p.off_kt + s * p.kv_stride),
                            reinterpret_cast<bf16*>(ws + p.off_vt + s * p.kv_stride), p.n_q,
                            p.npad / 16, 0, 0});
     }

@@ -116,10 +116,12 @@ __device__ __forceinline__ Window window_of(const Span& sp, int j) {
 
 // Window loads go global -> LDS through buffer resources (MUBUF loads with
 // the lds bit): one resource per head and key segment, whose size is the
-// segment's storage (cap or npad keys), so that a lane whose range-checked
-// offset falls past it reads zeros instead of faulting.  In both key layouts
-// key k sits at byte 2*HD*k of the segment (K: [keys][HD]; V:
-// [keys/16][HD][16]).  The hardware puts lane i's 16 bytes at M0 + 16*i.
+// segment's storage (cap or npad keys, or up to the last unit key), so that a
+// lane whose range-checked offset falls past it reads zeros instead of
+// faulting.  Key k of a segment sits at byte 2*HD*k of the ring layouts (K:
+// [keys][HD]; V: [keys/16][HD][16]) and at byte 2*H*HD*k of unit keys read
+// where the caller keeps them ([n][H][HD]); `row_bytes` is that key stride.
+// The hardware puts lane i's 16 bytes at M0 + 16*i.
 //
 // The load is issued from inline assembly on purpose: it has no register
 // outputs, and the compiler, which cannot tell one LDS stage buffer from
@@ -140,12 +142,12 @@ __device__ __forceinline__ Window window_of(const Span& sp, int j) {
 // the others pass it as the scalar offset.  Scores of keys outside [lo, hi)
 // are masked and their values zeroed in LDS before use.
 // Offsets are 32-bit unsigned byte counts: a window that starts below the
-// segment's end (start * HD * 2 < 2^31) can reach up to 16 KiB past it, which
-// the range check turns into zeros.
+// segment's end (start * row_bytes < 2^31) can reach up to 64 keys past it,
+// which the range check turns into zeros.
 template <int HD, bool CHECKED, int N>
-__device__ __forceinline__ void load_tile(const i32x4& rs, int start, char* dst,
+__device__ __forceinline__ void load_tile(const i32x4& rs, int start, int row_bytes, char* dst,
                                           const int (&off)[N], int wave) {
-  const uint32_t woff = (uint32_t)start * (HD * 2);
+  const uint32_t woff = (uint32_t)start * (uint32_t)row_bytes;
   // LDS destination: one wave-uniform base (the tile plus this wave's first
   // 1 KiB block) and a constant offset per instruction.
   const uint32_t base =
@@ -300,7 +302,7 @@ void attn_kernel(AttnArgs a) {
     Span sp;
     i32x4 rk, rv;
     if (sg == 2) {
-      rk = make_rsrc(s.kt_u + (int64_t)h * s.npad * HD, s.npad * HD * 2);
+      rk = make_rsrc(s.kt_u + h * s.ku_head, s.ku_bytes);
       rv = make_rsrc(s.vt_u + (int64_t)h * s.npad * HD, s.npad * HD * 2);
       sp.lo = 0;
       sp.hi = s.n_q;
@@ -330,13 +332,15 @@ void attn_kernel(AttnArgs a) {
     const int row0 = qblk * kAttnBlockM + wave * kAttnRowsPerWave;
     const bool active = __builtin_amdgcn_readfirstlane(row0 < s.n_q ? 1 : 0) != 0;   // wave-uniform
 
-    // Loop-invariant lane offsets (bytes) of the window loads.
+    // Loop-invariant lane offsets (bytes) of the window loads; krow: the
+    // segment's elements from one key to the next.
+    const int krow = sg == 2 ? s.ku_stride : HD;
     int koff[T::K_PER_WAVE], voff[T::V_PER_WAVE];
 #pragma unroll
     for (int i = 0; i < T::K_PER_WAVE; ++i) {
       constexpr int CPR = HD / 8;                   // 16-byte chunks per key row
       const int key = (wave + kAttnWaves * i) * (1024 / (2 * HD)) + lane / CPR;
-      koff[i] = (key * HD + ((lane % CPR) ^ kswz<HD>(key)) * 8) * 2;
+      koff[i] = (key * krow + ((lane % CPR) ^ kswz<HD>(key)) * 8) * 2;
     }
     const int sigma = (j32 & 3) | (((j32 >> 3) & 3) << 2) | (((j32 >> 2) & 1) << 4);
 #pragma unroll
@@ -356,16 +360,17 @@ void attn_kernel(AttnArgs a) {
 
     // Prologue: K(0), V(0), K(1), V(1), K(2), V(2), K(3).
     const Window w0 = win(0);
-    load_tile<HD, true>(rk, w0.start, kbuf(0), koff, wave);
-    load_tile<HD, true>(rv, w0.start, vbuf(0), voff, wave);
+    load_tile<HD, true>(rk, w0.start, krow * 2, kbuf(0), koff, wave);
+    load_tile<HD, true>(rv, w0.start, HD * 2, vbuf(0), voff, wave);
 #pragma unroll
     for (int t = 1; t < 3; ++t) {
       if (t < nw) {
-        load_tile<HD, true>(rk, w0.start + t * kAttnWindow, kbuf(t), koff, wave);
-        load_tile<HD, true>(rv, w0.start + t * kAttnWindow, vbuf(t), voff, wave);
+        load_tile<HD, true>(rk, w0.start + t * kAttnWindow, krow * 2, kbuf(t), koff, wave);
+        load_tile<HD, true>(rv, w0.start + t * kAttnWindow, HD * 2, vbuf(t), voff, wave);
       }
     }
-    if (nw > 3) load_tile<HD, true>(rk, w0.start + 3 * kAttnWindow, kbuf(3), koff, wave);
+    if (nw > 3)
+      load_tile<HD, true>(rk, w0.start + 3 * kAttnWindow, krow * 2, kbuf(3), koff, wave);
 
     // Q^T operand: lane (j, g) holds query row0+j, features 16kc+8g..+7.  The
     // address comes from an opaque copy of the lane index, so that nothing
@@ -449,8 +454,10 @@ void attn_kernel(AttnArgs a) {
         wait_loads_and_barrier<2 * T::V_PER_WAVE + T::K_PER_WAVE>();
         // K(j+4) -> the buffer of K(j) (read by QK(j) in step j-1);
         // V(j+3) -> the buffer of V(j-1) (read by P*V(j-1)).
-        load_tile<HD, false>(rk, sp.start0 + (j + 4) * kAttnWindow, kbuf(stage), koff, wave);
-        load_tile<HD, false>(rv, sp.start0 + (j + 3) * kAttnWindow, vbuf(st3), voff, wave);
+        load_tile<HD, false>(rk, sp.start0 + (j + 4) * kAttnWindow, krow * 2, kbuf(stage), koff,
+                             wave);
+        load_tile<HD, false>(rv, sp.start0 + (j + 3) * kAttnWindow, HD * 2, vbuf(st3), voff,
+                             wave);
       } else {
         if (j + 3 < nw)
           wait_loads_and_sync<2 * T::V_PER_WAVE + T::K_PER_WAVE>();
@@ -468,9 +475,11 @@ void attn_kernel(AttnArgs a) {
           }
         }
         if (j + 4 < nw)
-          load_tile<HD, true>(rk, sp.start0 + (j + 4) * kAttnWindow, kbuf(stage), koff, wave);
+          load_tile<HD, true>(rk, sp.start0 + (j + 4) * kAttnWindow, krow * 2, kbuf(stage), koff,
+                              wave);
         if (j + 3 < nw)
-          load_tile<HD, true>(rv, sp.start0 + (j + 3) * kAttnWindow, vbuf(st3), voff, wave);
+          load_tile<HD, true>(rv, sp.start0 + (j + 3) * kAttnWindow, HD * 2, vbuf(st3), voff,
+                              wave);
       }
       if (active) {
         // One step is NQK + NPV MFMA slots, issued in this order: the QK

@@ -150,7 +150,7 @@ constexpr int kVtBlocks = 4;   // 16-token blocks per work-group of the unit K/V
 struct VtSess {
   const bf16* k;    // [n][H][hd]   the unit's keys
   const bf16* v;    // [n][H][hd]   the unit's values
-  bf16* kt;         // [H][npad][hd]           keys, head-major, zero past n
+  bf16* kt;         // [H][npad][hd]           keys, head-major, zero past n (nullptr: values only)
   bf16* vt;         // [H][npad/16][hd][16]   values, 16-key blocks, zero past n
   int32_t n;
   int32_t nblk;     // npad/16
@@ -166,8 +166,11 @@ struct VtArgs {
 
 struct AttnSess {
   const bf16* q;      // [n_q][H][hd]
-  const bf16* kt_u;   // [H][npad][hd]           (workspace copy of the unit's keys)
+  const bf16* kt_u;   // the unit's keys: [H][npad][hd] (a staged copy) or [n_q][H][hd] (as given)
   const bf16* vt_u;   // [H][npad/16][hd][16]   (workspace copy of the unit's values)
+  int64_t ku_head;    // elements from one head's unit keys to the next's (npad*hd or hd)
+  int32_t ku_stride;  // elements from one unit key to the next (hd or H*hd)
+  int32_t ku_bytes;   // bytes of one head's unit keys from its first (its buffer range)
   const bf16* ring_k; // [H][cap][hd]
   const bf16* ring_v; // [H][cap/16][hd][16]
   bf16* o;            // [n_q][H][hd]            (lanes that lie in one group)

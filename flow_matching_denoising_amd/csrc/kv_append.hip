@@ -84,7 +84,9 @@ __global__ __launch_bounds__(2 * HD) void append_kernel(AppendArgs a) {
 
 // The unit's own keys and values, staged in the ring's layouts so that the
 // attention kernel streams every key segment the same way:
-//   keys   [n][H][hd] -> [H][npad][hd]
+//   keys   [n][H][hd] -> [H][npad][hd]          (skipped when kt is null: the
+//                                               attention then reads the keys
+//                                               where they are)
 //   values [n][H][hd] -> [H][npad/16][hd][16]
 // (npad = n rounded up to 16; rows past n are zero).  One work-group per
 // (session, head, kVtBlocks 16-token blocks); every load of a thread is
@@ -110,13 +112,14 @@ __global__ __launch_bounds__(256) void vt_kernel(VtArgs a) {
   const int nb = min(kVtBlocks, s.nblk - blk0);
   const int H = a.H;
   const int part = threadIdx.x % PARTS;
+  const bool keys = s.kt != nullptr;       // uniform: stage the keys as well as the values
   u32x4 kx[PASSES], vx[PASSES];
 #pragma unroll
   for (int p = 0; p < PASSES; ++p) {
     const int tok = blk0 * 16 + p * ROWS + threadIdx.x / PARTS;
     kx[p] = vx[p] = u32x4{0u, 0u, 0u, 0u};
     if (tok < s.n) {
-      kx[p] = ld16(s.k + ((int64_t)tok * H + h) * HD + part * 8);
+      if (keys) kx[p] = ld16(s.k + ((int64_t)tok * H + h) * HD + part * 8);
       vx[p] = ld16(s.v + ((int64_t)tok * H + h) * HD + part * 8);
     }
   }
@@ -124,7 +127,7 @@ __global__ __launch_bounds__(256) void vt_kernel(VtArgs a) {
   for (int p = 0; p < PASSES; ++p) {
     const int r = p * ROWS + threadIdx.x / PARTS;
     if (r < nb * 16) {
-      st16(s.kt + ((int64_t)h * s.nblk * 16 + blk0 * 16 + r) * HD + part * 8, kx[p]);
+      if (keys) st16(s.kt + ((int64_t)h * s.nblk * 16 + blk0 * 16 + r) * HD + part * 8, kx[p]);
       st16(&tile[r][part * 8], vx[p]);
     }
   }
