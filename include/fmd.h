@@ -189,9 +189,11 @@ typedef struct fmd_unit_io {
 } fmd_unit_io;
 
 /* Workspace bytes fmd_denoise_unit needs for n_steps steps (pure host
- * arithmetic).  The unit keys and values of all n_steps steps are staged in
- * the attention's layouts by one launch before the first step, so the
- * workspace holds n_steps copies of them (one when every session's
+ * arithmetic).  The unit values of all n_steps steps are staged in the
+ * attention's 16-key blocked layout by one launch before the first step; the
+ * attention reads the unit keys where the caller keeps them (they are staged
+ * too, in [H][npad][hd], only when n_q * d * 2 bytes reach 2^31).  The
+ * workspace holds n_steps copies of room for both (one when every session's
  * step_stride_elems is 0).  Errors: as fmd_denoise_unit's validation. */
 int fmd_unit_workspace_bytes(const fmd_unit_io* sessions, int32_t n_sessions, int32_t n_steps,
                              size_t* out_bytes);
@@ -378,7 +380,7 @@ const char* fmd_last_error(void);
 /* Kernel classes that fmd_profile_* report on. */
 enum {
   FMD_KERNEL_APPEND = 0,    /* ring append */
-  FMD_KERNEL_VT = 1,        /* staging of the unit's keys/values in the ring layouts */
+  FMD_KERNEL_VT = 1,        /* staging of the unit's values (and keys, if needed) in the ring layouts */
   FMD_KERNEL_ATTN = 2,      /* attention main kernel */
   FMD_KERNEL_COMBINE = 3,   /* merge of the pieces of cut (head, session) lanes */
   FMD_KERNEL_PROJ = 4,      /* projection GEMM with the Euler update */
