@@ -31,10 +31,11 @@
  *  - `stream` is a hipStream_t (NULL = the default stream).  Calls enqueue
  *    work and return; results are valid once the stream reaches that point.
  *  - Every argument is validated before anything is enqueued.  A non-zero
- *    return means no kernel was launched and no host state (a cache's
- *    len_tokens/head_tokens) changed.  fmd_last_error() then describes the
- *    first failed check.  Errors of an already-enqueued launch are reported
- *    as FMD_E_HIP.
+ *    return other than FMD_E_HIP means no kernel was launched and no host
+ *    state (a cache's len_tokens/head_tokens) changed.  fmd_last_error() then
+ *    describes the first failed check.  FMD_E_HIP means the HIP runtime
+ *    refused a launch: the launches before it stay enqueued, and a ring
+ *    whose append was among them has advanced (the others are unchanged).
  *  - All tensor pointers must be 16-byte aligned (FMD_E_ALIGN otherwise).
  *  - bf16 = IEEE binary32's upper 16 bits; fp32 = IEEE binary32.
  *  - Calls on different caches are independent; one cache must not be used
