@@ -111,6 +111,14 @@ constexpr int vmcnt_imm(int vm, int lgkm) {
   return (vm & 15) | ((vm >> 4) << 14) | (7 << 4) | (lgkm << 8);
 }
 
+// s_barrier with no fence of its own: the caller has already waited (with
+// s_waitcnt) for whatever the other waves must see.
+__device__ __forceinline__ void bare_barrier() {
+  __asm__ volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  __asm__ volatile("" ::: "memory");
+}
+
 // Wait until at most N of this wave's loads are outstanding, then barrier.
 template <int N>
 __device__ __forceinline__ void wait_loads_and_sync() {

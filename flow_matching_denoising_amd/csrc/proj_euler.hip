@@ -8,22 +8,30 @@
 // velocity network is reduced here to one dense output projection of the
 // attention output; sampling runs tau from 1 to 0 with positive step sizes h.
 //
-// Tile 160 rows x 128 output features, k step 64, 4 waves (one per SIMD);
-// wave w owns output features 32w..32w+31 of the tile for all 160 rows (five
-// MFMA 32x32 accumulators).  160-row tiles split a 928-row unit into 6 row
-// tiles, so a 5120-wide projection is 240 work-groups: one balanced round on
-// 256 CUs (256-row tiles would leave 96 CUs idle).  O and W rows are both
-// k-contiguous ([n_q][d] and [d_out][d_in]).  Operands go global -> LDS with
-// MUBUF loads (lds bit), one 1 KiB block (8 rows x 64 k) per wave
-// instruction, each row read whole (128 contiguous bytes).  Inside a block,
-// the 16-byte chunk c of row r is stored at chunk position c ^ ((r >> 1) & 7),
-// which keeps the ds_read_b128 operand reads (16 lanes = 16 rows of one
-// chunk per LDS cycle) free of bank conflicts.  The buffer resources cover
-// exactly the tile's valid rows, so rows past n_q (or past d for W) read as
-// zeros.  Four LDS stages (144 KiB) keep three k steps of loads in flight:
-// the operands come mostly from other work-groups' misses in L2 and the
-// Infinity Cache, so the bytes a CU has in flight, not the L2 bandwidth,
-// set its load rate.
+// Tile 160 rows x 128 output features, k step 64, eight waves in two roles.
+// Four MFMA waves (one per SIMD): wave w owns output features 32w..32w+31 of
+// the tile for all 160 rows (five MFMA 32x32 accumulators) and only reads
+// its operands from LDS.  Four DMA waves (one per SIMD) issue every global
+// load and finish the epilogue: with one MFMA wave per SIMD, a wave that also
+// issued the operand loads would stall its MFMA stream at each load issue,
+// with nothing else on the SIMD to fill the gap.  160-row tiles split a
+// 928-row unit into 6 row tiles, so a 5120-wide projection is 240
+// work-groups: one balanced round on 256 CUs (256-row tiles would leave 96
+// CUs idle).  O and W rows are both k-contiguous ([n_q][d] and
+// [d_out][d_in]).  Operands go global -> LDS with MUBUF loads (lds bit), one
+// 1 KiB block (8 rows x 64 k) per wave instruction, each row read whole (128
+// contiguous bytes).  Inside a block, the 16-byte chunk c of row r is stored
+// at chunk position c ^ ((r >> 1) & 7), which keeps the ds_read_b128 operand
+// reads (16 lanes = 16 rows of one chunk per LDS cycle) free of bank
+// conflicts.  The buffer resources cover exactly the tile's valid rows, so
+// rows past n_q (or past d for W) read as zeros.  Four LDS stages (144 KiB)
+// keep three k steps of loads in flight.
+// Epilogue: the z (and residual) values of the tile are loaded by the DMA
+// waves in chunks spread over the k loop, into registers laid out like the
+// MFMA waves' accumulators, so that neither their latency nor a burst of
+// every work-group reading them at once falls at the end; after the loop the
+// MFMA waves hand their accumulators over through LDS and the DMA waves apply
+// the update and store.
 // Item order inside a session: k part major, then output-feature tile, then
 // row tile, so the row tiles that share one slab of W are adjacent and run on
 // the same XCD.  With k parts (small units), each work-group multiplies one
@@ -38,24 +46,33 @@ namespace {
 constexpr int BM = kProjTile;                       // 160 rows
 constexpr int BN = kProjTileN;                      // 128 output features
 constexpr int BK = kProjBK;
-constexpr int WAVES = 4;
+constexpr int WAVES = 4;                            // MFMA waves, one per SIMD
+constexpr int DWAVES = 4;                           // DMA waves, one per SIMD
+constexpr int THREADS = (WAVES + DWAVES) * 64;
 constexpr int MT = BM / 32;                         // 5 row tiles of 32
 constexpr int STAGES = 4;
 constexpr int A_BLOCKS = BM / 8;                    // 20 blocks of 8 rows x 64 k
 constexpr int B_BLOCKS = BN / 8;                    // 16
 constexpr int STAGE_BYTES = (A_BLOCKS + B_BLOCKS) * 1024;
-constexpr int LOADS_PER_WAVE = (A_BLOCKS + B_BLOCKS) / WAVES;   // 9
+constexpr int LOADS_PER_WAVE = (A_BLOCKS + B_BLOCKS) / DWAVES;   // 9
 constexpr int LDS_BYTES = STAGES * STAGE_BYTES;     // 144 KiB
-static_assert(A_BLOCKS % WAVES == 0 && B_BLOCKS % WAVES == 0, "loads must split evenly over waves");
+constexpr int ACC_WAVE_BYTES = MT * 16 * 64 * 4;    // one MFMA wave's accumulators
+static_assert(A_BLOCKS % DWAVES == 0 && B_BLOCKS % DWAVES == 0, "loads must split evenly over waves");
 static_assert(BN == 32 * WAVES, "one 32-feature column tile per wave");
+static_assert(WAVES * ACC_WAVE_BYTES <= LDS_BYTES, "the accumulator hand-over fits in LDS");
 static_assert((STAGES & (STAGES - 1)) == 0, "the stage index wraps with a mask");
+// Epilogue chunk c (16 values per lane: row tile c of z, then row tile c - MT
+// of the residual) is loaded in k step kZ0 + kZStep * c, after that step's
+// operand loads; chunks issued in the three previous k steps are still in
+// flight at a k step's wait, which counts them.
+constexpr int kZ0 = 4, kZStep = 6, kZLoads = 16;
 
 }  // namespace
 
 constexpr int kProjPartial = -1;   // epilogue: store the fp32 partial tile
 
 template <int MODE>
-__global__ __launch_bounds__(WAVES * 64) void proj_kernel(ProjArgs a) {
+__global__ __launch_bounds__(THREADS) void proj_kernel(ProjArgs a) {
   extern __shared__ __attribute__((aligned(1024))) char lds[];
   const int item = xcd_remap(blockIdx.x, a.items);
   int si = 0;
@@ -79,36 +96,156 @@ __global__ __launch_bounds__(WAVES * 64) void proj_kernel(ProjArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int r = lane & 31, g = lane >> 5;
-
-  // The tile's rows of O and W; rows past n_q (past d) read as zeros.
   const int n_out = a.n_out;
-  const i32x4 ra = make_rsrc(s.a + (int64_t)m0 * d, min(BM, n_q - m0) * d * 2);
-  const i32x4 rb = make_rsrc(a.w + (int64_t)n0 * d, min(BN, n_out - n0) * d * 2);
-
-  // Loop-invariant lane offsets (bytes): wave w fills 1 KiB blocks w, w+4, ...
-  // (blocks 0..19: A, 20..35: B); block b holds 8 consecutive rows of its
-  // operand, lane i -> row i/8, k chunk (i%8) ^ swizzle(row).
-  int voff[LOADS_PER_WAVE];
-#pragma unroll
-  for (int i = 0; i < LOADS_PER_WAVE; ++i) {
-    const int b = wave + WAVES * i;
-    const int rt = (i < A_BLOCKS / WAVES ? b : b - A_BLOCKS) * 8 + (lane >> 3);
-    const int chunk = (lane & 7) ^ ((rt >> 1) & 7);
-    voff[i] = rt * d * 2 + chunk * 16;
-  }
   const int nk_all = d / BK;
   const int kb = part * nk_all / a.splits;
   const int nk = (part + 1) * nk_all / a.splits - kb;      // this work-group's k steps
-  auto load_stage = [&](int kt, int st) __attribute__((always_inline)) {
-    kt += kb;
-    char* base = lds + st * STAGE_BYTES;
+  const bool full = m0 + BM <= n_q;                // uniform
+  // C layout of a 32x32 accumulator: lane (col r, group g), register q ->
+  // row 8*(q/4) + 4*g + q%4 of the tile; row tile i starts at row m0 + 32i.
+  auto row = [&](int i, int q) { return m0 + i * 32 + (q >> 2) * 8 + g * 4 + (q & 3); };
+  // Where MFMA wave w's accumulator registers 4j..4j+3 of row tile i go for
+  // the hand-over (lane-contiguous 16-byte slots).
+  auto acc_slot = [&](int w, int i, int j) {
+    return lds + w * ACC_WAVE_BYTES + ((i * 4 + j) * 64 + lane) * 16;
+  };
+  constexpr bool kHandOver = MODE != kProjPartial;
+
+  if (wave >= WAVES) {
+    // ---- DMA wave dw: operand loads, epilogue loads and the epilogue. ----
+    const int dw = wave - WAVES;
+    // The tile's rows of O and W; rows past n_q (past d) read as zeros.
+    const i32x4 ra = make_rsrc(s.a + (int64_t)m0 * d, min(BM, n_q - m0) * d * 2);
+    const i32x4 rb = make_rsrc(a.w + (int64_t)n0 * d, min(BN, n_out - n0) * d * 2);
+    // Loop-invariant lane offsets (bytes): wave dw fills 1 KiB blocks dw,
+    // dw+4, ... (blocks 0..19: A, 20..35: B); block b holds 8 consecutive
+    // rows of its operand, lane i -> row i/8, k chunk (i%8) ^ swizzle(row).
+    int voff[LOADS_PER_WAVE];
 #pragma unroll
     for (int i = 0; i < LOADS_PER_WAVE; ++i) {
-      // Blocks wave + 4i: i < 5 are A blocks for every wave.
-      dma16(i < A_BLOCKS / WAVES ? ra : rb, voff[i], kt * BK * 2,
-            base + (wave + WAVES * i) * 1024);
+      const int b = dw + DWAVES * i;
+      const int rt = (i < A_BLOCKS / DWAVES ? b : b - A_BLOCKS) * 8 + (lane >> 3);
+      const int chunk = (lane & 7) ^ ((rt >> 1) & 7);
+      voff[i] = rt * d * 2 + chunk * 16;
     }
-  };
+    auto load_stage = [&](int kt, int st) __attribute__((always_inline)) {
+      kt += kb;
+      char* base = lds + st * STAGE_BYTES;
+#pragma unroll
+      for (int i = 0; i < LOADS_PER_WAVE; ++i)
+        dma16(i < A_BLOCKS / DWAVES ? ra : rb, voff[i], kt * BK * 2,
+              base + (dw + DWAVES * i) * 1024);
+    };
+    // Epilogue inputs of column n (MFMA wave dw's lane layout): z, and for a
+    // layer the residual.  Buffer loads over the tile's valid rows: every
+    // chunk issues exactly kZLoads loads whatever the row and column bounds,
+    // which the k loop's wait counts rely on (out-of-range lanes read zeros
+    // or values that are never stored).
+    constexpr int NZ = MODE == kProjEuler ? MT : (kHandOver ? 2 * MT : 0);
+    const int n = n0 + dw * 32 + r;
+    const int rows_here = min(BM, n_q - m0);
+    const __amdgpu_buffer_rsrc_t rz =
+        __builtin_amdgcn_make_buffer_rsrc(z + (int64_t)m0 * d, 0, rows_here * d * 4, kRsrcWord3);
+    const __amdgpu_buffer_rsrc_t rr = __builtin_amdgcn_make_buffer_rsrc(
+        (MODE == kProjLayer || MODE == kProjLayerLast) ? s.r + (int64_t)m0 * d : z, 0,
+        rows_here * d * 4, kRsrcWord3);
+    float ev[NZ > 0 ? NZ : 1][16];
+    auto load_chunk = [&](int c) __attribute__((always_inline)) {
+      const int i = c < MT ? c : c - MT;
+#pragma unroll
+      for (int q = 0; q < kZLoads; ++q)
+        ev[c][q] = __builtin_bit_cast(
+            float, __builtin_amdgcn_raw_buffer_load_b32(c < MT ? rz : rr,
+                                                        ((row(i, q) - m0) * d + n) * 4, 0, 0));
+    };
+    const bool spread = NZ > 0 && kZ0 + kZStep * (NZ - 1) + 8 <= nk;
+
+    load_stage(0, 0);
+    if (nk > 1) load_stage(1, 1);
+    if (nk > 2) load_stage(2, 2);
+    if (nk > 3) load_stage(3, 3);
+    if (nk > 3)
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(3 * LOADS_PER_WAVE, 15));
+    else if (nk > 2)
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * LOADS_PER_WAVE, 15));
+    else if (nk > 1)
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(LOADS_PER_WAVE, 15));
+    else
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0, 15));
+    bare_barrier();                                // k step 0 has landed
+    for (int kt = 0; kt + 1 < nk; ++kt) {
+      // k step kt+1 must have landed before the MFMA waves pass the barrier
+      // that ends their reads of k step kt's buffer; that buffer then takes
+      // k step kt+4.  Loads issued after k step kt+1's: k steps kt+2 and
+      // kt+3, and an epilogue chunk if one went out in k steps kt-3..kt-1
+      // (never in the last three waits: the last chunk goes out at least
+      // eight k steps before the end).
+      const int t = kt - kZ0;
+      const bool recent = spread && t >= 1 && t <= kZStep * (NZ - 1) + 3 && t % kZStep >= 1 &&
+                          t % kZStep <= 3;
+      if (kt + 3 < nk) {
+        if (recent)
+          __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * LOADS_PER_WAVE + kZLoads, 15));
+        else
+          __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * LOADS_PER_WAVE, 15));
+      } else if (kt + 2 < nk) {
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(LOADS_PER_WAVE, 15));
+      } else {
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0, 15));
+      }
+      bare_barrier();
+      if (kt + 4 < nk) load_stage(kt + 4, kt & (STAGES - 1));
+      if (spread) {
+#pragma unroll
+        for (int c = 0; c < NZ; ++c)
+          if (kt == kZ0 + kZStep * c) load_chunk(c);
+      }
+    }
+    if constexpr (kHandOver) {
+      if (!spread) {
+#pragma unroll
+        for (int c = 0; c < NZ; ++c) load_chunk(c);
+      }
+      bare_barrier();                              // the MFMA waves are done with the operands
+      bare_barrier();                              // their accumulators are in LDS
+      float* const zc = z + n;
+      bf16* const zbc = s.zb ? s.zb + n : nullptr;
+      float* const rc = (MODE == kProjLayer || MODE == kProjLayerLast) ? s.r + n : nullptr;
+      const bool col_in = n < n_out;
+#pragma unroll
+      for (int i = 0; i < MT; ++i) {
+        f32x4 y4[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) y4[j] = *reinterpret_cast<const f32x4*>(acc_slot(dw, i, j));
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+          const int m = row(i, q);
+          if (!(col_in && (full || m < n_q))) continue;
+          const float y = y4[q >> 2][q & 3];
+          if constexpr (MODE == kProjEuler) {
+            // z[m][n] -= h * y[m][n] (and zb = bf16(z)).
+            const float zn = ev[i][q] - hstep * y;
+            zc[(int64_t)m * d] = zn;
+            if (zbc) zbc[(int64_t)m * d] = (bf16)zn;
+          } else if constexpr (MODE == kProjLayer) {
+            // Residual stream of a layer stack (see kProjLayer).
+            const float rn = ev[MT + i][q] + y;
+            rc[(int64_t)m * d] = rn;
+            if (zbc) zbc[(int64_t)m * d] = (bf16)(ev[i][q] + rn);
+          } else {
+            // The stack's last layer (see kProjLayerLast).
+            const float zn = ev[i][q] - hstep * (ev[MT + i][q] + y);
+            zc[(int64_t)m * d] = zn;
+            rc[(int64_t)m * d] = 0.f;
+            if (zbc) zbc[(int64_t)m * d] = (bf16)zn;
+          }
+        }
+      }
+    }
+    return;
+  }
+
+  // ---- MFMA wave. ----
   // Operand reads: lane (g, r) of a 32-row tile wants row r, k chunk 2kc+g;
   // byte offset within the tile (tile bases are compile-time immediates).
   int roff[4];
@@ -121,9 +258,9 @@ __global__ __launch_bounds__(WAVES * 64) void proj_kernel(ProjArgs a) {
   for (int i = 0; i < MT; ++i) acc[i] = f32x16{};
   // Pipeline: four LDS stages, k step t in buffer t % 4.  The barrier that
   // publishes k step t+1 sits DA slots before the end of k step t, right
-  // after every wave has issued its last read of buffer t: the reads of
+  // after every MFMA wave has issued its last read of buffer t: the reads of
   // k step t+1's first operands then overlap the last MFMAs of k step t, and
-  // the DMA of k step t+4 (into buffer t % 4) is issued after that barrier.
+  // the DMA waves load k step t+4 into buffer t % 4 after that barrier.
   // MFMA slot sl = kc*MT + i multiplies A fragment (kc, i) by B fragment kc;
   // every slot issues the read of the A fragment DA slots ahead (and the B
   // fragment of a k chunk that starts there), continuing into the next k step.
@@ -136,18 +273,7 @@ __global__ __launch_bounds__(WAVES * 64) void proj_kernel(ProjArgs a) {
   auto bread = [&](const char* al, int kc) {
     return *reinterpret_cast<const bf16x8*>(al + A_BLOCKS * 1024 + wave * 4096 + roff[kc]);
   };
-  load_stage(0, 0);
-  if (nk > 1) load_stage(1, 1);
-  if (nk > 2) load_stage(2, 2);
-  if (nk > 3) load_stage(3, 3);
-  if (nk > 3)
-    wait_loads_and_sync<3 * LOADS_PER_WAVE>();
-  else if (nk > 2)
-    wait_loads_and_sync<2 * LOADS_PER_WAVE>();
-  else if (nk > 1)
-    wait_loads_and_sync<LOADS_PER_WAVE>();
-  else
-    wait_loads_and_sync<0>();
+  bare_barrier();                                  // k step 0 has landed
   bf16x8 ar[RA], br[2];
   br[0] = bread(lds, 0);
 #pragma unroll
@@ -162,19 +288,10 @@ __global__ __launch_bounds__(WAVES * 64) void proj_kernel(ProjArgs a) {
 #pragma unroll
     for (int sl = 0; sl < NS; ++sl) {
       if (sl == NS - DA && more) {
-        // This wave's reads of buffer st are all issued; wait for them and
-        // for k step kt+1's DMA (k steps kt+2 and kt+3 may stay in flight),
-        // then barrier.
-        if (kt + 3 < nk)
-          __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * LOADS_PER_WAVE, 0));
-        else if (kt + 2 < nk)
-          __builtin_amdgcn_s_waitcnt(vmcnt_imm(LOADS_PER_WAVE, 0));
-        else
-          __builtin_amdgcn_s_waitcnt(vmcnt_imm(0, 0));
-        __asm__ volatile("" ::: "memory");
-        __syncthreads();
-        __asm__ volatile("" ::: "memory");
-        if (kt + 4 < nk) load_stage(kt + 4, st);
+        // This wave's reads of buffer st are all issued; wait for them, then
+        // barrier (the DMA waves have waited for k step kt+1's loads).
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(63, 0));
+        bare_barrier();
       }
       const int nx = sl + DA;
       if (nx < NS) {
@@ -190,76 +307,28 @@ __global__ __launch_bounds__(WAVES * 64) void proj_kernel(ProjArgs a) {
     st = stn;
   }
 
-  // Epilogue.  C layout: lane (col r, group g), register q -> row
-  // 8*(q/4) + 4*g + q%4 of the 32x32 tile.
-  const int n = n0 + wave * 32 + r;
-  if (n >= n_out) return;
-  const bool full = m0 + BM <= n_q;                // uniform
-  // Every z (and r) value of the lane's 160 rows is loaded before the first
-  // store: the stores to z could alias later loads as far as the compiler
-  // knows, so loads issued per row tile would wait out the memory latency
-  // once per tile.
-  auto row = [&](int i, int q) { return m0 + i * 32 + (q >> 2) * 8 + g * 4 + (q & 3); };
   if constexpr (MODE == kProjPartial) {
+    const int n = n0 + wave * 32 + r;
+    if (n >= n_out) return;
     float* const pc = s.part + (int64_t)part * n_q * d + n;
 #pragma unroll
     for (int i = 0; i < MT; ++i)
 #pragma unroll
       for (int q = 0; q < 16; ++q)
         if (full || row(i, q) < n_q) pc[(int64_t)row(i, q) * d] = acc[i][q];
-  } else if constexpr (MODE == kProjEuler) {
-    // z[m][n] -= h * y[m][n] (and zb = bf16(z)).
-    float* const zc = z + n;
-    bf16* const zbc = s.zb ? s.zb + n : nullptr;
-    float zv[MT][16];
+  } else {
+    // Hand the accumulators to the DMA waves once every MFMA wave is done
+    // reading operands.
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(63, 0));
+    bare_barrier();
 #pragma unroll
     for (int i = 0; i < MT; ++i)
 #pragma unroll
-      for (int q = 0; q < 16; ++q)
-        zv[i][q] = (full || row(i, q) < n_q) ? zc[(int64_t)row(i, q) * d] : 0.f;
-#pragma unroll
-    for (int i = 0; i < MT; ++i)
-#pragma unroll
-      for (int q = 0; q < 16; ++q) {
-        const int m = row(i, q);
-        if (full || m < n_q) {
-          const float zn = zv[i][q] - hstep * acc[i][q];
-          zc[(int64_t)m * d] = zn;
-          if (zbc) zbc[(int64_t)m * d] = (bf16)zn;
-        }
-      }
-  } else if constexpr (MODE == kProjLayer || MODE == kProjLayerLast) {
-    // Residual stream of a layer stack (see kProjLayer / kProjLayerLast).
-    float* const zc = z + n;
-    float* const rc = s.r + n;
-    bf16* const zbc = s.zb ? s.zb + n : nullptr;
-    float zv[MT][16], rv[MT][16];
-#pragma unroll
-    for (int i = 0; i < MT; ++i)
-#pragma unroll
-      for (int q = 0; q < 16; ++q) {
-        const bool in = full || row(i, q) < n_q;
-        zv[i][q] = in ? zc[(int64_t)row(i, q) * d] : 0.f;
-        rv[i][q] = in ? rc[(int64_t)row(i, q) * d] : 0.f;
-      }
-#pragma unroll
-    for (int i = 0; i < MT; ++i)
-#pragma unroll
-      for (int q = 0; q < 16; ++q) {
-        const int m = row(i, q);
-        if (full || m < n_q) {
-          const float rn = rv[i][q] + acc[i][q];
-          if constexpr (MODE == kProjLayer) {
-            rc[(int64_t)m * d] = rn;
-            if (zbc) zbc[(int64_t)m * d] = (bf16)(zv[i][q] + rn);
-          } else {
-            const float zn = zv[i][q] - hstep * rn;
-            zc[(int64_t)m * d] = zn;
-            rc[(int64_t)m * d] = 0.f;
-            if (zbc) zbc[(int64_t)m * d] = (bf16)zn;
-          }
-        }
-      }
+      for (int j = 0; j < 4; ++j)
+        *reinterpret_cast<f32x4*>(acc_slot(wave, i, j)) =
+            f32x4{acc[i][4 * j], acc[i][4 * j + 1], acc[i][4 * j + 2], acc[i][4 * j + 3]};
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(63, 0));
+    bare_barrier();
   }
 }
 
@@ -389,7 +458,7 @@ hipError_t launch_proj(const ProjArgs& a, int mode, hipStream_t st) {
     return e;
   }();
   if (attr_err != hipSuccess) return attr_err;
-  const dim3 grid(a.items), block(WAVES * 64);
+  const dim3 grid(a.items), block(THREADS);
   if (a.splits > 1) mode = kProjPartial;
   switch (mode) {
     case kProjPartial:
