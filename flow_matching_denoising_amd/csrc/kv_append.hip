@@ -90,7 +90,10 @@ __global__ __launch_bounds__(2 * HD) void append_kernel(AppendArgs a) {
 //   values [n][H][hd] -> [H][npad/16][hd][16]
 // (npad = n rounded up to 16; rows past n are zero).  One work-group per
 // (session, head, kVtBlocks 16-token blocks); every load of a thread is
-// issued before its first store.
+// issued before its first store.  The staged copies carry the non-temporal
+// hint: a unit stages every step's values up front, and the attention of a
+// later step reads them long after other traffic has passed through the
+// caches (8.6 -> 8.0 us for one step's 928x40x128 values).
 template <int HD>
 __global__ __launch_bounds__(256) void vt_kernel(VtArgs a) {
   constexpr int PARTS = HD / 8;            // 16-byte parts of one token row
@@ -138,7 +141,7 @@ __global__ __launch_bounds__(256) void vt_kernel(VtArgs a) {
     union { u32x4 v; bf16 b[8]; } u;
 #pragma unroll
     for (int i = 0; i < 8; ++i) u.b[i] = tile[b * 16 + hh * 8 + i][e];
-    st16(s.vt + (((int64_t)h * s.nblk + blk0 + b) * HD + e) * 16 + hh * 8, u.v);
+    st16_nt(s.vt + (((int64_t)h * s.nblk + blk0 + b) * HD + e) * 16 + hh * 8, u.v);
   }
 }
 
