@@ -149,6 +149,33 @@ def test_projection_isolated_from_attention_rounding():
     assert rel_l2(got, v_ref) <= 1e-5, rel_l2(got, v_ref)
 
 
+@pytest.mark.parametrize("H,hd,n_q", [(41, 64, 1000), (40, 128, 497)])
+def test_projection_euler_epilogue_full_tiles(H, hd, n_q):
+    # Unsplit projections (at least 128 output tiles) whose z values are loaded
+    # during the k loop: 41 x 64 features leave half a feature tile at the end
+    # and 1000 or 497 rows a partial row tile.  With z and h given, the step
+    # must equal z - h * (O W^T) computed in float64 from the GPU's own O.
+    rng = np.random.default_rng(H * 1000 + n_q)
+    d, cap = H * hd, 256
+    rk, rv = random_bits(rng, (H, cap, hd)), random_bits(rng, (H, cap, hd))
+    q, ku, vu = (random_bits(rng, (n_q, H, hd)) for _ in range(3))
+    w = random_bits(rng, (d, d), scale=d ** -0.5)
+    z0 = rng.standard_normal((n_q, d)).astype(np.float32)
+    h = 0.37
+    shape = workload.custom_session(H, hd, n_q, 0, 0, cap, 200, 31, (h,))
+    cache = make_cache(fmd, shape, rk, rv)
+    unit = fmd.UnitStep(cache, dev_bf16(q), dev_bf16(ku), dev_bf16(vu),
+                        z=torch.from_numpy(z0.copy()).to(DEV), h=h)
+    o = fmd.attention([unit])
+    fmd.denoise_step([unit], dev_bf16(w))
+    torch.cuda.synchronize()
+    v_ref = host_f64(o).reshape(n_q, d) @ oracle.bf16_bits_to_f64(w).T
+    z_ref = z0.astype(np.float64) - h * v_ref
+    got = host_f64(unit.z)
+    assert rel_l2(got - z0, z_ref - z0) <= 1e-5, rel_l2(got - z0, z_ref - z0)
+    assert np.max(np.abs(got - z_ref)) <= 1e-5
+
+
 def test_unit_deterministic():
     wl = workload.get("v01_unit")
     _, _, za = _run_unit(wl)
