@@ -15,8 +15,8 @@
 // the row tiles of one feature tile, so each weight tile is fetched once into
 // that XCD's L2 and the small bf16 latent is what every XCD re-reads.
 //
-// Operands go global -> LDS with MUBUF loads (lds bit), one 1 KiB block (8
-// rows x 64 k) per wave instruction, 16-byte chunk c of row r stored at chunk
+// Operands go global -> LDS with MUBUF loads (lds bit), issued by the first
+// wave of each SIMD, one 1 KiB block (8 rows x 64 k) per wave instruction, 16-byte chunk c of row r stored at chunk
 // position c ^ ((r >> 1) & 7) (bank-conflict-free operand reads).  Two LDS
 // stages of 64 KiB: the loads of k step t+1 are in flight while k step t is
 // multiplied, one barrier per k step, taken before the step's last 16-k
@@ -48,10 +48,11 @@ constexpr int WA_BLOCKS = WBM / WROWS;                          // 32
 constexpr int WB_BLOCKS = WBN / WROWS;                          // 32
 constexpr int WSTAGE_BYTES = (WA_BLOCKS + WB_BLOCKS) * 1024;    // 64 KiB
 constexpr int WSTAGES = 2;
-constexpr int WLOADS = (WA_BLOCKS + WB_BLOCKS) / WWAVES;        // 8 per wave per stage
+constexpr int WLOAD_WAVES = 4;                                  // one per SIMD
+constexpr int WLOADS = (WA_BLOCKS + WB_BLOCKS) / WLOAD_WAVES;   // 16 per loading wave per stage
 constexpr int WLDS_BYTES = WSTAGES * WSTAGE_BYTES;              // 128 KiB
 constexpr int WTILE_ROW_BYTES = WBN * 2;                        // epilogue tile row: 512 B
-static_assert(WA_BLOCKS % WWAVES == 0, "A blocks split evenly over waves");
+static_assert(WA_BLOCKS % WLOAD_WAVES == 0, "A blocks split evenly over the loading waves");
 static_assert(WBM * WTILE_ROW_BYTES <= WLDS_BYTES, "the bf16 tile fits in the stages");
 
 __device__ __forceinline__ int operand_swz(int row) { return (row >> 1) & 7; }
@@ -91,22 +92,30 @@ void qkv_wide_kernel(QkvArgs a) {
   const i32x4 ra = make_rsrc(s.zb + (int64_t)m0 * d, min(WBM, n_q - m0) * d * 2);
   const i32x4 rb = make_rsrc(a.w + (int64_t)n0 * d, min(WBN, n_out - n0) * d * 2);
 
-  // Wave w fills 1 KiB blocks w + 8i of a stage: i < 4 -> A blocks, else B.
+  // The loads come from the first wave of each SIMD (waves 0..3): wave w
+  // fills 1 KiB blocks w + 4i of a stage (i < 8 -> A blocks, else B), and the
+  // SIMD's other wave only multiplies, so a stall at a load's issue holds up
+  // one of the SIMD's two MFMA streams, not both (138 -> 127 us per
+  // 640x368-class launch; with the second wave of each SIMD as the loader,
+  // 137 against 132 on a slower box).
   // Lane i of a block: row i/8, k chunk (i%8) ^ swizzle(row).
+  const int lw = wave & (WLOAD_WAVES - 1);
   int voff[WLOADS];
 #pragma unroll
   for (int i = 0; i < WLOADS; ++i) {
-    const int b = wave + WWAVES * i;
+    const int b = lw + WLOAD_WAVES * i;
     const int rt = (b % WA_BLOCKS) * WROWS + (lane >> 3);
     const int chunk = (lane & 7) ^ operand_swz(rt);
     voff[i] = rt * d * 2 + chunk * 16;
   }
   auto load_stage = [&](int kt, int st) __attribute__((always_inline)) {
     char* base = lds + st * WSTAGE_BYTES;
+    if (wave < WLOAD_WAVES) {
 #pragma unroll
-    for (int i = 0; i < WLOADS; ++i)
-      dma16(i < WA_BLOCKS / WWAVES ? ra : rb, voff[i], kt * WBK * 2,
-            base + (wave + WWAVES * i) * 1024);
+      for (int i = 0; i < WLOADS; ++i)
+        dma16(i < WA_BLOCKS / WLOAD_WAVES ? ra : rb, voff[i], kt * WBK * 2,
+              base + (lw + WLOAD_WAVES * i) * 1024);
+    }
   };
   // Operand read of row `row` (of the A or B region), 16-k sub-step ks: lane
   // (g, r) wants k chunk 2ks + g.
