@@ -373,11 +373,16 @@ constexpr int kProjTile = 160;
 constexpr int kProjTileN = 128;
 constexpr int kProjBK = 64;
 // k-range parts of a projection launch with `tiles` output tiles and nk k
-// steps: enough work-groups to fill the chip when the tiles fill less than
-// half of it, with at least two k steps per part.
+// steps, when the tiles fill less than half of the chip: as many parts as fit
+// the chip, at most kProjMaxSplits and at least two k steps each.  Every part
+// writes an fp32 copy of the output for the reduce to read back, so filling
+// the chip does not pay: on the 192x336-class unit (24 tiles, 24 k steps) 4
+// parts take 14.4 us with the reduce, 10 parts (240 work-groups) 15.4, 3
+// parts 14.7 and 2 parts 15.8.
+constexpr int kProjMaxSplits = 4;
 inline int proj_splits(int64_t tiles, int nk) {
   if (tiles <= 0 || tiles * 2 >= kTargetCUs) return 1;
-  const int64_t want = kTargetCUs / tiles;
+  const int64_t want = std::min<int64_t>(kTargetCUs / tiles, kProjMaxSplits);
   return (int)std::max<int64_t>(1, std::min<int64_t>(want, nk / 2));
 }
 // Q/K/V projection tiling: 256 rows x 256 output features per block.

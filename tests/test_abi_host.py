@@ -406,28 +406,29 @@ def _model_pieces(H, per_head, lanes, groups):
 def _proj_part_bytes(n_q, d):
     """fp32 partial products of a split projection: 160 x 128 output tiles;
     when they fill less than half of 256 CUs, the k range (d / 64 steps) is
-    cut into enough parts to fill the chip, at least two k steps each."""
+    cut into as many parts as fit the chip, at most 4 and at least two k
+    steps each."""
     tiles = -(-n_q // 160) * -(-d // 128)
     if tiles * 2 >= 256:
         return 0
-    splits = max(1, min(256 // tiles, (d // 64) // 2))
+    splits = max(1, min(256 // tiles, 4, (d // 64) // 2))
     return splits * n_q * d * 4 if splits > 1 else 0
 
 
 def test_projection_split_workspace():
     # The 192x336-class unit (12 heads x 128, 260 queries): 2 x 12 tiles, so
-    # the k range of 24 steps is cut into 10 parts of fp32 partials.
+    # the k range of 24 steps is cut into 4 parts of fp32 partials.
     c = _cache(H=12, hd=128, cap=8576, ln=8576, head=0)
     rc, n_split = _ws([_step(c, 252, 8)])
     assert rc == 0
-    assert _proj_part_bytes(260, 1536) == 10 * 260 * 1536 * 4
+    assert _proj_part_bytes(260, 1536) == 4 * 260 * 1536 * 4
     big = _cache(H=40, hd=128, cap=60416, ln=60416, head=0)
     rc, n_big = _ws([_step(big, 920, 8)])
     assert rc == 0 and _proj_part_bytes(928, 5120) == 0
     # Staged unit K and V (npad = 272), O and the partials; the 8,836 keys per
     # query make few windows, so no lane is cut into pieces here or the
     # pieces' bytes come on top.
-    base = 2 * 12 * 272 * 128 * 2 + 260 * 1536 * 2 + 10 * 260 * 1536 * 4
+    base = 2 * 12 * 272 * 128 * 2 + 260 * 1536 * 2 + 4 * 260 * 1536 * 4
     assert n_split >= base
 
 
