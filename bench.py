@@ -88,14 +88,16 @@ def _log(args, *a):
         print(*a, file=sys.stderr, flush=True)
 
 
-def _attn_traffic(workload_name):
+def _attn_traffic(workload_name, steps_per_launch):
     """HBM bytes per attention launch from committed rocprofv3 counter runs,
-    valid only for the workload they were taken on and while attention.hip is
-    unchanged since then."""
+    valid only for the workload and the solver steps per launch they were
+    taken on and while attention.hip is unchanged since then."""
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
         if t.get("workload", "").split(" ")[0] != workload_name:
+            return None
+        if t.get("steps_per_launch") != steps_per_launch:
             return None
         with open(ATTN_SRC, "rb") as f:
             h = hashlib.sha256(f.read()).hexdigest()
@@ -571,16 +573,24 @@ def main():
     units_per_s = n_sess * args.steps / wall
     attn_ms, attn_n = kt["attn"]
     attn_avg_s = attn_ms / attn_n / 1e3
-    attn_flops_launch = wl.attention_flops_per_step()    # one launch covers all sessions of a step
+    # One launch covers the attention of every session for one or several
+    # solver steps (the unit driver batches steps whose inputs are given).
+    s0 = wl.sessions[0]
+    attn_launches_per_unit = attn_n / args.steps
+    steps_per_launch = s0.n_steps / attn_launches_per_unit
+    attn_flops_launch = wl.attention_flops_per_step() * steps_per_launch
     attn_tflops = attn_flops_launch / attn_avg_s / 1e12
-    traffic = _attn_traffic(wl.name)
+    traffic = _attn_traffic(wl.name, round(steps_per_launch, 3))
     per_kernel_us = {k: (v[0] / v[1] * 1e3 if v[1] else None) for k, v in kt.items()}
     app_ms, app_n = kt["append"]
     append_gbs = wl.append_bytes() / (app_ms / app_n / 1e3) / 1e9 if app_n else None
     proj_ms, proj_n = kt["proj"]
-    proj_tflops = wl.projection_flops_per_step() / (proj_ms / proj_n / 1e3) / 1e12 if proj_n else None
+    # A projection record covers one solver step, or every step of a batch
+    # when small units chain their split projections into one launch.
+    proj_steps = s0.n_steps * min(args.steps, 10) / proj_n if proj_n else 0
+    proj_tflops = (wl.projection_flops_per_step() * proj_steps / (proj_ms / proj_n / 1e3) / 1e12
+                   if proj_n else None)
 
-    s0 = wl.sessions[0]
     out = {
         "metric": "denoised units/sec (1 GPU) at 640×368-class shape; attn TFLOP/s vs MFMA peak",
         "value": round(units_per_s, 3),
@@ -612,15 +622,18 @@ def main():
             "kernel": "attn_kernel<128>",
             "flops_per_launch": attn_flops_launch,
             "avg_launch_us": round(attn_avg_s * 1e6, 2),
+            "solver_steps_per_launch": round(steps_per_launch, 3),
         },
         "per_kernel_us": {k: (round(v, 2) if v is not None else None)
                           for k, v in per_kernel_us.items()},
         # launches of each class per unit (the staging launch covers every step)
-        "launches_per_unit": {k: (round(v[1] / min(args.steps, 10), 2) if v[1] else 0)
-                              for k, v in kt.items() if k != "attn"},
+        "launches_per_unit": dict({k: (round(v[1] / min(args.steps, 10), 2) if v[1] else 0)
+                                   for k, v in kt.items() if k != "attn"},
+                                  attn=round(attn_launches_per_unit, 2)),
         "append_GBps": round(append_gbs, 1) if append_gbs else None,
         "append_frac_hbm": round(append_gbs / HBM_PEAK_GBS, 4) if append_gbs else None,
         "proj_TFLOPs": round(proj_tflops, 1) if proj_tflops else None,
+        "proj_steps_per_record": round(proj_steps, 3),
         "unit_layers_per_160ms": round(UNIT_BUDGET_S / (ms_per_step / 1e3 / n_sess), 2),
         "step_ms_median": round(unit_ms[len(unit_ms) // 2], 4),
         "step_ms_p90": round(unit_ms[min(len(unit_ms) - 1, (9 * len(unit_ms)) // 10)], 4),

@@ -113,7 +113,7 @@ _denoise_unit = _sig("fmd_denoise_unit", ctypes.c_int, ctypes.POINTER(_UnitIO), 
                      _vp, _sz, _vp)
 _denoise_unit_noalloc = _sig("fmd_denoise_unit_noalloc", ctypes.c_int, ctypes.POINTER(_UnitIO),
                             _i32, _i32, _vp, _vp)
-FMD_NOALLOC_SCRATCH_BYTES = 128 << 20
+FMD_NOALLOC_SCRATCH_BYTES = 256 << 20
 _unit_qkv_workspace_bytes = _sig("fmd_unit_qkv_workspace_bytes", ctypes.c_int,
                                  ctypes.POINTER(_UnitQkvIO), _i32, ctypes.POINTER(_sz))
 _denoise_unit_qkv = _sig("fmd_denoise_unit_qkv", ctypes.c_int, ctypes.POINTER(_UnitQkvIO), _i32,

@@ -190,6 +190,7 @@ struct SessPlan {
   int64_t total;
   int npart;
   int proj_splits;   // k-range parts of the launch's projection (1: none)
+  int proj_chain;    // > 1: a unit projects this many steps in one launch
   size_t off_kt, off_vt, off_o, off_opart, off_lse, off_part;   // workspace offsets
   size_t kv_stride;  // bytes between copies of the staged unit keys/values
 };
@@ -381,11 +382,17 @@ int check_workspace(void* ws, size_t have, size_t need) {
 // pair's first branch's) kt/vt workspace slots, copy kv_copy (written there by
 // the Q/K/V projection, or by a unit's staging of every step up front); no
 // staging launch.
+// phases: kPhaseAttn enqueues the staging, attention, merge and mix launches,
+// kPhaseProj the projection; a unit whose steps' attention runs as one launch
+// calls the two phases separately (each session's O stays in its workspace
+// slot, plans[...].off_o, in between).
+constexpr int kPhaseAttn = 1, kPhaseProj = 2, kPhaseAll = 3;
+
 int enqueue_steps(const fmd_unit_step* units, int n, const std::vector<SessPlan>& plans,
                   const void* w_o, char* ws, bf16* o_out, hipStream_t st,
                   bf16* const* zb_out = nullptr, const float* guidance = nullptr,
                   int proj_mode = kProjEuler, float* const* r_out = nullptr,
-                  bool kv_staged = false, int kv_copy = 0) {
+                  bool kv_staged = false, int kv_copy = 0, int phases = kPhaseAll) {
   const int H = units[0].cache->n_heads, hd = units[0].cache->head_dim;
   const int d = H * hd;
   const float scale_log2 = (float)(1.4426950408889634 / sqrt((double)hd));
@@ -488,18 +495,20 @@ int enqueue_steps(const fmd_unit_step* units, int n, const std::vector<SessPlan>
     // combine kernel finds its session by item0, so they get an empty range
     // at the current end.
     int rc;
-    if (va.items > 0 &&
-        (rc = timed_launch(FMD_KERNEL_VT, st, [&] { return launch_vt(va, hd, st); })))
-      return rc;
-    if ((rc = timed_launch(FMD_KERNEL_ATTN, st, [&] { return launch_attn(aa, hd, st); })))
-      return rc;
-    if (any_split &&
-        (rc = timed_launch(FMD_KERNEL_COMBINE, st, [&] { return launch_combine(ca, hd, st); })))
-      return rc;
-    if (guidance &&
-        (rc = timed_launch(FMD_KERNEL_MIX, st, [&] { return launch_mix(ma, st); })))
-      return rc;
-    if (!o_out && (rc = timed_launch(FMD_KERNEL_PROJ, st, [&] {
+    if (phases & kPhaseAttn) {
+      if (va.items > 0 &&
+          (rc = timed_launch(FMD_KERNEL_VT, st, [&] { return launch_vt(va, hd, st); })))
+        return rc;
+      if ((rc = timed_launch(FMD_KERNEL_ATTN, st, [&] { return launch_attn(aa, hd, st); })))
+        return rc;
+      if (any_split &&
+          (rc = timed_launch(FMD_KERNEL_COMBINE, st, [&] { return launch_combine(ca, hd, st); })))
+        return rc;
+      if (guidance &&
+          (rc = timed_launch(FMD_KERNEL_MIX, st, [&] { return launch_mix(ma, st); })))
+        return rc;
+    }
+    if ((phases & kPhaseProj) && !o_out && (rc = timed_launch(FMD_KERNEL_PROJ, st, [&] {
                      hipError_t e = launch_proj(pa, proj_mode, st);
                      return e == hipSuccess ? launch_proj_reduce(pa, proj_mode, st) : e;
                    })))
@@ -752,14 +761,117 @@ static int unit_kv_copies(const fmd_unit_io* ss, int n, int n_steps) {
   return 1;
 }
 
-// Plan a validated unit: post-append ring states, the step plans and the
-// workspace bytes.
-static void plan_unit(const fmd_unit_io* sessions, int n_sessions, int n_steps,
+// Solver steps whose attention one launch covers in fmd_denoise_unit.  There
+// the steps' Q, K_u and V_u are inputs (no step's attention reads the latent),
+// so the attention of several steps is one launch whose sessions are the
+// (step, session) pairs, and the projections then update z step by step, in
+// order.  The batch is the largest divisor of n_steps whose pairs fit one
+// launch, so every batch of a unit has the same plan.
+static int unit_step_batch(int n_sessions, int n_steps) {
+  const int most = std::max(1, kMaxSessPerLaunch / n_sessions);
+  for (int b = std::min(n_steps, most); b > 1; --b)
+    if (n_steps % b == 0) return b;
+  return 1;
+}
+
+// Plan a validated unit: the post-append ring states, the plans of one batch
+// of steps (entry b * n + i: step b of the batch, session i) and the workspace
+// bytes.  Workspace: per session, the staged unit values (and keys, when they
+// are not read in place) of every step (one copy when every session reuses
+// one set) and the projection's fp32
+// partials (shared by the steps, which project one after another); per (step
+// of the batch, session), O and the pieces of the lanes cut by group ends.
+static void plan_unit(const fmd_unit_io* sessions, int n, int n_steps,
                       std::vector<fmd_kv_cache>& after, std::vector<fmd_unit_step>& steps,
                       std::vector<SessPlan>& plans, size_t* need) {
-  post_append_steps(sessions, n_sessions, after, steps);
-  plan_steps(steps.data(), n_sessions, false, plans, need,
-             unit_kv_copies(sessions, n_sessions, n_steps));
+  post_append_steps(sessions, n, after, steps);
+  const int B = unit_step_batch(n, n_steps);
+  const int H = after[0].n_heads, hd = after[0].head_dim, d = H * hd;
+  const int copies = unit_kv_copies(sessions, n, n_steps);
+  plans.assign((size_t)B * n, SessPlan{});
+  for (int b = 0; b < B; ++b)
+    for (int i = 0; i < n; ++i)
+      plan_session(&after[i], steps[i].n_video + steps[i].n_audio, plans[(size_t)b * n + i]);
+  plan_groups(plans, H);
+  // Each step projects its n sessions (launch chunks as in enqueue_steps),
+  // unless the batch's projections split over the k range: then the B steps'
+  // partial products are one launch (B * n <= kMaxSessPerLaunch) and one
+  // reduce applies the steps' updates in order (proj_chain = B).
+  std::vector<SessPlan> one(plans.begin(), plans.begin() + n);
+  plan_proj(one, d);
+  int chain_splits = 1;
+  if (B > 1) {
+    int64_t tiles = 0;
+    for (const auto& p : plans)
+      tiles += (int64_t)((p.n_q + kProjTile - 1) / kProjTile) * ((d + kProjTileN - 1) / kProjTileN);
+    chain_splits = proj_splits(tiles, d / kProjBK);
+  }
+  const bool chain = chain_splits > 1;
+  size_t off = 0;
+  for (int i = 0; i < n; ++i) {
+    // Keys the attention reads in place take no staging room.
+    const size_t kvb = align256((size_t)H * one[i].npad * hd * 2);
+    const int kv_regions = unit_keys_in_place(sessions[i].k_u, one[i].n_q, d) ? 1 : 2;
+    const size_t kv_off = off;
+    off += (size_t)copies * kv_regions * kvb;
+    const size_t part_off = off;
+    if (!chain && one[i].proj_splits > 1)
+      off = align256(off + (size_t)one[i].proj_splits * one[i].n_q * d * 4);
+    for (int b = 0; b < B; ++b) {
+      SessPlan& p = plans[(size_t)b * n + i];
+      p.proj_splits = chain ? chain_splits : one[i].proj_splits;
+      p.proj_chain = chain ? B : 1;
+      p.off_kt = kv_off;
+      p.off_vt = kv_off + (kv_regions - 1) * kvb;
+      p.kv_stride = kv_regions * kvb;
+      p.off_part = part_off;
+    }
+  }
+  for (auto& p : plans) {
+    p.off_o = off;
+    off = align256(off + (size_t)p.n_q * d * 2);
+    p.off_opart = p.off_lse = off;
+    if (p.npart > 0) {
+      off = align256(off + (size_t)p.npart * p.n_q * d * 2);
+      p.off_lse = off;
+      off = align256(off + (size_t)p.npart * p.n_q * H * 4);
+    }
+    if (chain) {   // each step's own partials: the steps' products run together
+      p.off_part = off;
+      off = align256(off + (size_t)chain_splits * p.n_q * d * 4);
+    }
+  }
+  *need = off;
+}
+
+// The projections of a batch of m = B * n (step, session) pairs (step-major,
+// one launch chunk) whose k range is split: one launch of every pair's fp32
+// partial products, then one reduce that applies the B steps' Euler updates
+// to each latent in step order.
+static int enqueue_proj_chain(const fmd_unit_step* units, int m, int chain,
+                              const std::vector<SessPlan>& plans, const void* w_o, char* ws,
+                              hipStream_t st) {
+  const int d = units[0].cache->n_heads * units[0].cache->head_dim;
+  const int ntiles = (d + kProjTileN - 1) / kProjTileN;
+  ProjArgs pa = {};
+  pa.n_sess = m;
+  pa.d = d;
+  pa.n_out = d;
+  pa.w = static_cast<const bf16*>(w_o);
+  pa.splits = plans[0].proj_splits;
+  pa.chain = chain;
+  for (int k = 0; k < m; ++k) {
+    const SessPlan& p = plans[k];
+    const int mtiles = (p.n_q + kProjTile - 1) / kProjTile;
+    pa.s[k] = ProjSess{reinterpret_cast<bf16*>(ws + p.off_o), units[k].z, nullptr, nullptr,
+                       reinterpret_cast<float*>(ws + p.off_part), p.n_q, mtiles, pa.items,
+                       units[k].h};
+    pa.items += mtiles * ntiles * pa.splits;
+  }
+  return timed_launch(FMD_KERNEL_PROJ, st, [&] {
+    hipError_t e = launch_proj(pa, kProjEuler, st);
+    return e == hipSuccess ? launch_proj_reduce(pa, kProjEuler, st) : e;
+  });
 }
 
 int fmd_unit_workspace_bytes(const fmd_unit_io* sessions, int32_t n_sessions, int32_t n_steps,
@@ -833,19 +945,43 @@ static int run_unit(fmd_unit_io* sessions, int n_sessions, int n_steps, const vo
       (rc = enqueue_appends(caches.data(), ks.data(), vs.data(), ts.data(), (int)caches.size(), st)))
     return rc;
   if ((rc = enqueue_unit_staging(sessions, n_sessions, n_steps, plans, workspace, st))) return rc;
-  const bool one_copy = unit_kv_copies(sessions, n_sessions, n_steps) == 1;
-  for (int s = 0; s < n_steps; ++s) {
-    for (int i = 0; i < n_sessions; ++i) {
-      const int64_t off = (int64_t)s * sessions[i].step_stride_elems;
-      steps[i].cache = sessions[i].cache;   // now in its post-append state
-      steps[i].q = static_cast<const bf16*>(sessions[i].q) + off;
-      steps[i].k_u = static_cast<const bf16*>(sessions[i].k_u) + off;
-      steps[i].v_u = static_cast<const bf16*>(sessions[i].v_u) + off;
-      steps[i].h = sessions[i].h[s];
-    }
-    if ((rc = enqueue_steps(steps.data(), n_sessions, plans, w_o, workspace, nullptr, st,
-                            nullptr, nullptr, kProjEuler, nullptr, true, one_copy ? 0 : s)))
+  const int n = n_sessions, B = (int)plans.size() / n_sessions;
+  const bool one_copy = unit_kv_copies(sessions, n, n_steps) == 1;
+  std::vector<fmd_unit_step> att((size_t)B * n);
+  std::vector<SessPlan> pb(plans);
+  for (int s0 = 0; s0 < n_steps; s0 += B) {
+    // The attention of steps s0 .. s0 + B - 1: one launch (per chunk of
+    // kMaxSessPerLaunch pairs), each pair reading its step's staged copy.
+    for (int b = 0; b < B; ++b)
+      for (int i = 0; i < n; ++i) {
+        const int s = s0 + b;
+        const size_t e = (size_t)b * n + i;
+        const int64_t off = (int64_t)s * sessions[i].step_stride_elems;
+        fmd_unit_step& u = att[e];
+        u = steps[i];
+        u.cache = sessions[i].cache;   // now in its post-append state
+        u.q = static_cast<const bf16*>(sessions[i].q) + off;
+        u.k_u = static_cast<const bf16*>(sessions[i].k_u) + off;
+        u.v_u = static_cast<const bf16*>(sessions[i].v_u) + off;
+        u.h = sessions[i].h[s];
+        const size_t copy = one_copy ? 0 : (size_t)s;
+        pb[e].off_kt = plans[e].off_kt + copy * plans[e].kv_stride;
+        pb[e].off_vt = plans[e].off_vt + copy * plans[e].kv_stride;
+      }
+    if ((rc = enqueue_steps(att.data(), B * n, pb, w_o, workspace, nullptr, st, nullptr, nullptr,
+                            kProjEuler, nullptr, true, 0, kPhaseAttn)))
       return rc;
+    // Then each step's projection and Euler update, in step order.
+    if (pb[0].proj_chain > 1) {
+      if ((rc = enqueue_proj_chain(att.data(), B * n, B, pb, w_o, workspace, st))) return rc;
+      continue;
+    }
+    for (int b = 0; b < B; ++b) {
+      const std::vector<SessPlan> ps(pb.begin() + (size_t)b * n, pb.begin() + (size_t)(b + 1) * n);
+      if ((rc = enqueue_steps(att.data() + (size_t)b * n, n, ps, w_o, workspace, nullptr, st,
+                              nullptr, nullptr, kProjEuler, nullptr, true, 0, kPhaseProj)))
+        return rc;
+    }
   }
   return FMD_OK;
 }

@@ -295,6 +295,9 @@ struct ProjArgs {
   int32_t n_out;
   int32_t items;
   int32_t splits;     // k-range parts (1: the epilogue runs in the GEMM)
+  int32_t chain;      // splits > 1, kProjEuler: the sessions are `chain`
+                      // solver steps of n_sess / chain latents, step-major;
+                      // the reduce applies them in step order (0, 1: none)
 };
 
 // Q/K/V projection of the latent: [Q | K_u | V_u] = bf16(zb * W_qkv^T)

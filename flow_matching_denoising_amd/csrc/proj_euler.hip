@@ -378,18 +378,44 @@ __global__ __launch_bounds__(256) void mix_kernel(MixArgs a) {
   *reinterpret_cast<bf16x8*>(s.oc + e) = y;
 }
 
+// y = part[0] + part[1] + ... (in that order) at element offset e of one
+// session's [splits][n_q][d] partials (ne = n_q * d).
+__device__ __forceinline__ f32x4 sum_parts(const float* pp, int64_t ne, int splits) {
+  f32x4 y = *reinterpret_cast<const f32x4*>(pp);
+  // Parts 1, 2, ... added in order, their loads issued four at a time.
+  for (int j0 = 1; j0 < splits; j0 += 4) {
+    f32x4 p[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      p[u] = j0 + u < splits ? *reinterpret_cast<const f32x4*>(pp + (j0 + u) * ne)
+                             : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (j0 + u < splits)
+#pragma unroll
+        for (int t = 0; t < 4; ++t) y[t] += p[u][t];
+  }
+  return y;
+}
+
 // The split projection's second half: y = part[0] + part[1] + ... (in that
 // order), then the epilogue of MODE on 4 consecutive elements per thread.
+// With chain > 1 (Euler mode) the launch's sessions are `chain` consecutive
+// solver steps of the same latents, step-major (session b * nc + i is step b
+// of latent i, nc = n_sess / chain): each thread applies the steps' updates
+// z <- z - h_b * y_b to its elements in step order.
 template <int MODE>
 __global__ __launch_bounds__(256) void proj_reduce_kernel(ProjArgs a) {
-  // Element E of the launch: sessions' [n_q][d] outputs back to back.
+  // Element E of the launch: the first nc sessions' [n_q][d] outputs back to back.
   const int64_t E = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
   const int d = a.d;
+  const int chain = a.chain > 1 ? a.chain : 1;
+  const int nc = a.n_sess / chain;
   int si = -1;
   int64_t base = 0, e = 0;
 #pragma unroll
   for (int i = 0; i < kMaxSessPerLaunch; ++i) {
-    if (i < a.n_sess) {
+    if (i < nc) {
       const int64_t ne_i = (int64_t)a.s[i].n_q * d;
       if (si < 0 && E < base + ne_i) {
         si = i;
@@ -401,27 +427,17 @@ __global__ __launch_bounds__(256) void proj_reduce_kernel(ProjArgs a) {
   if (si < 0) return;
   const ProjSess& s = a.s[si];
   const int64_t ne = (int64_t)s.n_q * d;
-  const float* const pp = s.part + e;
-  f32x4 y = *reinterpret_cast<const f32x4*>(pp);
-  // Parts 1, 2, ... added in order, their loads issued four at a time.
-  for (int j0 = 1; j0 < a.splits; j0 += 4) {
-    f32x4 p[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u)
-      p[u] = j0 + u < a.splits ? *reinterpret_cast<const f32x4*>(pp + (j0 + u) * ne)
-                               : f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int u = 0; u < 4; ++u)
-      if (j0 + u < a.splits)
-#pragma unroll
-        for (int t = 0; t < 4; ++t) y[t] += p[u][t];
-  }
   f32x4 zv = *reinterpret_cast<const f32x4*>(s.z + e);
   if constexpr (MODE == kProjEuler) {
+    for (int b = 0; b < chain; ++b) {
+      const ProjSess& sb = a.s[b * nc + si];
+      const f32x4 y = sum_parts(sb.part + e, ne, a.splits);
 #pragma unroll
-    for (int t = 0; t < 4; ++t) zv[t] = zv[t] - s.h * y[t];
+      for (int t = 0; t < 4; ++t) zv[t] = zv[t] - sb.h * y[t];
+    }
     *reinterpret_cast<f32x4*>(s.z + e) = zv;
   } else {
+    const f32x4 y = sum_parts(s.part + e, ne, a.splits);
     f32x4 rv = *reinterpret_cast<const f32x4*>(s.r + e);
 #pragma unroll
     for (int t = 0; t < 4; ++t) rv[t] += y[t];
@@ -476,8 +492,10 @@ hipError_t launch_proj(const ProjArgs& a, int mode, hipStream_t st) {
 
 hipError_t launch_proj_reduce(const ProjArgs& a, int mode, hipStream_t st) {
   if (a.items <= 0 || a.splits <= 1) return hipSuccess;
-  int64_t rows = 0;   // one thread per 4 elements of the sessions' outputs
-  for (int i = 0; i < a.n_sess; ++i) rows += a.s[i].n_q;
+  if (a.chain > 1 && (mode != kProjEuler || a.n_sess % a.chain != 0)) return hipErrorInvalidValue;
+  const int nc = a.chain > 1 ? a.n_sess / a.chain : a.n_sess;
+  int64_t rows = 0;   // one thread per 4 elements of the (first nc) sessions' outputs
+  for (int i = 0; i < nc; ++i) rows += a.s[i].n_q;
   const int64_t threads = rows * a.d / 4;
   const dim3 grid((unsigned)((threads + 255) / 256)), block(256);
   switch (mode) {

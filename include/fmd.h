@@ -194,14 +194,20 @@ typedef struct fmd_unit_io {
  * attention's 16-key blocked layout by one launch before the first step; the
  * attention reads the unit keys where the caller keeps them (they are staged
  * too, in [H][npad][hd], only when n_q * d * 2 bytes reach 2^31).  The
- * workspace holds n_steps copies of room for both (one when every session's
- * step_stride_elems is 0).  Errors: as fmd_denoise_unit's validation. */
+ * workspace holds n_steps copies of room for what is staged (one when every
+ * session's step_stride_elems is 0).  Errors: as fmd_denoise_unit's
+ * validation. */
 int fmd_unit_workspace_bytes(const fmd_unit_io* sessions, int32_t n_sessions, int32_t n_steps,
                              size_t* out_bytes);
 
 /*
  * One denoised unit for n_sessions sessions: one batched append, then
- * n_steps solver steps, each as fmd_denoise_step with h[s].
+ * n_steps solver steps, each as fmd_denoise_step with h[s].  The steps' Q,
+ * K_u and V_u are inputs, so no step's attention reads the latent: the
+ * attention of B steps runs as one launch whose sessions are the (step,
+ * session) pairs (B: the largest divisor of n_steps with B * n_sessions <= 16,
+ * else 1), then the B projections and Euler updates follow in step order.
+ * The workspace holds O and the pieces of cut lanes for each of the B steps.
  * Errors: as fmd_kv_append and fmd_denoise_step; n_steps < 1 -> FMD_E_INVAL.
  */
 int fmd_denoise_unit(fmd_unit_io* sessions, int32_t n_sessions, int32_t n_steps,
@@ -213,13 +219,13 @@ int fmd_denoise_unit(fmd_unit_io* sessions, int32_t n_sessions, int32_t n_steps,
  * allocate device memory (code under HIP graph capture, tight serving loops,
  * harnesses that forbid allocation).  Same arguments, semantics, validation
  * and errors as fmd_denoise_unit, and the same kernels; their scratch is a
- * static device array of FMD_NOALLOC_SCRATCH_BYTES (128 MiB) that the
+ * static device array of FMD_NOALLOC_SCRATCH_BYTES (256 MiB) that the
  * library holds on every GPU it runs on until the process ends.  The call
  * allocates no device memory.
  *   - A unit whose scratch need (fmd_unit_workspace_bytes) exceeds
  *     FMD_NOALLOC_SCRATCH_BYTES -> FMD_E_WORKSPACE, nothing enqueued.  One
  *     640x368-class session (40 heads x 928 queries, 4 steps with their own
- *     Q/K/V) needs 124 MB with 60,416 cached keys and 134 MB with the wrapped
+ *     Q/K/V) needs 192 MB with 60,416 cached keys and 230 MB with the wrapped
  *     241,664-key ring, and fits; two such sessions do not.
  *   - `stream` must belong to the current device (FMD_E_INVAL otherwise).
  *   - Every call on one GPU shares that GPU's scratch: calls that overlap on
@@ -227,7 +233,7 @@ int fmd_denoise_unit(fmd_unit_io* sessions, int32_t n_sessions, int32_t n_steps,
  *     give wrong results.  Calls ordered on one stream are safe.  Nothing in
  *     the scratch needs to start at zero; it keeps the last call's contents.
  */
-#define FMD_NOALLOC_SCRATCH_BYTES (128u << 20)
+#define FMD_NOALLOC_SCRATCH_BYTES (256u << 20)
 int fmd_denoise_unit_noalloc(fmd_unit_io* sessions, int32_t n_sessions, int32_t n_steps,
                              const void* w_o, void* stream);
 

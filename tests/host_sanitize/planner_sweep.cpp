@@ -8,7 +8,8 @@
 // Checks beside the sanitizers:
 //  - every planner call on a valid description succeeds and is deterministic
 //    (the same bytes twice);
-//  - the unit planner agrees with the step planner on the post-append state;
+//  - the unit planner agrees with the step planner on the post-append state
+//    (one step; the unit keys read in place take no staging room);
 //  - the z-dependent planner needs at least the plain one's bytes (the same
 //    plan plus its slabs), the guided one at least its four slabs per unit;
 //  - invalid descriptions are rejected with the documented status and leave
@@ -116,15 +117,44 @@ int main(int argc, char** argv) {
     CHECK(rc == FMD_OK, "case %d: unit planner rc=%d", c, rc);
     rc = fmd_workspace_bytes(st.data(), n, &b);
     CHECK(rc == FMD_OK, "case %d: step planner rc=%d", c, rc);
-    CHECK(a == b, "case %d: unit %zu vs step %zu bytes", c, a, b);
+    // One step: the step planner's regions, less the staging room of unit
+    // keys that the attention reads in place (n_q * d * 2 bytes below 2^31).
+    size_t keys_in_place = 0;
+    for (int i = 0; i < n; ++i) {
+      const int64_t nq = (int64_t)ss[i].n_video + ss[i].n_audio;
+      if (nq * d * 2 < ((int64_t)1 << 31))
+        keys_in_place += ((size_t)H * ((nq + 15) & ~15) * hd * 2 + 255) & ~(size_t)255;
+    }
+    CHECK(a + keys_in_place == b, "case %d: unit %zu + keys %zu vs step %zu bytes", c, a,
+          keys_in_place, b);
     rc = fmd_unit_workspace_bytes(io.data(), n, 1, &a2);
     CHECK(rc == FMD_OK && a2 == a, "case %d: planner not deterministic", c);
     int64_t min_bytes = 0;
     for (int i = 0; i < n; ++i) {
       const int64_t nq = (int64_t)ss[i].n_video + ss[i].n_audio;
-      min_bytes += 3 * nq * d * 2;   // unit K, unit V, O
+      min_bytes += (nq * d * 2 < ((int64_t)1 << 31) ? 2 : 3) * nq * d * 2;   // [unit K,] unit V, O
     }
     CHECK((int64_t)a >= min_bytes, "case %d: %zu bytes < %lld", c, a, (long long)min_bytes);
+    // Four steps with their own inputs: every step's values (and keys not
+    // read in place) are staged, and the attention of B steps (the largest
+    // divisor of 4 with B * n <= 16) runs as one launch, each with its own O.
+    {
+      std::vector<fmd_unit_io> io4(io);
+      for (int i = 0; i < n; ++i)
+        io4[i].step_stride_elems = ((int64_t)ss[i].n_video + ss[i].n_audio) * d;
+      size_t a4 = 0, a4b = 0;
+      rc = fmd_unit_workspace_bytes(io4.data(), n, 4, &a4);
+      CHECK(rc == FMD_OK, "case %d: 4-step unit planner rc=%d", c, rc);
+      rc = fmd_unit_workspace_bytes(io4.data(), n, 4, &a4b);
+      CHECK(rc == FMD_OK && a4b == a4, "case %d: 4-step planner not deterministic", c);
+      const int B = n <= 4 ? 4 : (n <= 8 ? 2 : 1);
+      int64_t min4 = 0;
+      for (int i = 0; i < n; ++i) {
+        const int64_t nq = (int64_t)ss[i].n_video + ss[i].n_audio;
+        min4 += (4 * (nq * d * 2 < ((int64_t)1 << 31) ? 1 : 2) + B) * nq * d * 2;
+      }
+      CHECK((int64_t)a4 >= min4, "case %d: 4-step %zu bytes < %lld", c, a4, (long long)min4);
+    }
     ++planned;
 
     // The z-dependent and layer-stack planners.

@@ -3,9 +3,11 @@
 Each workload runs as the benchmark launches it: every session of the unit in
 one ``denoise_unit`` call (append, then every solver step).  Afterwards the
 attention output of every step is taken through ``fmd_attention`` on the
-post-append rings, with the same cut of the keys into group ranges as inside
-the unit (the plan depends only on the shapes), and compared element by
-element with the oracle:
+post-append rings, with the steps batched into launches as the unit batches
+them (the (step, session) pairs of B steps in one launch, B the largest
+divisor of the step count with B * sessions <= 16), so the keys are cut into
+the same group ranges as inside the unit (the plan depends only on the
+shapes), and compared element by element with the oracle:
 every row and head of O for the steps named below, and ``dz = z - eps``.
 
 Tolerances: max-abs 2e-2 and rel-L2 1e-2 on O and dz (rel-L2 on its own is the
@@ -26,6 +28,14 @@ import torch  # noqa: E402
 from tests.gpu_util import DEV, assert_close, dev_bf16, host_f64, host_u16, make_cache  # noqa: E402
 
 pytestmark = pytest.mark.gpu
+
+
+def _steps_per_launch(n_sessions, n_steps):
+    """Solver steps whose attention the unit driver runs as one launch."""
+    for b in range(min(n_steps, max(1, 16 // n_sessions)), 1, -1):
+        if n_steps % b == 0:
+            return b
+    return 1
 
 
 class _UnitRun:
@@ -50,19 +60,23 @@ class _UnitRun:
         self.name, self.wl, self.ui = name, wl, ui
         self.z = [host_f64(z) for z in zs]
         self.state = [(c.len_tokens, c.head_tokens) for c in caches]
-        # O of every step, all sessions in one launch (bf16 bits, per session).
+        # O of every step (bf16 bits, per session): the (step, session) pairs
+        # of B steps in one launch, step-major, as the unit runs them.
         self.o = []
         n_steps = wl.sessions[0].n_steps
-        for st in range(n_steps):
+        B = _steps_per_launch(len(ui.sessions), n_steps)
+        for st0 in range(0, n_steps, B):
             units = [fmd.UnitStep(c, dev_bf16(si.q[st]), dev_bf16(si.k_u[st]),
                                   dev_bf16(si.v_u[st]), n_audio=si.shape.n_audio)
-                     for si, c in zip(ui.sessions, caches)]
+                     for st in range(st0, st0 + B) for si, c in zip(ui.sessions, caches)]
             o = host_u16(fmd.attention(units))
-            per, r0 = [], 0
-            for si in ui.sessions:
-                per.append(o[r0:r0 + si.shape.n_q])
-                r0 += si.shape.n_q
-            self.o.append(per)
+            r0 = 0
+            for _ in range(B):
+                per = []
+                for si in ui.sessions:
+                    per.append(o[r0:r0 + si.shape.n_q])
+                    r0 += si.shape.n_q
+                self.o.append(per)
         del caches, ios, zs
         torch.cuda.empty_cache()
 

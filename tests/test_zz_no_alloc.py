@@ -49,7 +49,7 @@ def _compare(name, wl):
 
 
 def test_noalloc_two_calls_second_smaller():
-    # First the 640x368-class unit (about 67 MB of scratch), then three small
+    # First the 640x368-class unit (about 192 MB of scratch), then three small
     # ragged sessions reusing the same scratch with the first call's contents
     # left in it.
     big = workload.get("v02_unit")
@@ -62,20 +62,22 @@ def test_noalloc_two_calls_second_smaller():
 
 
 def test_noalloc_rejects_a_unit_beyond_the_scratch_untouched():
-    # Two sessions over wrapped 242k-key rings of the 640x368-class shape need
-    # more scratch than the static array: FMD_E_WORKSPACE, no kernel, ring
-    # states unchanged.
+    # Two sessions over wrapped 242k-key rings of the 640x368-class shape,
+    # four steps with their own Q/K/V, need more scratch than the static
+    # array (384 MB against 256 MiB): FMD_E_WORKSPACE, no kernel, ring states
+    # unchanged.
     H, hd, units = 40, 128, 256
     cap = units * 944
     ios, caches = [], []
     w = torch.zeros((H * hd, H * hd), dtype=torch.bfloat16, device=DEV)
     for _ in range(2):
         cache = fmd.KVCache(H, hd, cap, device=DEV, len_tokens=cap, head_tokens=100 * 944)
-        q = torch.zeros((928, H, hd), dtype=torch.bfloat16, device=DEV)
+        q = torch.zeros((4, 928, H, hd), dtype=torch.bfloat16, device=DEV)
         z = torch.zeros((928, H * hd), dtype=torch.float32, device=DEV)
         ks = torch.zeros((944, H, hd), dtype=torch.bfloat16, device=DEV)
-        ios.append(fmd.UnitIO(cache, ks, ks, q, q, q, z, [0.5, 0.5], n_audio=8))
+        ios.append(fmd.UnitIO(cache, ks, ks, q, q, q, z, [0.25] * 4, n_audio=8))
         caches.append(cache)
+    assert fmd.unit_workspace_bytes(ios) > fmd.FMD_NOALLOC_SCRATCH_BYTES
     with pytest.raises(fmd.FmdError) as e:
         fmd.denoise_unit_noalloc(ios, w)
     assert e.value.code == -5
