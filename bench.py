@@ -4,7 +4,8 @@ One step = one denoised unit of the 640x368-class workload (40 heads x 128,
 920 video + 8 audio queries, a 64-unit ring of 944-token slices = 60,416 keys):
 the slice append, then 4 Euler solver steps, each attention over
 [60,416 cached keys || 928 unit keys] -> projection (5120 x 5120) -> Euler
-update.  Inputs are seeded synthetic tensors (no weights or data were
+update.  The steps' Q, K_u, V_u are inputs, so the unit runs the 4 steps'
+attention as one launch, then the projections and updates in step order.  Inputs are seeded synthetic tensors (no weights or data were
 released for the method), resident in HBM before the timed region.
 
 Prints ONE JSON line (rank 0, N=1).  Besides throughput it reports:
