@@ -778,9 +778,10 @@ static int unit_step_batch(int n_sessions, int n_steps) {
 // of steps (entry b * n + i: step b of the batch, session i) and the workspace
 // bytes.  Workspace: per session, the staged unit values (and keys, when they
 // are not read in place) of every step (one copy when every session reuses
-// one set) and the projection's fp32
-// partials (shared by the steps, which project one after another); per (step
-// of the batch, session), O and the pieces of the lanes cut by group ends.
+// one set) and the projection's fp32 partials (shared by the steps, which
+// project one after another); per (step of the batch, session), O, the pieces
+// of the lanes cut by group ends and, when the batch's split projections
+// share one launch, that step's partials.
 static void plan_unit(const fmd_unit_io* sessions, int n, int n_steps,
                       std::vector<fmd_kv_cache>& after, std::vector<fmd_unit_step>& steps,
                       std::vector<SessPlan>& plans, size_t* need) {
