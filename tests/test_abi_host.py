@@ -495,3 +495,55 @@ def test_noalloc_rejects_units_beyond_the_static_scratch():
             assert all((c.len_tokens, c.head_tokens) == (cap, 100 * 944) for c in cs)
         # Validation comes first, as for fmd_denoise_unit.
         assert fmd._denoise_unit_noalloc(arr, n, 0, FAKE, None) == -1
+
+
+@pytest.mark.parametrize("n_sessions,steps_per_launch", [(1, 4), (3, 4), (5, 2), (8, 2), (17, 1)])
+def test_unit_workspace_batches_the_steps_attention(n_sessions, steps_per_launch):
+    # fmd_denoise_unit runs the attention of B steps as one launch whose
+    # sessions are the (step, session) pairs, step-major (B: the largest
+    # divisor of the 4 steps with B * sessions <= 16).  Its workspace is, per
+    # session, the 4 steps' staged unit values (the keys are read in place),
+    # and per (step of the batch, session) O and the pieces of the lanes that
+    # the launch's group ranges cut, by an independent model of the partition.
+    H, hd, n_q, cap, head = 40, 128, 928, 60416, 59472
+    h = (ctypes.c_float * 4)(0.25, 0.25, 0.25, 0.25)
+    hp = ctypes.cast(h, ctypes.POINTER(ctypes.c_float))
+    cs = [_Cache(FAKE + i * 0x1000000, FAKE + 0x100000 + i * 0x1000000, H, hd, cap, cap, head)
+          for i in range(n_sessions)]
+    ios = [_UnitIO(ctypes.pointer(c), None, None, 0, FAKE, FAKE, FAKE, n_q * H * hd,
+                   FAKE + 0x40000000 + i * 0x2000000, 920, 8, hp) for i, c in enumerate(cs)]
+    arr = (_UnitIO * n_sessions)(*ios)
+    need = ctypes.c_size_t(0)
+    assert fmd._unit_workspace_bytes(arr, n_sessions, 4, ctypes.byref(need)) == 0
+
+    def a256(x):
+        return (x + 255) // 256 * 256
+    start = head % cap
+    n0 = (cap - (start & ~15) + 63) // 64
+    n1 = (start + 63) // 64
+    n2 = (n_q + 63) // 64
+    B = steps_per_launch
+    m = B * n_sessions                                 # attention sessions per launch
+    per_head = m * (n0 + n1 + n2)
+    groups = min(64, H * per_head // 8)                # 8 XCDs x 8 groups of 4 work-groups
+    if groups // H * H * 20 >= groups * 17:
+        groups = groups // H * H
+    if m <= 16:
+        pieces = _model_pieces(H, per_head, [(k * (n0 + n1 + n2), [n0, n1, n2])
+                                             for k in range(m)], groups)
+    else:                                              # several launches of at most 16
+        pieces = []
+        for c0 in range(0, m, 16):
+            cn = min(16, m - c0)
+            ph = cn * (n0 + n1 + n2)
+            g = min(64, H * ph // 8)
+            if g // H * H * 20 >= g * 17:
+                g = g // H * H
+            pieces += _model_pieces(H, ph, [(k * (n0 + n1 + n2), [n0, n1, n2])
+                                            for k in range(cn)], g)
+    size = n_sessions * 4 * a256(H * n_q * hd * 2)      # 4 steps' staged values
+    for npart in pieces:
+        size += a256(n_q * H * hd * 2)                  # O
+        if npart > 1:
+            size += a256(npart * n_q * H * hd * 2) + a256(npart * n_q * H * 4)
+    assert need.value == size, (need.value, size)
